@@ -1,0 +1,361 @@
+"""Staged float64 NumPy oracle of the MoE layer forward (test infrastructure only).
+
+Pages cited (by title and section):
+
+* [DWDP] README of "DWDP-Triton-MoE-Inference-Engine": sections "How To Use",
+  "Router Module", "Dispatcher Module", "Scheduler Module", "Executor Module",
+  "Merger Module", "Runtime Integration Layer", "Hugging Face Adapter Layer".
+* [diffulex] API reference "diffulex.moe": sections "diffulex.moe.topk",
+  "diffulex.moe.layer".
+* [refit] modelexpress test "test_reshard_refit_moe_experts.py": the module
+  docstring and class ``FusedMoEModel`` (fused ``w13`` = gate rows then up rows).
+* [ep_dispatch] metrale "ep_dispatch.rs": ``EpRoutingTable``,
+  ``build_ep_routing_table`` and its tests.
+
+Readings taken where the pages are silent (each is listed with its reason in the
+design notes of the repository):
+
+* the router weight is ``[E, H]`` (a linear layer), logits = x . Wr^T (+ bias);
+* top-k is taken on the logits (softmax is monotone), ties go to the lower
+  expert id, -0.0 equals +0.0, and slots are ordered by descending logit;
+* renormalised weights are p[id_j] / sum_j p[id_j] with p = softmax(logits);
+* the token permutation is a gather map ``perm[p] = a`` over the token-major
+  flat assignment index ``a = t*k + j``, sorted stably by (expert, a), and
+  ``inv[a] = p``; offsets have E+1 entries;
+* an expert computes ``h = silu(gate) * up`` with ``silu(z) = z / (1 + e^-z)``,
+  then ``y = W2 h``; routing weights are applied in the combine;
+* the shared expert output is scaled by sigmoid(x . g) for a gate vector g [H].
+
+Everything is float64; bf16 inputs are widened exactly and nothing is rounded
+on the way.  This module imports NumPy only.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+
+__all__ = [
+    "widen",
+    "router_logits",
+    "shared_gate_logit",
+    "select_topk",
+    "routing_probs",
+    "routing_weights",
+    "dispatch_plan",
+    "w13_gate",
+    "w13_up",
+    "silu",
+    "swiglu_expert",
+    "expert_ffn",
+    "combine",
+    "shared_expert",
+    "forward",
+    "token_outputs",
+    "ep_routing_table",
+]
+
+
+# --------------------------------------------------------------------------
+# input decoding
+# --------------------------------------------------------------------------
+def widen(a: np.ndarray) -> np.ndarray:
+    """Decode a stored tensor to float64 exactly.
+
+    ``uint16`` arrays are bf16 bit patterns: the 16 bits are the upper half of
+    an IEEE binary32, so shifting them up by 16 gives the exact value.
+    ``float32``/``float64`` arrays are converted (exactly).
+    """
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if a.dtype in (np.float32, np.float64):
+        return a.astype(np.float64)
+    raise TypeError(f"unsupported stored dtype {a.dtype}")
+
+
+# --------------------------------------------------------------------------
+# router  ([DWDP] "Router Module"; [diffulex] "diffulex.moe.topk")
+# --------------------------------------------------------------------------
+def router_logits(x: np.ndarray, router_weight: np.ndarray,
+                  router_bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """Router logits ``L[t, e] = sum_h x[t, h] * Wr[e, h] (+ bias[e])`` in float64.
+
+    [DWDP] "Router Module" lists router logits as the first router output.  The
+    weight layout [E, H] (a linear layer from H to E) is the reading taken.  The
+    optional bias is the per-expert bias of the skewed-routing workload; it is
+    added before softmax, so it moves both the selection and the weights.
+    """
+    L = widen(x) @ widen(router_weight).T
+    if router_bias is not None:
+        L = L + widen(router_bias)[None, :]
+    return L
+
+
+def shared_gate_logit(x: np.ndarray, shared_gate: np.ndarray) -> np.ndarray:
+    """Scalar gate logit of the shared expert, ``x[t] . g``  ([diffulex]
+    "diffulex.moe.layer" names a shared expert MLP; the sigmoid gate on it is
+    the Qwen1.5-MoE form the [DWDP] "Hugging Face Adapter Layer" targets)."""
+    return widen(x) @ widen(shared_gate)
+
+
+def select_topk(logits: np.ndarray, top_k: int) -> np.ndarray:
+    """Top-k expert ids per token, ``[T, k]`` int32.
+
+    [DWDP] "Router Module" (top-k expert indices).  The k largest logits are
+    chosen; slots are in descending logit order, equal values go to the lower
+    expert id (a stable sort of the negated logits keeps index order among
+    equal keys, and -0.0 compares equal to +0.0).
+    """
+    L = np.asarray(logits, dtype=np.float64)
+    T, E = L.shape
+    if not (1 <= top_k <= E):
+        raise ValueError("top_k out of range")
+    order = np.argsort(-L, axis=1, kind="stable")
+    return order[:, :top_k].astype(np.int32)
+
+
+def routing_probs(logits: np.ndarray) -> np.ndarray:
+    """Softmax over all experts per token, float64 ([DWDP] "Router Module":
+    routing probabilities)."""
+    L = np.asarray(logits, dtype=np.float64)
+    m = L.max(axis=1, keepdims=True)
+    e = np.exp(L - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def routing_weights(logits: np.ndarray, ids: np.ndarray, renormalize: bool = True) -> np.ndarray:
+    """Routing weights of the selected experts, ``[T, k]`` float64.
+
+    [DWDP] "Router Module" (normalized routing weights): the softmax
+    probabilities of the chosen experts, divided by their sum when
+    ``renormalize`` is set, so that each token's weights sum to one.
+    """
+    p = routing_probs(logits)
+    sel = np.take_along_axis(p, np.asarray(ids, dtype=np.int64), axis=1)
+    if renormalize:
+        sel = sel / sel.sum(axis=1, keepdims=True)
+    return sel
+
+
+# --------------------------------------------------------------------------
+# dispatch plan  ([DWDP] "Dispatcher Module"; [ep_dispatch] flat index order)
+# --------------------------------------------------------------------------
+def dispatch_plan(ids: np.ndarray, weights: np.ndarray, num_experts: int) -> Dict[str, np.ndarray]:
+    """Token-major assignments -> expert-major layout.
+
+    [DWDP] "Dispatcher Module" names the outputs: expert-major grouping,
+    per-expert counts, expert offsets, token permutation, inverse permutation,
+    packed token indices and packed routing weights.  The assignments are read
+    row-major from ``[T, k]`` (flat index ``a = t*k + j``, as
+    ``build_ep_routing_table`` in [ep_dispatch] does), and kept in the order
+    given within each expert (a stable sort by expert id).
+
+    Returns int32 ``counts [E]``, ``offsets [E+1]`` (exclusive scan,
+    ``offsets[E] = T*k``), ``perm [P]`` (``perm[p] = a``), ``inv [P]``
+    (``inv[a] = p``), ``packed_ids [P]`` (``a // k``) and float64
+    ``packed_w [P]``.
+    """
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    flat = ids.reshape(-1).astype(np.int64)
+    if flat.size and (flat.min() < 0 or flat.max() >= num_experts):
+        raise ValueError("expert id out of range")
+    P = flat.size
+    perm = np.argsort(flat, kind="stable")
+    inv = np.empty(P, dtype=np.int64)
+    inv[perm] = np.arange(P)
+    counts = np.bincount(flat, minlength=num_experts)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    packed_ids = perm // k
+    packed_w = np.asarray(weights, dtype=np.float64).reshape(-1)[perm]
+    return {
+        "counts": counts.astype(np.int32),
+        "offsets": offsets.astype(np.int32),
+        "perm": perm.astype(np.int32),
+        "inv": inv.astype(np.int32),
+        "packed_ids": packed_ids.astype(np.int32),
+        "packed_w": packed_w,
+    }
+
+
+# --------------------------------------------------------------------------
+# experts  ([DWDP] "Executor Module"; [refit] FusedMoEModel w13 layout)
+# --------------------------------------------------------------------------
+def w13_gate(w13: np.ndarray, e: int) -> np.ndarray:
+    """Gate (w1) rows of expert ``e`` in a fused ``w13 [E, 2I, H]`` buffer: the
+    low half of the expert's slot ([refit] FusedMoEModel: member 0 is w1)."""
+    I = w13.shape[1] // 2
+    return w13[e, 0:I, :]
+
+
+def w13_up(w13: np.ndarray, e: int) -> np.ndarray:
+    """Up (w3) rows of expert ``e``: the high half of the slot ([refit]
+    FusedMoEModel: member 1 is w3, placed after INTER_PER_TP gate rows)."""
+    I = w13.shape[1] // 2
+    return w13[e, I:2 * I, :]
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """``silu(z) = z * sigmoid(z) = z / (1 + exp(-z))`` (standard SwiGLU
+    activation; the pages name SwiGLU experts but print no formula)."""
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu_expert(X: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """One SwiGLU MLP on rows ``X [M, H]``: ``W_down (silu(W_gate x) * (W_up x))``.
+
+    ``w_gate``/``w_up`` are ``[I, H]``, ``w_down`` is ``[H, I]``; all float64.
+    """
+    g = X @ w_gate.T
+    u = X @ w_up.T
+    return (silu(g) * u) @ w_down.T
+
+
+def expert_ffn(x: np.ndarray, packed_ids: np.ndarray, offsets: np.ndarray,
+               w13: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """Grouped expert FFN over the expert-major layout, ``y [P, H]`` float64.
+
+    [DWDP] "Executor Module": gather the token rows of each expert range, run
+    the expert MLP, write packed expert outputs.  Expert ``e`` owns rows
+    ``offsets[e]:offsets[e+1]`` of the packed layout; row ``p`` reads token
+    ``packed_ids[p]``.  Routing weights are not applied here (see ``combine``).
+    """
+    X = widen(x)
+    W13 = widen(w13)
+    W2 = widen(w2)
+    E = W13.shape[0]
+    P = int(offsets[E])
+    y = np.zeros((P, X.shape[1]), dtype=np.float64)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue  # empty expert: its weights are never read
+        rows = X[np.asarray(packed_ids[lo:hi], dtype=np.int64)]
+        y[lo:hi] = swiglu_expert(rows, w13_gate(W13, e), w13_up(W13, e), W2[e])
+    return y
+
+
+def combine(y: np.ndarray, inv: np.ndarray, weights: np.ndarray) -> np.ndarray:
+    """Weighted combine back to token order, ``out [T, H]`` float64.
+
+    [DWDP] "Merger Module": restore token-major assignment order, accumulate the
+    top-k expert outputs, apply the routing weights.
+    ``out[t] = sum_j w[t, j] * y[inv[t*k + j]]``, summed in ascending j.
+    """
+    w = np.asarray(weights, dtype=np.float64)
+    T, k = w.shape
+    rows = np.asarray(inv, dtype=np.int64).reshape(T, k)
+    out = np.zeros((T, y.shape[1]), dtype=np.float64)
+    for j in range(k):
+        out += w[:, j:j + 1] * y[rows[:, j]]
+    return out
+
+
+def shared_expert(x: np.ndarray, shared_w13: np.ndarray, shared_w2: np.ndarray,
+                  gate_logit: np.ndarray) -> np.ndarray:
+    """Shared expert term ``sigmoid(x.g) * SwiGLU_s(x)``, ``[T, H]`` float64.
+
+    [diffulex] "diffulex.moe.layer" (SharedExpertMLP) with the Qwen1.5-MoE
+    sigmoid gate; ``shared_w13 [2Is, H]`` is gate rows then up rows like an
+    expert slot, ``shared_w2 [H, Is]``.
+    """
+    X = widen(x)
+    W13 = widen(shared_w13)
+    Is = W13.shape[0] // 2
+    s = swiglu_expert(X, W13[:Is], W13[Is:], widen(shared_w2))
+    sig = 1.0 / (1.0 + np.exp(-np.asarray(gate_logit, dtype=np.float64)))
+    return sig[:, None] * s
+
+
+# --------------------------------------------------------------------------
+# the whole layer  ([DWDP] "Runtime Integration Layer": Router -> Dispatcher ->
+# Scheduler -> Executor -> Merger; the comms planner has no single-GPU role)
+# --------------------------------------------------------------------------
+def forward(inputs: Dict[str, np.ndarray], top_k: int, renormalize: bool = True,
+            ids: Optional[np.ndarray] = None, weights: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Full staged forward.  ``inputs`` holds the arrays of ``workloads.generate``.
+
+    When ``ids``/``weights`` are given they replace the oracle's own routing, so
+    that the expert and combine stages can be checked on a GPU routing result.
+    """
+    x = inputs["x"]
+    E = inputs["router_weight"].shape[0]
+    L = router_logits(x, inputs["router_weight"], inputs.get("router_bias"))
+    if ids is None:
+        ids = select_topk(L, top_k)
+    if weights is None:
+        weights = routing_weights(L, ids, renormalize)
+    plan = dispatch_plan(ids, weights, E)
+    y = expert_ffn(x, plan["packed_ids"], plan["offsets"], inputs["w13"], inputs["w2"])
+    out = combine(y, plan["inv"], weights)
+    res = {"logits": L, "ids": np.asarray(ids, dtype=np.int32), "weights": np.asarray(weights, dtype=np.float64),
+           "y": y, "out": out, **plan}
+    if "shared_w13" in inputs:
+        gl = shared_gate_logit(x, inputs["shared_gate"])
+        s = shared_expert(x, inputs["shared_w13"], inputs["shared_w2"], gl)
+        res["shared_gate_logit"] = gl
+        res["shared"] = s
+        res["out"] = out + s
+    return res
+
+
+def token_outputs(inputs: Dict[str, np.ndarray], tokens: np.ndarray, ids: np.ndarray,
+                  weights: np.ndarray) -> np.ndarray:
+    """Layer output for a sample of tokens, one token at a time, float64.
+
+    Uses the dispatch-free form ``out[t] = sum_j w[t,j] * FFN_{ids[t,j]}(x[t])``
+    (plus the gated shared expert), which needs only the chosen experts'
+    weights, so it runs at full workload sizes.  ``ids``/``weights`` are the
+    full ``[T, k]`` routing (for instance a GPU result); only the sampled rows are read.
+    """
+    tokens = np.asarray(tokens, dtype=np.int64)
+    x = inputs["x"]
+    w13 = inputs["w13"]
+    w2 = inputs["w2"]
+    H = x.shape[1]
+    out = np.zeros((len(tokens), H), dtype=np.float64)
+    for n, t in enumerate(tokens):
+        xt = widen(x[t:t + 1])
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j])
+            W13e = widen(w13[e])
+            I = W13e.shape[0] // 2
+            out[n] += float(weights[t, j]) * swiglu_expert(xt, W13e[:I], W13e[I:], widen(w2[e]))[0]
+        if "shared_w13" in inputs:
+            gl = shared_gate_logit(x[t:t + 1], inputs["shared_gate"])
+            out[n] += shared_expert(x[t:t + 1], inputs["shared_w13"], inputs["shared_w2"], gl)[0]
+    return out
+
+
+# --------------------------------------------------------------------------
+# expert-parallel local/remote split  ([ep_dispatch] build_ep_routing_table)
+# --------------------------------------------------------------------------
+def ep_routing_table(gate_indices, gate_weights, num_tokens: int, top_k: int,
+                     local_expert_start: int, local_expert_end: int) -> Dict[str, np.ndarray]:
+    """Split row-major ``[num_tokens, top_k]`` assignments into the experts of
+    one rank (``start <= id < end``) and the rest, each bucket in assignment
+    order, as ``build_ep_routing_table`` in [ep_dispatch] specifies.
+
+    Raises ``ValueError`` with "gate_indices length mismatch" /
+    "gate_weights length mismatch" when a length differs from
+    ``num_tokens * top_k`` (the Rust function panics with those texts).
+    """
+    gi = np.asarray(gate_indices).reshape(-1)
+    gw = np.asarray(gate_weights).reshape(-1)
+    total = num_tokens * top_k
+    if gi.size != total:
+        raise ValueError("gate_indices length mismatch")
+    if gw.size != total:
+        raise ValueError("gate_weights length mismatch")
+    a = np.arange(total)
+    local = (gi >= local_expert_start) & (gi < local_expert_end)
+    tok = a // max(top_k, 1)
+    return {
+        "local_token_indices": tok[local].astype(np.uint32),
+        "local_expert_ids": gi[local].astype(np.uint32),
+        "local_weights": gw[local].astype(np.float32),
+        "remote_token_indices": tok[~local].astype(np.uint32),
+        "remote_expert_ids": gi[~local].astype(np.uint32),
+        "remote_weights": gw[~local].astype(np.float32),
+    }

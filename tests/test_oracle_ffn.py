@@ -1,0 +1,201 @@
+"""Pins of the oracle's expert FFN, combine, shared expert and whole forward.
+
+Pinned against: the fused w13 byte offset of the modelexpress refit test, a
+library SwiGLU MLP (torch CPU ops in float64), a dense routing-mask identity
+that needs no dispatch plan, a scalar pure-Python loop, and special cases
+(identical experts, zero down projection, zero gate, k=1 permutation, shared
+expert with a zero gate vector).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def tiny(seed=0, **kw):
+    base = dict(num_tokens=9, hidden_size=12, num_experts=5, top_k=2, intermediate_size=6)
+    base.update(kw)
+    cfg = workloads.config("tiny_fp32").scaled(**base)
+    return cfg, workloads.generate(cfg, seed=seed)
+
+
+def test_w13_layout_byte_offset():
+    g = json.load(open(os.path.join(GOLDEN, "w13_layout.json")))
+    H, I, E = g["hidden"], g["inter_per_tp"], g["local_experts"]
+    w13 = np.zeros((E, 2 * I, H), dtype=np.float32)
+    up = oracle.w13_up(w13, g["expert"])
+    gate = oracle.w13_gate(w13, g["expert"])
+    base = w13.__array_interface__["data"][0]
+    assert up.__array_interface__["data"][0] - base == g["expected_byte_offset"]
+    assert gate.__array_interface__["data"][0] - base == g["expected_byte_offset"] - I * H * g["elsize"]
+    assert up.shape == (I, H) and gate.shape == (I, H)
+
+
+def test_silu_against_library():
+    z = np.linspace(-30, 30, 1001)
+    ref = F.silu(torch.from_numpy(z)).numpy()
+    assert np.allclose(oracle.silu(z), ref, rtol=1e-14, atol=1e-300)
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+
+
+def test_single_expert_is_textbook_swiglu():
+    """E=1, k=1: the layer is a dense SwiGLU MLP (torch F.linear / F.silu, float64)."""
+    cfg, inp = tiny(num_experts=1, top_k=1, num_tokens=7, hidden_size=10, intermediate_size=4, seed=5)
+    res = oracle.forward(inp, cfg.top_k)
+    w13 = torch.from_numpy(inp["w13"].astype(np.float64))[0]
+    w2 = torch.from_numpy(inp["w2"].astype(np.float64))[0]
+    x = torch.from_numpy(inp["x"].astype(np.float64))
+    I = cfg.intermediate_size
+    ref = F.linear(F.silu(F.linear(x, w13[:I])) * F.linear(x, w13[I:]), w2)
+    assert np.allclose(res["out"], ref.numpy(), rtol=1e-12, atol=1e-15)
+    assert (res["weights"] == 1.0).all()
+
+
+def _dense_reference(inp, ids, w):
+    """out = sum_e G[:, e] * FFN_e(x), G[t, e] = w[t, j] if ids[t, j] == e.  No plan."""
+    x = inp["x"].astype(np.float64)
+    E = inp["w13"].shape[0]
+    I = inp["w13"].shape[1] // 2
+    T = x.shape[0]
+    G = np.zeros((T, E))
+    for t in range(T):
+        for j in range(ids.shape[1]):
+            G[t, ids[t, j]] += w[t, j]
+    out = np.zeros_like(x)
+    for e in range(E):
+        W = inp["w13"][e].astype(np.float64)
+        g = x @ W[:I].T
+        u = x @ W[I:].T
+        ffn = ((g / (1 + np.exp(-g))) * u) @ inp["w2"][e].astype(np.float64).T
+        out += G[:, e:e + 1] * ffn
+    return out
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_forward_matches_dense_mask_identity(seed):
+    cfg, inp = tiny(seed=seed, num_tokens=16, num_experts=6, top_k=3)
+    res = oracle.forward(inp, cfg.top_k)
+    assert np.allclose(res["out"], _dense_reference(inp, res["ids"], res["weights"]), rtol=1e-12, atol=1e-14)
+
+
+def test_scatter_form_equals_gather_form():
+    cfg, inp = tiny(seed=1)
+    res = oracle.forward(inp, cfg.top_k)
+    out = np.zeros_like(res["out"])
+    for p in range(len(res["perm"])):
+        out[res["packed_ids"][p]] += res["packed_w"][p] * res["y"][p]
+    assert np.allclose(out, res["out"], rtol=1e-13, atol=1e-15)
+
+
+def test_token_outputs_matches_staged():
+    cfg, inp = tiny(seed=2, num_tokens=11)
+    res = oracle.forward(inp, cfg.top_k)
+    toks = np.array([0, 3, 10])
+    sample = oracle.token_outputs(inp, toks, res["ids"], res["weights"])
+    assert np.allclose(sample, res["out"][toks], rtol=1e-13, atol=1e-15)
+
+
+def test_identical_experts_give_plain_ffn():
+    cfg, inp = tiny(seed=3)
+    inp["w13"][:] = inp["w13"][0:1]
+    inp["w2"][:] = inp["w2"][0:1]
+    res = oracle.forward(inp, cfg.top_k)
+    x = inp["x"].astype(np.float64)
+    I = cfg.intermediate_size
+    W = inp["w13"][0].astype(np.float64)
+    ffn = oracle.silu(x @ W[:I].T) * (x @ W[I:].T) @ inp["w2"][0].astype(np.float64).T
+    assert np.allclose(res["out"], ffn, rtol=1e-12, atol=1e-15)
+
+
+def test_zero_down_projection_and_zero_gate():
+    cfg, inp = tiny(seed=4)
+    a = dict(inp)
+    a["w2"] = np.zeros_like(inp["w2"])
+    assert (oracle.forward(a, cfg.top_k)["out"] == 0).all()
+    b = dict(inp)
+    w13 = inp["w13"].copy()
+    w13[:, :cfg.intermediate_size] = 0  # gate rows: silu(0) = 0
+    b["w13"] = w13
+    assert (oracle.forward(b, cfg.top_k)["out"] == 0).all()
+    c = dict(inp)
+    w13 = inp["w13"].copy()
+    w13[:, cfg.intermediate_size:] = 0  # up rows
+    c["w13"] = w13
+    assert (oracle.forward(c, cfg.top_k)["out"] == 0).all()
+
+
+def test_top1_unit_weight_combine_is_a_permutation():
+    rng = np.random.default_rng(0)
+    T, E, H = 13, 4, 6
+    ids = rng.integers(0, E, size=(T, 1))
+    plan = oracle.dispatch_plan(ids, np.ones((T, 1)), E)
+    y = rng.standard_normal((T, H))
+    out = oracle.combine(y, plan["inv"], np.ones((T, 1)))
+    assert (out == y[plan["inv"]]).all()
+    assert (out[plan["packed_ids"]] == y).all()
+
+
+def test_scalar_loop_reference():
+    """Pure-Python triple loop over a tiny layer, independent of NumPy matmul."""
+    cfg, inp = tiny(seed=6, num_tokens=4, hidden_size=3, num_experts=3, top_k=2, intermediate_size=2)
+    res = oracle.forward(inp, cfg.top_k)
+    x, W13, W2 = inp["x"], inp["w13"], inp["w2"]
+    H, I = 3, 2
+    for t in range(4):
+        for c in range(H):
+            total = 0.0
+            for j in range(2):
+                e = int(res["ids"][t, j])
+                acc = 0.0
+                for i in range(I):
+                    g = sum(float(x[t, h]) * float(W13[e, i, h]) for h in range(H))
+                    u = sum(float(x[t, h]) * float(W13[e, I + i, h]) for h in range(H))
+                    acc += float(W2[e, c, i]) * (g / (1.0 + math.exp(-g))) * u
+                total += float(res["weights"][t, j]) * acc
+            assert res["out"][t, c] == pytest.approx(total, rel=1e-10, abs=1e-14)
+
+
+def test_shared_expert_special_cases():
+    cfg = workloads.config("qwen15_moe_decode").scaled(num_tokens=5, hidden_size=16, num_experts=6,
+                                                        top_k=2, intermediate_size=8, shared_intermediate_size=12)
+    inp = workloads.generate(cfg, seed=1)
+    # zero gate vector -> sigmoid(0) = 0.5 exactly; routed path off (w2 = 0)
+    a = dict(inp)
+    a["shared_gate"] = np.zeros_like(inp["shared_gate"])
+    a["w2"] = np.zeros_like(inp["w2"])
+    res = oracle.forward(a, cfg.top_k)
+    x = oracle.widen(inp["x"])
+    W = oracle.widen(inp["shared_w13"])
+    Is = cfg.shared_intermediate_size
+    s = oracle.silu(x @ W[:Is].T) * (x @ W[Is:].T) @ oracle.widen(inp["shared_w2"]).T
+    assert np.allclose(res["out"], 0.5 * s, rtol=1e-12, atol=1e-15)
+    # full: out = routed + sigmoid(x.g) * shared
+    res = oracle.forward(inp, cfg.top_k)
+    gl = x @ oracle.widen(inp["shared_gate"])
+    routed = _dense_reference({k: oracle.widen(v) if v.dtype == np.uint16 else v for k, v in inp.items()},
+                              res["ids"], res["weights"])
+    ref = routed + (1 / (1 + np.exp(-gl)))[:, None] * s
+    assert np.allclose(res["out"], ref, rtol=1e-12, atol=1e-14)
+    sample = oracle.token_outputs(inp, np.array([1, 4]), res["ids"], res["weights"])
+    assert np.allclose(sample, res["out"][[1, 4]], rtol=1e-12, atol=1e-14)
+
+
+def test_empty_experts_are_skipped():
+    cfg, inp = tiny(seed=8, num_tokens=6, num_experts=8, top_k=1)
+    ids = np.zeros((6, 1), np.int32)  # every token to expert 0
+    w = np.ones((6, 1))
+    plan = oracle.dispatch_plan(ids, w, 8)
+    y = oracle.expert_ffn(inp["x"], plan["packed_ids"], plan["offsets"], inp["w13"], inp["w2"])
+    x = inp["x"].astype(np.float64)
+    ref = oracle.swiglu_expert(x, oracle.w13_gate(inp["w13"].astype(np.float64), 0),
+                               oracle.w13_up(inp["w13"].astype(np.float64), 0), inp["w2"][0].astype(np.float64))
+    assert np.allclose(y, ref, rtol=1e-13)
