@@ -1,0 +1,243 @@
+/*
+ * moe.h - C ABI of a single-GPU Mixture-of-Experts layer forward for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer is the pipeline the DWDP-Triton-MoE-Inference-Engine README lays
+ * out ("Runtime Integration Layer"): a router (router logits, routing
+ * probabilities, top-k expert ids, normalised routing weights), a dispatcher
+ * (token-major assignments -> expert-major layout), an executor (grouped
+ * SwiGLU experts over the expert ranges) and a merger (weighted combine back
+ * to token order).  The comms planner of that pipeline has no role on one GPU.
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ *  - Every tensor argument is a DEVICE pointer to a contiguous row-major
+ *    array owned by the caller; the library never allocates, frees or keeps
+ *    a pointer after the call returns.  Pointers to activations, weights and
+ *    outputs must be 16-byte aligned.
+ *  - `dtype` (moe_dtype) is the storage type of the hidden states and of every
+ *    weight.  Logits, routing weights, router bias, shared-gate logits and the
+ *    packed expert outputs are always float32; expert ids and every dispatch
+ *    array are int32.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *    call only enqueues work on that stream: it does not synchronise and does
+ *    not copy anything to the host.
+ *  - Shapes: T = num_tokens, H = hidden_size, E = num_experts, k = top_k,
+ *    I = intermediate_size, P = T*k (number of (token, expert) assignments).
+ *  - Assignments are indexed token-major, a = t*k + j (row-major [T, k]), as
+ *    build_ep_routing_table in metrale's ep_dispatch.rs reads its gate arrays.
+ *  - Errors: every argument check runs on the host before anything is
+ *    enqueued; on any status other than MOE_OK nothing was enqueued, except
+ *    for MOE_ERR_HIP, which reports a failed launch.  moe_last_error_message()
+ *    returns a per-thread text naming the offending argument (for example
+ *    "topk_ids is NULL" or "workspace too small").  num_tokens == 0 is a valid
+ *    no-op that returns MOE_OK.
+ *  - Device-side preconditions that the host cannot see (expert ids in
+ *    [0, E), offsets consistent with P) are the caller's contract; the plan
+ *    produced by moe_dispatch_plan always satisfies them.
+ *  - Limits: 1 <= E <= 512, 1 <= k <= E, T*k < 2^31.  bf16: H and I are
+ *    multiples of 64.  f32: H multiple of 8, I multiple of 16.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_EXPERTS 512
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, k out of range, length mismatch */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but not supported: E > 512, H/I alignment, misaligned pointer */
+  MOE_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the *_workspace_size() result */
+  MOE_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_DTYPE_F32 = 0,
+  MOE_DTYPE_BF16 = 1
+} moe_dtype;
+
+/* MOE_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+
+/* Static text of a status code ("MOE_OK", ...). Never NULL. */
+const char* moe_status_string(int status);
+
+/* Per-thread text of the last error raised by a call on this thread, "" if
+ * the last call succeeded. Valid until the next call on the same thread. */
+const char* moe_last_error_message(void);
+
+/*
+ * Router: logits, softmax, top-k, routing weights.
+ * [DWDP README "Router Module"; diffulex.moe "diffulex.moe.topk": a standard
+ *  top-k router]
+ *
+ *   router_logits[t,e] = sum_h hidden_states[t,h] * router_weight[e,h]
+ *                        (+ router_bias[e])                          (fp32 accumulate)
+ *   topk_ids[t,:]      = the k experts with the largest logits, in descending
+ *                        logit order; equal fp32 logits go to the lower id first,
+ *                        -0.0 counts as equal to +0.0
+ *   topk_weights[t,j]  = softmax(router_logits[t])[topk_ids[t,j]], divided by the
+ *                        sum over the k chosen experts when renormalize != 0
+ *                        (so each token's weights sum to one)
+ *   routing_probs[t,e] = softmax(router_logits[t])[e]
+ *   shared_gate_logit[t] = sum_h hidden_states[t,h] * shared_gate[h]
+ *
+ * hidden_states [T,H] dtype; router_weight [E,H] dtype; router_bias [E] f32 or
+ * NULL (added before the softmax, so it moves the selection and the weights);
+ * shared_gate [H] dtype or NULL; router_logits [T,E] f32 (required: the
+ * top-k stage reads it back); routing_probs [T,E] f32 or NULL; topk_ids [T,k]
+ * int32 (required);
+ * topk_weights [T,k] f32 (required); shared_gate_logit [T] f32, required iff
+ * shared_gate != NULL.
+ * Errors: INVALID_ARG for a NULL required pointer, k < 1 or k > E, negative
+ * sizes, shared_gate without shared_gate_logit (or the reverse);
+ * UNSUPPORTED for E > 512, alignment.
+ */
+moe_status moe_router_topk(const void* hidden_states, const void* router_weight,
+                           const float* router_bias, const void* shared_gate,
+                           int64_t num_tokens, int64_t hidden_size, int64_t num_experts,
+                           int64_t top_k, int renormalize, int dtype,
+                           float* router_logits, float* routing_probs,
+                           int32_t* topk_ids, float* topk_weights,
+                           float* shared_gate_logit, void* stream);
+
+/*
+ * Dispatch plan: token-major assignments -> expert-major layout.
+ * [DWDP README "Dispatcher Module": expert-major grouping, per-expert counts,
+ *  expert offsets, token permutation, inverse permutation, packed token
+ *  indices, packed routing weights; metrale ep_dispatch.rs EpRoutingTable:
+ *  assignments kept in the order given]
+ *
+ *   expert_counts[e]          = #{a : topk_ids[a] == e}                        [E]
+ *   expert_offsets[e]         = sum_{e' < e} expert_counts[e'], offsets[E] = P  [E+1]
+ *   token_permutation[p]      = a, listing the assignments sorted stably by
+ *                               (expert id, a)                                 [P]
+ *   inverse_permutation[a]    = p with token_permutation[p] == a               [P]
+ *   packed_token_indices[p]   = token_permutation[p] / k                       [P]
+ *   packed_routing_weights[p] = topk_weights[token_permutation[p]]             [P] f32
+ *
+ * The plan is deterministic: positions come from counts and prefix sums, never
+ * from the order of atomic operations.  topk_weights may be NULL, then
+ * packed_routing_weights must be NULL too.
+ * workspace: at least moe_dispatch_workspace_size(T, k, E) bytes of device
+ * memory, 256-byte aligned; its contents are scratch.
+ * Errors: INVALID_ARG for NULL outputs or k/E out of range; WORKSPACE.
+ */
+size_t moe_dispatch_workspace_size(int64_t num_tokens, int64_t top_k, int64_t num_experts);
+moe_status moe_dispatch_plan(const int32_t* topk_ids, const float* topk_weights,
+                             int64_t num_tokens, int64_t top_k, int64_t num_experts,
+                             int32_t* expert_counts, int32_t* expert_offsets,
+                             int32_t* token_permutation, int32_t* inverse_permutation,
+                             int32_t* packed_token_indices, float* packed_routing_weights,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Grouped expert SwiGLU FFN over the expert-major layout.
+ * [DWDP README "Executor Module": gather token activations per expert range,
+ *  run the expert, write packed expert outputs; modelexpress refit test,
+ *  FusedMoEModel: w13 holds the gate (w1) rows then the up (w3) rows of each
+ *  expert slot]
+ *
+ * For every expert e and packed row p in [expert_offsets[e], expert_offsets[e+1]),
+ * with x = hidden_states[packed_token_indices[p]]:
+ *   g = w13[e, 0:I, :] . x,  u = w13[e, I:2I, :] . x
+ *   h = silu(g) * u,  silu(z) = z / (1 + exp(-z))
+ *   packed_expert_outputs[p] = w2[e] . h                                     [P,H] f32
+ * Routing weights are NOT applied here (moe_combine applies them).
+ *
+ * hidden_states [T,H] dtype; packed_token_indices [P] int32, or NULL meaning
+ * row p reads token p (requires P <= T); expert_offsets [E+1] int32 device, or
+ * NULL meaning a single expert (E must be 1) owning all P rows; w13 [E,2I,H]
+ * dtype; w2 [E,H,I] dtype.  P = num_tokens * top_k.
+ * Numerics (bf16): fp32 accumulation, h rounded once to bf16 (it is the
+ * operand of the second bf16 GEMM), outputs fp32.  f32: fp32 throughout.
+ * Experts with no rows are skipped and their weights are not read.
+ * workspace: moe_grouped_ffn_workspace_size(...) bytes (holds h).
+ */
+size_t moe_grouped_ffn_workspace_size(int64_t num_tokens, int64_t top_k, int64_t num_experts,
+                                      int64_t intermediate_size, int dtype);
+moe_status moe_grouped_ffn(const void* hidden_states, const int32_t* packed_token_indices,
+                           const int32_t* expert_offsets, const void* w13, const void* w2,
+                           int64_t num_tokens, int64_t hidden_size, int64_t num_experts,
+                           int64_t top_k, int64_t intermediate_size, int dtype,
+                           float* packed_expert_outputs,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Weighted combine back to token order.
+ * [DWDP README "Merger Module": restore token-major assignment order,
+ *  accumulate the top-k expert outputs, apply routing weights]
+ *
+ *   output[t] = sum_{j=0..k-1} topk_weights[t,j] * packed_expert_outputs[inverse_permutation[t*k+j]]
+ *               (+ sigmoid(shared_gate_logit[t]) * shared_output[t])
+ * summed in ascending j in fp32, the shared term added last.
+ *
+ * packed_expert_outputs [P,H] f32; inverse_permutation [P] int32; topk_weights
+ * [T,k] f32; shared_output [T,H] f32 or NULL; shared_gate_logit [T] f32 or NULL
+ * (NULL with a shared_output means a gate of 1); out_dtype MOE_DTYPE_F32 or
+ * MOE_DTYPE_BF16 (round to nearest even); output [T,H] out_dtype.
+ */
+moe_status moe_combine(const float* packed_expert_outputs, const int32_t* inverse_permutation,
+                       const float* topk_weights, const float* shared_output,
+                       const float* shared_gate_logit,
+                       int64_t num_tokens, int64_t hidden_size, int64_t top_k,
+                       int out_dtype, void* output, void* stream);
+
+/*
+ * Whole layer forward: router -> dispatch plan -> grouped FFN -> combine,
+ * plus an optional sigmoid-gated shared expert.
+ * [DWDP README "How To Use": build_reference binds one explicit layer of
+ *  hidden_size, num_experts, top_k and expert weights; "Runtime Integration
+ *  Layer": the runtime owns reusable workspaces; diffulex.moe
+ *  "diffulex.moe.layer": SharedExpertMLP]
+ *
+ *   output = combine(grouped_ffn(dispatch(router(x))))
+ *            + sigmoid(x . shared_gate) * W2s (silu(W13s[0:Is] x) * W13s[Is:2Is] x)
+ *
+ * shared_w13 [2*Is,H], shared_w2 [H,Is], shared_gate [H] (all dtype) are all
+ * given or all NULL (then shared_intermediate_size is ignored).
+ * Optional outputs (NULL to skip): topk_ids_out [T,k] int32, topk_weights_out
+ * [T,k] f32, router_logits_out [T,E] f32.
+ * workspace: moe_forward_workspace_size(...) bytes; it holds the routing, the
+ * plan, h and the packed expert outputs.
+ */
+size_t moe_forward_workspace_size(int64_t num_tokens, int64_t hidden_size, int64_t num_experts,
+                                  int64_t top_k, int64_t intermediate_size,
+                                  int64_t shared_intermediate_size, int dtype);
+moe_status moe_forward(const void* hidden_states, const void* router_weight,
+                       const float* router_bias, const void* w13, const void* w2,
+                       const void* shared_w13, const void* shared_w2, const void* shared_gate,
+                       int64_t num_tokens, int64_t hidden_size, int64_t num_experts,
+                       int64_t top_k, int64_t intermediate_size,
+                       int64_t shared_intermediate_size, int renormalize, int dtype,
+                       int out_dtype, void* output,
+                       int32_t* topk_ids_out, float* topk_weights_out, float* router_logits_out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Kernel timing for measurement tools.  While enabled, every kernel the
+ * library launches is bracketed by two HIP events recorded on the stream the
+ * kernel is launched on.  moe_profile_collect() waits for the recorded events,
+ * adds each kernel's elapsed time to its name's total, and clears the record.
+ * This is process-wide state guarded by a mutex; it is meant for benchmarks,
+ * not for concurrent production calls.
+ *   names   : receives up to `capacity` static kernel-name strings
+ *   total_ms: summed duration per name; launches: launch count per name
+ * Returns the number of distinct names recorded (may exceed capacity).
+ */
+void moe_profile_enable(int enable);
+int moe_profile_collect(const char** names, double* total_ms, int64_t* launches, int capacity);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

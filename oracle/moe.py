@@ -302,29 +302,29 @@ def forward(inputs: Dict[str, np.ndarray], top_k: int, renormalize: bool = True,
 
 def token_outputs(inputs: Dict[str, np.ndarray], tokens: np.ndarray, ids: np.ndarray,
                   weights: np.ndarray) -> np.ndarray:
-    """Layer output for a sample of tokens, one token at a time, float64.
+    """Layer output for a sample of tokens, float64.
 
     Uses the dispatch-free form ``out[t] = sum_j w[t,j] * FFN_{ids[t,j]}(x[t])``
     (plus the gated shared expert), which needs only the chosen experts'
     weights, so it runs at full workload sizes.  ``ids``/``weights`` are the
-    full ``[T, k]`` routing (for instance a GPU result); only the sampled rows are read.
+    full ``[T, k]`` routing (for instance a GPU result); only the sampled rows
+    are read.  Each touched expert is decoded once for all sampled tokens
+    routed to it (a token picks an expert at most once).
     """
     tokens = np.asarray(tokens, dtype=np.int64)
-    x = inputs["x"]
-    w13 = inputs["w13"]
-    w2 = inputs["w2"]
-    H = x.shape[1]
-    out = np.zeros((len(tokens), H), dtype=np.float64)
-    for n, t in enumerate(tokens):
-        xt = widen(x[t:t + 1])
-        for j in range(ids.shape[1]):
-            e = int(ids[t, j])
-            W13e = widen(w13[e])
-            I = W13e.shape[0] // 2
-            out[n] += float(weights[t, j]) * swiglu_expert(xt, W13e[:I], W13e[I:], widen(w2[e]))[0]
-        if "shared_w13" in inputs:
-            gl = shared_gate_logit(x[t:t + 1], inputs["shared_gate"])
-            out[n] += shared_expert(x[t:t + 1], inputs["shared_w13"], inputs["shared_w2"], gl)[0]
+    X = widen(inputs["x"][tokens])
+    sel = np.asarray(ids)[tokens].astype(np.int64)
+    wsel = np.asarray(weights, dtype=np.float64)[tokens]
+    out = np.zeros_like(X)
+    for e in np.unique(sel):
+        rows, slots = np.nonzero(sel == e)
+        W13e = widen(inputs["w13"][e])
+        I = W13e.shape[0] // 2
+        y = swiglu_expert(X[rows], W13e[:I], W13e[I:], widen(inputs["w2"][e]))
+        out[rows] += wsel[rows, slots][:, None] * y
+    if "shared_w13" in inputs:
+        gl = shared_gate_logit(inputs["x"][tokens], inputs["shared_gate"])
+        out += shared_expert(inputs["x"][tokens], inputs["shared_w13"], inputs["shared_w2"], gl)
     return out
 
 

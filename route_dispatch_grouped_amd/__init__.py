@@ -1,0 +1,384 @@
+"""MI355X-native single-GPU MoE layer forward: Python binding of the C ABI.
+
+This module only marshals arguments: it checks tensor devices, dtypes, shapes
+and contiguity, allocates outputs and workspaces with torch, and calls the
+entry points of ``lib/libmoe_mi355x.so`` (declared in ``include/moe.h``) on
+torch's current HIP stream.  Every step of the layer runs in the library's
+HIP kernels; there is no Python or CPU fallback.  Importing works without a
+GPU; the first call raises if the library is missing.
+
+Entry points (same names as the C ABI):
+  moe_router_topk, moe_dispatch_plan, moe_grouped_ffn, moe_combine, moe_forward
+plus ``MoeLayer``, a bound layer with a reusable workspace (the "explicit
+layer" of the DWDP README's ``build_reference``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+from .build import LIB_PATH
+
+__all__ = [
+    "LIB_PATH",
+    "MOE_OK",
+    "MOE_DTYPE_F32",
+    "MOE_DTYPE_BF16",
+    "MoeError",
+    "load_library",
+    "library_loaded",
+    "moe_router_topk",
+    "moe_dispatch_plan",
+    "moe_grouped_ffn",
+    "moe_combine",
+    "moe_forward",
+    "moe_forward_workspace_size",
+    "MoeLayer",
+    "profile_enable",
+    "profile_collect",
+]
+
+MOE_OK = 0
+MOE_DTYPE_F32 = 0
+MOE_DTYPE_BF16 = 1
+
+_c_void_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_size = ctypes.c_size_t
+
+_SIGNATURES = {
+    "moe_abi_version": (_int, []),
+    "moe_status_string": (ctypes.c_char_p, [_int]),
+    "moe_last_error_message": (ctypes.c_char_p, []),
+    "moe_router_topk": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _int, _int,
+                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "moe_dispatch_workspace_size": (_size, [_i64, _i64, _i64]),
+    "moe_dispatch_plan": (_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                 _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "moe_grouped_ffn_workspace_size": (_size, [_i64, _i64, _i64, _i64, _int]),
+    "moe_grouped_ffn": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64,
+                               _i64, _int, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "moe_combine": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _int,
+                           _c_void_p, _c_void_p]),
+    "moe_forward_workspace_size": (_size, [_i64, _i64, _i64, _i64, _i64, _i64, _int]),
+    "moe_forward": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                           _i64, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _c_void_p, _c_void_p,
+                           _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "moe_profile_enable": (None, [_int]),
+    "moe_profile_collect": (_int, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                                   ctypes.POINTER(_i64), _int]),
+}
+
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    """A library call returned a status other than MOE_OK."""
+
+    def __init__(self, fn: str, status: int, text: str, message: str):
+        super().__init__(f"{fn}: {text}: {message}")
+        self.status = status
+        self.text = text
+        self.message = message
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the built HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"HIP library {p} is missing: build it with route_dispatch_grouped_amd.build.build()")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def library_loaded() -> bool:
+    return _lib is not None
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        lib = load_library()
+        raise MoeError(fn, status, lib.moe_status_string(status).decode(), lib.moe_last_error_message().decode())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return MOE_DTYPE_BF16
+    if t == torch.float32:
+        return MOE_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t}; use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} length mismatch: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def moe_router_topk(hidden_states: torch.Tensor, router_weight: torch.Tensor, top_k: int,
+                    router_bias: Optional[torch.Tensor] = None, shared_gate: Optional[torch.Tensor] = None,
+                    renormalize: bool = True, return_probs: bool = False, stream=None) -> Dict[str, torch.Tensor]:
+    """Router logits -> softmax -> top-k -> routing weights (include/moe.h: moe_router_topk).
+
+    Returns ``logits [T,E] f32``, ``topk_ids [T,k] int32``, ``topk_weights [T,k] f32`` and
+    optionally ``probs [T,E]`` and ``shared_gate_logit [T]``.
+    """
+    lib = load_library()
+    T, H = hidden_states.shape
+    E = router_weight.shape[0]
+    dt = hidden_states.dtype
+    _need(hidden_states, "hidden_states", (T, H), dt)
+    _need(router_weight, "router_weight", (E, H), dt)
+    if router_bias is not None:
+        _need(router_bias, "router_bias", (E,), torch.float32)
+    if shared_gate is not None:
+        _need(shared_gate, "shared_gate", (H,), dt)
+    dev = hidden_states.device
+    out = {
+        "logits": torch.empty((T, E), dtype=torch.float32, device=dev),
+        "topk_ids": torch.empty((T, top_k), dtype=torch.int32, device=dev),
+        "topk_weights": torch.empty((T, top_k), dtype=torch.float32, device=dev),
+    }
+    if return_probs:
+        out["probs"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if shared_gate is not None:
+        out["shared_gate_logit"] = torch.empty((T,), dtype=torch.float32, device=dev)
+    st = lib.moe_router_topk(_ptr(hidden_states), _ptr(router_weight), _ptr(router_bias), _ptr(shared_gate),
+                             T, H, E, int(top_k), int(bool(renormalize)), _dtype_code(dt),
+                             _ptr(out["logits"]), _ptr(out.get("probs")), _ptr(out["topk_ids"]),
+                             _ptr(out["topk_weights"]), _ptr(out.get("shared_gate_logit")), _stream(stream))
+    _check("moe_router_topk", st)
+    return out
+
+
+def moe_dispatch_plan(topk_ids: torch.Tensor, topk_weights: Optional[torch.Tensor], num_experts: int,
+                      stream=None) -> Dict[str, torch.Tensor]:
+    """Token-major assignments -> expert-major plan (include/moe.h: moe_dispatch_plan).
+
+    Returns int32 ``counts [E]``, ``offsets [E+1]``, ``perm [P]``, ``inv [P]``,
+    ``packed_ids [P]`` and f32 ``packed_w [P]`` (when weights are given).
+    """
+    lib = load_library()
+    T, k = topk_ids.shape
+    _need(topk_ids, "topk_ids", (T, k), torch.int32)
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", (T, k), torch.float32)
+    dev = topk_ids.device
+    P = T * k
+    out = {
+        "counts": torch.empty((num_experts,), dtype=torch.int32, device=dev),
+        "offsets": torch.empty((num_experts + 1,), dtype=torch.int32, device=dev),
+        "perm": torch.empty((P,), dtype=torch.int32, device=dev),
+        "inv": torch.empty((P,), dtype=torch.int32, device=dev),
+        "packed_ids": torch.empty((P,), dtype=torch.int32, device=dev),
+    }
+    if topk_weights is not None:
+        out["packed_w"] = torch.empty((P,), dtype=torch.float32, device=dev)
+    ws_bytes = lib.moe_dispatch_workspace_size(T, k, num_experts)
+    ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
+    st = lib.moe_dispatch_plan(_ptr(topk_ids), _ptr(topk_weights), T, k, int(num_experts), _ptr(out["counts"]),
+                               _ptr(out["offsets"]), _ptr(out["perm"]), _ptr(out["inv"]), _ptr(out["packed_ids"]),
+                               _ptr(out.get("packed_w")), _ptr(ws), ws.numel(), _stream(stream))
+    _check("moe_dispatch_plan", st)
+    return out
+
+
+def moe_grouped_ffn(hidden_states: torch.Tensor, packed_token_indices: Optional[torch.Tensor],
+                    expert_offsets: Optional[torch.Tensor], w13: torch.Tensor, w2: torch.Tensor, top_k: int,
+                    stream=None) -> torch.Tensor:
+    """Grouped SwiGLU experts over the expert-major layout (include/moe.h: moe_grouped_ffn).
+
+    Returns the packed expert outputs ``[T*top_k, H]`` float32 (routing weights not applied).
+    """
+    lib = load_library()
+    T, H = hidden_states.shape
+    E, twoI, _ = w13.shape
+    I = twoI // 2
+    dt = hidden_states.dtype
+    P = T * top_k
+    _need(hidden_states, "hidden_states", (T, H), dt)
+    _need(w13, "w13", (E, 2 * I, H), dt)
+    _need(w2, "w2", (E, H, I), dt)
+    if packed_token_indices is not None:
+        _need(packed_token_indices, "packed_token_indices", (P,), torch.int32)
+    if expert_offsets is not None:
+        _need(expert_offsets, "expert_offsets", (E + 1,), torch.int32)
+    dev = hidden_states.device
+    y = torch.empty((P, H), dtype=torch.float32, device=dev)
+    ws_bytes = lib.moe_grouped_ffn_workspace_size(T, top_k, E, I, _dtype_code(dt))
+    ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
+    st = lib.moe_grouped_ffn(_ptr(hidden_states), _ptr(packed_token_indices), _ptr(expert_offsets), _ptr(w13),
+                             _ptr(w2), T, H, E, int(top_k), I, _dtype_code(dt), _ptr(y), _ptr(ws), ws.numel(),
+                             _stream(stream))
+    _check("moe_grouped_ffn", st)
+    return y
+
+
+def moe_combine(packed_expert_outputs: torch.Tensor, inverse_permutation: torch.Tensor, topk_weights: torch.Tensor,
+                shared_output: Optional[torch.Tensor] = None, shared_gate_logit: Optional[torch.Tensor] = None,
+                out_dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
+    """Weighted combine to token order (include/moe.h: moe_combine)."""
+    lib = load_library()
+    T, k = topk_weights.shape
+    H = packed_expert_outputs.shape[1]
+    _need(packed_expert_outputs, "packed_expert_outputs", (T * k, H), torch.float32)
+    _need(inverse_permutation, "inverse_permutation", (T * k,), torch.int32)
+    _need(topk_weights, "topk_weights", (T, k), torch.float32)
+    if shared_output is not None:
+        _need(shared_output, "shared_output", (T, H), torch.float32)
+    if shared_gate_logit is not None:
+        _need(shared_gate_logit, "shared_gate_logit", (T,), torch.float32)
+    out = torch.empty((T, H), dtype=out_dtype, device=packed_expert_outputs.device)
+    st = lib.moe_combine(_ptr(packed_expert_outputs), _ptr(inverse_permutation), _ptr(topk_weights),
+                         _ptr(shared_output), _ptr(shared_gate_logit), T, H, k, _dtype_code(out_dtype), _ptr(out),
+                         _stream(stream))
+    _check("moe_combine", st)
+    return out
+
+
+def moe_forward_workspace_size(T: int, H: int, E: int, k: int, I: int, Is: int, dtype: torch.dtype) -> int:
+    return int(load_library().moe_forward_workspace_size(T, H, E, k, I, Is, _dtype_code(dtype)))
+
+
+def moe_forward(hidden_states: torch.Tensor, router_weight: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor,
+                top_k: int, router_bias: Optional[torch.Tensor] = None, shared_w13: Optional[torch.Tensor] = None,
+                shared_w2: Optional[torch.Tensor] = None, shared_gate: Optional[torch.Tensor] = None,
+                renormalize: bool = True, out_dtype: torch.dtype = torch.float32, return_routing: bool = False,
+                workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, stream=None):
+    """Whole layer forward (include/moe.h: moe_forward).
+
+    Returns ``out [T,H]``; with ``return_routing`` a dict with ``out``,
+    ``topk_ids``, ``topk_weights`` and ``logits``.
+    """
+    lib = load_library()
+    T, H = hidden_states.shape
+    E = router_weight.shape[0]
+    I = w13.shape[1] // 2
+    dt = hidden_states.dtype
+    _need(hidden_states, "hidden_states", (T, H), dt)
+    _need(router_weight, "router_weight", (E, H), dt)
+    _need(w13, "w13", (E, 2 * I, H), dt)
+    _need(w2, "w2", (E, H, I), dt)
+    if router_bias is not None:
+        _need(router_bias, "router_bias", (E,), torch.float32)
+    Is = 0
+    if shared_w13 is not None:
+        Is = shared_w13.shape[0] // 2
+        _need(shared_w13, "shared_w13", (2 * Is, H), dt)
+        _need(shared_w2, "shared_w2", (H, Is), dt)
+        _need(shared_gate, "shared_gate", (H,), dt)
+    dev = hidden_states.device
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=dev)
+    else:
+        _need(out, "out", (T, H), out_dtype)
+    ws_bytes = lib.moe_forward_workspace_size(T, H, E, top_k, I, Is, _dtype_code(dt))
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
+    ids = wts = logits = None
+    if return_routing:
+        ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+        wts = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    st = lib.moe_forward(_ptr(hidden_states), _ptr(router_weight), _ptr(router_bias), _ptr(w13), _ptr(w2),
+                         _ptr(shared_w13), _ptr(shared_w2), _ptr(shared_gate), T, H, E, int(top_k), I, Is,
+                         int(bool(renormalize)), _dtype_code(dt), _dtype_code(out_dtype), _ptr(out), _ptr(ids),
+                         _ptr(wts), _ptr(logits), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("moe_forward", st)
+    if return_routing:
+        return {"out": out, "topk_ids": ids, "topk_weights": wts, "logits": logits}
+    return out
+
+
+class MoeLayer:
+    """One bound MoE layer with a reusable workspace and output buffer.
+
+    Mirrors the explicit-layer binding of the DWDP README ("How To Use",
+    ``build_reference(hidden_size, num_experts, top_k, experts)``): the expert
+    weights are given as the fused ``w13 [E, 2I, H]`` and ``w2 [E, H, I]``.
+    ``forward`` allocates nothing once the layer has seen the largest token
+    count it will be called with.
+    """
+
+    def __init__(self, router_weight, w13, w2, top_k, router_bias=None, shared_w13=None, shared_w2=None,
+                 shared_gate=None, renormalize=True, out_dtype=torch.float32):
+        self.router_weight, self.w13, self.w2 = router_weight, w13, w2
+        self.router_bias = router_bias
+        self.shared_w13, self.shared_w2, self.shared_gate = shared_w13, shared_w2, shared_gate
+        self.top_k = int(top_k)
+        self.renormalize = renormalize
+        self.out_dtype = out_dtype
+        self.hidden_size = w13.shape[2]
+        self.num_experts = w13.shape[0]
+        self.intermediate_size = w13.shape[1] // 2
+        self.shared_intermediate_size = 0 if shared_w13 is None else shared_w13.shape[0] // 2
+        self._ws = None
+        self._out = None
+
+    def workspace_bytes(self, num_tokens: int) -> int:
+        return moe_forward_workspace_size(num_tokens, self.hidden_size, self.num_experts, self.top_k,
+                                          self.intermediate_size, self.shared_intermediate_size, self.w13.dtype)
+
+    def reserve(self, num_tokens: int, device) -> None:
+        need = max(self.workspace_bytes(num_tokens), 256)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty((need,), dtype=torch.uint8, device=device)
+        if self._out is None or self._out.shape[0] < num_tokens:
+            self._out = torch.empty((num_tokens, self.hidden_size), dtype=self.out_dtype, device=device)
+
+    def forward(self, x: torch.Tensor, stream=None) -> torch.Tensor:
+        T = x.shape[0]
+        self.reserve(T, x.device)
+        out = self._out[:T]
+        return moe_forward(x, self.router_weight, self.w13, self.w2, self.top_k, self.router_bias, self.shared_w13,
+                           self.shared_w2, self.shared_gate, self.renormalize, self.out_dtype,
+                           workspace=self._ws, out=out, stream=stream)
+
+    __call__ = forward
+
+
+def profile_enable(on: bool = True) -> None:
+    """Bracket every library kernel launch with HIP events (see moe_profile_enable)."""
+    load_library().moe_profile_enable(1 if on else 0)
+
+
+def profile_collect() -> Dict[str, tuple]:
+    """Wait for recorded events; return {kernel name: (total ms, launches)} and clear."""
+    lib = load_library()
+    cap = 64
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_double * cap)()
+    cnt = (_i64 * cap)()
+    n = lib.moe_profile_collect(names, ms, cnt, cap)
+    return {names[i].decode(): (ms[i], int(cnt[i])) for i in range(min(n, cap))}

@@ -1,0 +1,504 @@
+// C ABI of the MoE layer forward: host-side argument checks, workspace
+// carving and launch sequencing.  Every check runs before anything is
+// enqueued, so a failed call leaves the stream untouched.
+//
+// Pipeline ([DWDP README "Runtime Integration Layer"]):
+//   router (logits GEMM -> top-k/softmax) -> dispatch plan (hist -> scan ->
+//   scatter) -> [shared expert gate/up -> down] -> experts gate/up+SwiGLU ->
+//   experts down -> combine.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+moe_status succeed() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return succeed();
+  return fail(MOE_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+size_t dtype_size(int dtype) { return dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+// Common size checks; returns MOE_OK or an error with the message set.
+moe_status check_sizes(int64_t T, int64_t H, int64_t E, int64_t k, int dtype, bool need_h) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "num_tokens is negative");
+  if (E < 1) return fail(MOE_ERR_INVALID_ARG, "num_experts must be >= 1");
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "num_experts > 512 is not supported");
+  if (k < 1 || k > E) return fail(MOE_ERR_INVALID_ARG, "top_k must be in [1, num_experts]");
+  if (T * k >= (int64_t)1 << 31) return fail(MOE_ERR_UNSUPPORTED, "num_tokens * top_k must be < 2^31");
+  if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16) return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
+  if (need_h) {
+    if (H < 1) return fail(MOE_ERR_INVALID_ARG, "hidden_size must be >= 1");
+    if (dtype == MOE_DTYPE_BF16 && H % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16 needs hidden_size % 64 == 0");
+    if (dtype == MOE_DTYPE_F32 && H % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "f32 needs hidden_size % 8 == 0");
+  }
+  return MOE_OK;
+}
+
+moe_status check_inter(int64_t I, int dtype, const char* name) {
+  if (I < 1) return fail(MOE_ERR_INVALID_ARG, std::string(name) + " must be >= 1");
+  if (dtype == MOE_DTYPE_BF16 && I % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, std::string("bf16 needs ") + name + " % 64 == 0");
+  if (dtype == MOE_DTYPE_F32 && I % 16 != 0) return fail(MOE_ERR_UNSUPPORTED, std::string("f32 needs ") + name + " % 16 == 0");
+  return MOE_OK;
+}
+
+#define REQUIRE_PTR(p)                                                       \
+  do {                                                                       \
+    if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, #p " is NULL");     \
+  } while (0)
+#define REQUIRE_ALIGNED(p)                                                              \
+  do {                                                                                  \
+    if ((p) != nullptr && !aligned16(p))                                                \
+      return fail(MOE_ERR_UNSUPPORTED, #p " is not 16-byte aligned");                   \
+  } while (0)
+#define RETURN_IF_ERR(x)              \
+  do {                                \
+    moe_status _st = (x);             \
+    if (_st != MOE_OK) return _st;    \
+  } while (0)
+
+// -------------------------------------------------------------- workspace
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+struct ForwardLayout {
+  float* logits;
+  float* gate_logit;
+  int32_t* ids;
+  float* weights;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv;
+  int32_t* packed_ids;
+  void* dispatch_scratch;
+  void* h;
+  float* y;
+  void* hs;
+  float* ys;
+  size_t bytes;
+};
+
+ForwardLayout carve_forward(void* ws, int64_t T, int64_t H, int64_t E, int64_t k, int64_t I, int64_t Is, int dtype) {
+  const int64_t P = T * k;
+  Carver c(ws);
+  ForwardLayout L;
+  L.logits = c.take<float>((size_t)(T * E));
+  L.gate_logit = c.take<float>((size_t)(Is > 0 ? T : 0));
+  L.ids = c.take<int32_t>((size_t)P);
+  L.weights = c.take<float>((size_t)P);
+  L.counts = c.take<int32_t>((size_t)E);
+  L.offsets = c.take<int32_t>((size_t)E + 1);
+  L.perm = c.take<int32_t>((size_t)P);
+  L.inv = c.take<int32_t>((size_t)P);
+  L.packed_ids = c.take<int32_t>((size_t)P);
+  L.dispatch_scratch = c.take<char>(moe::dispatch_scratch_bytes(P, E));
+  L.h = c.take<char>((size_t)(P * I) * dtype_size(dtype));
+  L.y = c.take<float>((size_t)(P * H));
+  L.hs = c.take<char>((size_t)(Is > 0 ? T * Is : 0) * dtype_size(dtype));
+  L.ys = c.take<float>((size_t)(Is > 0 ? T * H : 0));
+  L.bytes = c.off;
+  return L;
+}
+
+// -------------------------------------------------------------- stage launches
+moe::GemmArgs gemm_args() {
+  moe::GemmArgs a;
+  std::memset(&a, 0, sizeof(a));
+  return a;
+}
+
+hipError_t run_router(const void* x, const void* wr, const float* bias, const void* gate, int T, int H, int E, int k,
+                      int renorm, int dtype, float* logits, float* probs, int32_t* ids, float* weights,
+                      float* gate_logit, hipStream_t s) {
+  hipError_t e;
+  if (dtype == MOE_DTYPE_BF16) {
+    moe::GemmArgs a = gemm_args();
+    a.A = static_cast<const uint16_t*>(x);
+    a.M = T;
+    a.G = 1;
+    a.B = static_cast<const uint16_t*>(wr);
+    a.b_group_stride = 0;
+    a.b_extra = static_cast<const uint16_t*>(gate);
+    a.K = H;
+    a.N = E + (gate ? 1 : 0);
+    a.out = logits;
+    a.ldo = E;
+    a.bias = bias;
+    a.extra_out = gate_logit;
+    e = moe::launch_grouped_gemm_bf16(a, moe::EPI_ROUTER, s, "router_logits_bf16");
+  } else {
+    e = moe::launch_router_logits_f32(static_cast<const float*>(x), static_cast<const float*>(wr), bias,
+                                      static_cast<const float*>(gate), T, H, E, logits, gate_logit, s);
+  }
+  if (e != hipSuccess) return e;
+  return moe::launch_topk(logits, T, E, k, renorm, ids, weights, probs, s);
+}
+
+hipError_t run_ffn(const void* x, const int32_t* gather, const int32_t* offsets, const void* w13, const void* w2,
+                   int P, int H, int E, int I, int dtype, void* h, float* y, hipStream_t s, bool shared) {
+  hipError_t e;
+  if (dtype == MOE_DTYPE_BF16) {
+    moe::GemmArgs a = gemm_args();
+    a.A = static_cast<const uint16_t*>(x);
+    a.gather = gather;
+    a.offsets = offsets;
+    a.M = P;
+    a.G = E;
+    a.B = static_cast<const uint16_t*>(w13);
+    a.b_group_stride = (int64_t)2 * I * H;
+    a.K = H;
+    a.N = I;
+    a.up_row0 = I;
+    a.out = h;
+    a.ldo = I;
+    e = moe::launch_grouped_gemm_bf16(a, moe::EPI_SWIGLU, s, shared ? "shared_gate_up_bf16" : "ffn_gate_up_bf16");
+    if (e != hipSuccess) return e;
+    moe::GemmArgs b = gemm_args();
+    b.A = static_cast<const uint16_t*>(h);
+    b.gather = nullptr;
+    b.offsets = offsets;
+    b.M = P;
+    b.G = E;
+    b.B = static_cast<const uint16_t*>(w2);
+    b.b_group_stride = (int64_t)H * I;
+    b.K = I;
+    b.N = H;
+    b.out = y;
+    b.ldo = H;
+    return moe::launch_grouped_gemm_bf16(b, moe::EPI_F32, s, shared ? "shared_down_bf16" : "ffn_down_bf16");
+  }
+  e = moe::launch_ffn_gate_up_f32(static_cast<const float*>(x), gather, offsets, static_cast<const float*>(w13), P,
+                                  H, E, I, static_cast<float*>(h), s);
+  if (e != hipSuccess) return e;
+  return moe::launch_ffn_down_f32(static_cast<const float*>(h), offsets, static_cast<const float*>(w2), P, H, E, I,
+                                  y, s);
+}
+
+// -------------------------------------------------------------- profiling
+struct ProfRecord {
+  const char* name;
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof;
+thread_local int g_prof_open = -1;
+
+}  // namespace
+
+namespace moe {
+
+void profile_begin(const char* name, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_open = -1;
+  if (!g_prof_on) return;
+  ProfRecord r{name, nullptr, nullptr};
+  if (hipEventCreate(&r.start) != hipSuccess) return;
+  if (hipEventCreate(&r.stop) != hipSuccess) {
+    (void)hipEventDestroy(r.start);
+    return;
+  }
+  (void)hipEventRecord(r.start, s);
+  g_prof.push_back(r);
+  g_prof_open = (int)g_prof.size() - 1;
+}
+
+void profile_end(hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (g_prof_open < 0 || g_prof_open >= (int)g_prof.size()) return;
+  (void)hipEventRecord(g_prof[g_prof_open].stop, s);
+  g_prof_open = -1;
+}
+
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+}  // namespace moe
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error_message(void) { return g_last_error.c_str(); }
+
+moe_status moe_router_topk(const void* hidden_states, const void* router_weight, const float* router_bias,
+                           const void* shared_gate, int64_t num_tokens, int64_t hidden_size, int64_t num_experts,
+                           int64_t top_k, int renormalize, int dtype, float* router_logits, float* routing_probs,
+                           int32_t* topk_ids, float* topk_weights, float* shared_gate_logit, void* stream) {
+  RETURN_IF_ERR(check_sizes(num_tokens, hidden_size, num_experts, top_k, dtype, true));
+  if (num_tokens == 0) return succeed();
+  REQUIRE_PTR(hidden_states);
+  REQUIRE_PTR(router_weight);
+  REQUIRE_PTR(topk_ids);
+  REQUIRE_PTR(topk_weights);
+  REQUIRE_PTR(router_logits);
+  if ((shared_gate == nullptr) != (shared_gate_logit == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "shared_gate and shared_gate_logit must be given together");
+  REQUIRE_ALIGNED(hidden_states);
+  REQUIRE_ALIGNED(router_weight);
+  REQUIRE_ALIGNED(shared_gate);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(run_router(hidden_states, router_weight, router_bias, shared_gate, (int)num_tokens,
+                               (int)hidden_size, (int)num_experts, (int)top_k, renormalize ? 1 : 0, dtype,
+                               router_logits, routing_probs, topk_ids, topk_weights, shared_gate_logit, s),
+                    "moe_router_topk");
+}
+
+size_t moe_dispatch_workspace_size(int64_t num_tokens, int64_t top_k, int64_t num_experts) {
+  if (num_tokens < 0 || top_k < 1 || num_experts < 1) return 0;
+  return align_up(moe::dispatch_scratch_bytes(num_tokens * top_k, num_experts));
+}
+
+moe_status moe_dispatch_plan(const int32_t* topk_ids, const float* topk_weights, int64_t num_tokens, int64_t top_k,
+                             int64_t num_experts, int32_t* expert_counts, int32_t* expert_offsets,
+                             int32_t* token_permutation, int32_t* inverse_permutation, int32_t* packed_token_indices,
+                             float* packed_routing_weights, void* workspace, size_t workspace_bytes, void* stream) {
+  RETURN_IF_ERR(check_sizes(num_tokens, 1, num_experts, top_k, MOE_DTYPE_F32, false));
+  if (num_tokens == 0) return succeed();
+  REQUIRE_PTR(topk_ids);
+  REQUIRE_PTR(expert_counts);
+  REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(token_permutation);
+  REQUIRE_PTR(inverse_permutation);
+  REQUIRE_PTR(packed_token_indices);
+  if ((topk_weights == nullptr) != (packed_routing_weights == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "topk_weights and packed_routing_weights must be given together");
+  const size_t need = moe_dispatch_workspace_size(num_tokens, top_k, num_experts);
+  if (workspace == nullptr || workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(moe::launch_dispatch(topk_ids, topk_weights, (int)num_tokens, (int)top_k, (int)num_experts,
+                                         expert_counts, expert_offsets, token_permutation, inverse_permutation,
+                                         packed_token_indices, packed_routing_weights, workspace, s),
+                    "moe_dispatch_plan");
+}
+
+size_t moe_grouped_ffn_workspace_size(int64_t num_tokens, int64_t top_k, int64_t num_experts,
+                                      int64_t intermediate_size, int dtype) {
+  (void)num_experts;
+  if (num_tokens < 0 || top_k < 1 || intermediate_size < 1) return 0;
+  return align_up((size_t)(num_tokens * top_k * intermediate_size) * dtype_size(dtype));
+}
+
+moe_status moe_grouped_ffn(const void* hidden_states, const int32_t* packed_token_indices,
+                           const int32_t* expert_offsets, const void* w13, const void* w2, int64_t num_tokens,
+                           int64_t hidden_size, int64_t num_experts, int64_t top_k, int64_t intermediate_size,
+                           int dtype, float* packed_expert_outputs, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  RETURN_IF_ERR(check_sizes(num_tokens, hidden_size, num_experts, top_k, dtype, true));
+  RETURN_IF_ERR(check_inter(intermediate_size, dtype, "intermediate_size"));
+  if (num_tokens == 0) return succeed();
+  REQUIRE_PTR(hidden_states);
+  REQUIRE_PTR(w13);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR(packed_expert_outputs);
+  if (expert_offsets == nullptr && num_experts != 1)
+    return fail(MOE_ERR_INVALID_ARG, "expert_offsets may be NULL only with num_experts == 1");
+  if (packed_token_indices == nullptr && top_k != 1)
+    return fail(MOE_ERR_INVALID_ARG, "packed_token_indices may be NULL only with top_k == 1");
+  REQUIRE_ALIGNED(hidden_states);
+  REQUIRE_ALIGNED(w13);
+  REQUIRE_ALIGNED(w2);
+  REQUIRE_ALIGNED(packed_expert_outputs);
+  const size_t need = moe_grouped_ffn_workspace_size(num_tokens, top_k, num_experts, intermediate_size, dtype);
+  if (workspace == nullptr || workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small");
+  REQUIRE_ALIGNED(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int P = (int)(num_tokens * top_k);
+  return hip_status(run_ffn(hidden_states, packed_token_indices, expert_offsets, w13, w2, P, (int)hidden_size,
+                            (int)num_experts, (int)intermediate_size, dtype, workspace, packed_expert_outputs, s,
+                            false),
+                    "moe_grouped_ffn");
+}
+
+moe_status moe_combine(const float* packed_expert_outputs, const int32_t* inverse_permutation,
+                       const float* topk_weights, const float* shared_output, const float* shared_gate_logit,
+                       int64_t num_tokens, int64_t hidden_size, int64_t top_k, int out_dtype, void* output,
+                       void* stream) {
+  if (num_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "num_tokens is negative");
+  if (top_k < 1) return fail(MOE_ERR_INVALID_ARG, "top_k must be >= 1");
+  if (hidden_size < 1) return fail(MOE_ERR_INVALID_ARG, "hidden_size must be >= 1");
+  if (hidden_size % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "hidden_size % 8 != 0");
+  if (out_dtype != MOE_DTYPE_F32 && out_dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "out_dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
+  if (num_tokens * top_k >= (int64_t)1 << 31) return fail(MOE_ERR_UNSUPPORTED, "num_tokens * top_k must be < 2^31");
+  if (num_tokens == 0) return succeed();
+  REQUIRE_PTR(packed_expert_outputs);
+  REQUIRE_PTR(inverse_permutation);
+  REQUIRE_PTR(topk_weights);
+  REQUIRE_PTR(output);
+  if (shared_gate_logit != nullptr && shared_output == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "shared_gate_logit given without shared_output");
+  REQUIRE_ALIGNED(packed_expert_outputs);
+  REQUIRE_ALIGNED(shared_output);
+  REQUIRE_ALIGNED(output);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(moe::launch_combine(packed_expert_outputs, inverse_permutation, topk_weights, shared_output,
+                                        shared_gate_logit, (int)num_tokens, (int)hidden_size, (int)top_k,
+                                        out_dtype == MOE_DTYPE_BF16, output, s),
+                    "moe_combine");
+}
+
+size_t moe_forward_workspace_size(int64_t num_tokens, int64_t hidden_size, int64_t num_experts, int64_t top_k,
+                                  int64_t intermediate_size, int64_t shared_intermediate_size, int dtype) {
+  if (num_tokens < 0 || hidden_size < 1 || num_experts < 1 || top_k < 1 || intermediate_size < 1 ||
+      shared_intermediate_size < 0)
+    return 0;
+  return carve_forward(nullptr, num_tokens, hidden_size, num_experts, top_k, intermediate_size,
+                       shared_intermediate_size, dtype)
+      .bytes;
+}
+
+moe_status moe_forward(const void* hidden_states, const void* router_weight, const float* router_bias, const void* w13,
+                       const void* w2, const void* shared_w13, const void* shared_w2, const void* shared_gate,
+                       int64_t num_tokens, int64_t hidden_size, int64_t num_experts, int64_t top_k,
+                       int64_t intermediate_size, int64_t shared_intermediate_size, int renormalize, int dtype,
+                       int out_dtype, void* output, int32_t* topk_ids_out, float* topk_weights_out,
+                       float* router_logits_out, void* workspace, size_t workspace_bytes, void* stream) {
+  RETURN_IF_ERR(check_sizes(num_tokens, hidden_size, num_experts, top_k, dtype, true));
+  RETURN_IF_ERR(check_inter(intermediate_size, dtype, "intermediate_size"));
+  const int nshared = (shared_w13 != nullptr) + (shared_w2 != nullptr) + (shared_gate != nullptr);
+  if (nshared != 0 && nshared != 3)
+    return fail(MOE_ERR_INVALID_ARG, "shared_w13, shared_w2 and shared_gate must be given together");
+  const int64_t Is = nshared ? shared_intermediate_size : 0;
+  if (nshared) RETURN_IF_ERR(check_inter(Is, dtype, "shared_intermediate_size"));
+  if (out_dtype != MOE_DTYPE_F32 && out_dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "out_dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
+  if (num_tokens == 0) return succeed();
+  REQUIRE_PTR(hidden_states);
+  REQUIRE_PTR(router_weight);
+  REQUIRE_PTR(w13);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR(output);
+  REQUIRE_ALIGNED(hidden_states);
+  REQUIRE_ALIGNED(router_weight);
+  REQUIRE_ALIGNED(w13);
+  REQUIRE_ALIGNED(w2);
+  REQUIRE_ALIGNED(shared_w13);
+  REQUIRE_ALIGNED(shared_w2);
+  REQUIRE_ALIGNED(shared_gate);
+  REQUIRE_ALIGNED(output);
+  const size_t need = moe_forward_workspace_size(num_tokens, hidden_size, num_experts, top_k, intermediate_size, Is,
+                                                 dtype);
+  if (workspace == nullptr || workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small");
+  REQUIRE_ALIGNED(workspace);
+
+  const int T = (int)num_tokens, H = (int)hidden_size, E = (int)num_experts, k = (int)top_k;
+  const int I = (int)intermediate_size;
+  const int P = T * k;
+  ForwardLayout L = carve_forward(workspace, num_tokens, hidden_size, num_experts, top_k, intermediate_size, Is, dtype);
+  float* logits = router_logits_out ? router_logits_out : L.logits;
+  int32_t* ids = topk_ids_out ? topk_ids_out : L.ids;
+  float* weights = topk_weights_out ? topk_weights_out : L.weights;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  hipError_t e = run_router(hidden_states, router_weight, router_bias, Is ? shared_gate : nullptr, T, H, E, k,
+                            renormalize ? 1 : 0, dtype, logits, nullptr, ids, weights, Is ? L.gate_logit : nullptr, s);
+  if (e != hipSuccess) return hip_status(e, "moe_forward(router)");
+  e = moe::launch_dispatch(ids, nullptr, T, k, E, L.counts, L.offsets, L.perm, L.inv, L.packed_ids, nullptr,
+                           L.dispatch_scratch, s);
+  if (e != hipSuccess) return hip_status(e, "moe_forward(dispatch)");
+  if (Is) {
+    e = run_ffn(hidden_states, nullptr, nullptr, shared_w13, shared_w2, T, H, 1, (int)Is, dtype, L.hs, L.ys, s, true);
+    if (e != hipSuccess) return hip_status(e, "moe_forward(shared expert)");
+  }
+  e = run_ffn(hidden_states, L.packed_ids, L.offsets, w13, w2, P, H, E, I, dtype, L.h, L.y, s, false);
+  if (e != hipSuccess) return hip_status(e, "moe_forward(experts)");
+  e = moe::launch_combine(L.y, L.inv, weights, Is ? L.ys : nullptr, Is ? L.gate_logit : nullptr, T, H, k,
+                          out_dtype == MOE_DTYPE_BF16, output, s);
+  return hip_status(e, "moe_forward(combine)");
+}
+
+void moe_profile_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = enable != 0;
+}
+
+int moe_profile_collect(const char** names, double* total_ms, int64_t* launches, int capacity) {
+  std::vector<ProfRecord> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    recs.swap(g_prof);
+  }
+  std::vector<const char*> nm;
+  std::vector<double> ms;
+  std::vector<int64_t> cnt;
+  for (const ProfRecord& r : recs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.stop) == hipSuccess && hipEventElapsedTime(&t, r.start, r.stop) == hipSuccess) {
+      size_t i = 0;
+      while (i < nm.size() && std::strcmp(nm[i], r.name) != 0) ++i;
+      if (i == nm.size()) {
+        nm.push_back(r.name);
+        ms.push_back(0.0);
+        cnt.push_back(0);
+      }
+      ms[i] += t;
+      cnt[i] += 1;
+    }
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  for (size_t i = 0; i < nm.size() && (int)i < capacity; ++i) {
+    if (names) names[i] = nm[i];
+    if (total_ms) total_ms[i] = ms[i];
+    if (launches) launches[i] = cnt[i];
+  }
+  return (int)nm.size();
+}
+
+}  // extern "C"

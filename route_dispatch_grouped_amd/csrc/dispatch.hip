@@ -1,0 +1,164 @@
+// Dispatch plan: a deterministic counting sort of the token-major assignments
+// by expert id.  [DWDP README "Dispatcher Module": per-expert counts, expert
+// offsets, token permutation, inverse permutation, packed token indices and
+// packed routing weights; metrale ep_dispatch.rs: assignments a = t*k + j are
+// kept in the order given]
+//
+// The P = T*k assignments are cut into segments of 256 consecutive indices, one
+// wavefront per segment.
+//   1. hist    each wave counts its segment per expert in LDS and writes
+//              seg[e][u] (expert-major, U = number of segments).
+//   2. scan    one workgroup: per expert, an exclusive scan of seg[e][0..U) in
+//              place (wave-parallel over u); totals -> counts; an exclusive
+//              scan over experts -> offsets (offsets[E] = P).
+//   3. scatter each wave re-reads its segment 64 assignments at a time, in
+//              index order.  Lanes holding the same expert id find each other
+//              with ballots; a lane's rank among them plus the wave's running
+//              count for that expert plus seg[e][u] plus offsets[e] is the
+//              assignment's position p.  Equal ids therefore keep index order
+//              (stability), and no position depends on the timing of atomics.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kSeg = kDispatchSegment;  // 256 assignments per wave
+constexpr int kMaxE = MOE_MAX_GROUPS_INTERNAL;
+
+__global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __restrict__ ids, int P, int E, int U,
+                                                            int32_t* __restrict__ seg) {
+  __shared__ int cnt[4][kMaxE];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int u = blockIdx.x * 4 + w;
+  for (int e = lane; e < E; e += 64) cnt[w][e] = 0;
+  __syncthreads();
+  if (u < U) {
+#pragma unroll
+    for (int r = 0; r < kSeg / 64; ++r) {
+      const int a = u * kSeg + r * 64 + lane;
+      if (a < P) {
+        const int id = ids[a];
+        if ((unsigned)id < (unsigned)E) atomicAdd(&cnt[w][id], 1);  // ids outside [0, E) are a caller error
+      }
+    }
+  }
+  __syncthreads();
+  if (u < U)
+    for (int e = lane; e < E; e += 64) seg[(int64_t)e * U + u] = cnt[w][e];
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Single workgroup of 1024 threads (16 waves).
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ seg, int U, int E, int P,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets) {
+  __shared__ int tot[kMaxE];
+  __shared__ int wsum[16];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  for (int e = w; e < E; e += 16) {
+    int carry = 0;
+    for (int u0 = 0; u0 < U; u0 += 64) {
+      const int u = u0 + lane;
+      const int c = (u < U) ? seg[(int64_t)e * U + u] : 0;
+      const int incl = wave_incl_scan(c, lane);
+      if (u < U) seg[(int64_t)e * U + u] = carry + incl - c;
+      carry += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) tot[e] = carry;
+  }
+  __syncthreads();
+  // exclusive scan of tot over experts (E <= 512 <= 1024 threads)
+  const int i = threadIdx.x;
+  const int v = (i < E) ? tot[i] : 0;
+  const int incl = wave_incl_scan(v, lane);
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int q = 0; q < w; ++q) base += wsum[q];
+  if (i < E) {
+    counts[i] = v;
+    offsets[i] = base + incl - v;
+  }
+  if (i == 0) offsets[E] = P;
+}
+
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(
+    const int32_t* __restrict__ ids, const float* __restrict__ wts, int P, int k, int E, int U,
+    const int32_t* __restrict__ seg, const int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv, int32_t* __restrict__ packed_ids, float* __restrict__ packed_w) {
+  __shared__ int run[4][kMaxE];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int u = blockIdx.x * 4 + w;
+  for (int e = lane; e < E; e += 64) run[w][e] = 0;
+  __syncthreads();
+  if (u >= U) return;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+#pragma unroll 1
+  for (int r = 0; r < kSeg / 64; ++r) {
+    const int a = u * kSeg + r * 64 + lane;
+    int id = (a < P) ? ids[a] : -1;
+    const bool valid = (unsigned)id < (unsigned)E;
+    if (!valid) id = -1;
+    uint64_t todo = __ballot(valid);
+    uint64_t peers = 0;
+    while (todo) {
+      const int leader = __builtin_ctzll(todo);
+      const int lid = __builtin_amdgcn_readlane(id, leader);
+      const uint64_t m = __ballot(id == lid);
+      if (id == lid) peers = m;
+      todo &= ~m;
+    }
+    int pos = 0;
+    if (valid) pos = offsets[id] + seg[(int64_t)id * U + u] + run[w][id] + __popcll(peers & lt_mask);
+    __builtin_amdgcn_wave_barrier();
+    if (valid && lane == __builtin_ctzll(peers)) run[w][id] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      perm[pos] = a;
+      inv[a] = pos;
+      packed_ids[pos] = a / k;
+      if (packed_w != nullptr) packed_w[pos] = wts[a];
+    }
+  }
+}
+
+}  // namespace
+
+size_t dispatch_scratch_bytes(int64_t P, int64_t E) {
+  const int64_t U = (P + kSeg - 1) / kSeg;
+  return (size_t)(U * E * (int64_t)sizeof(int32_t));
+}
+
+hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int E, int32_t* counts,
+                           int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* packed_ids, float* packed_w,
+                           void* scratch, hipStream_t s) {
+  const int P = T * k;
+  if (P == 0) return hipSuccess;
+  const int U = (P + kSeg - 1) / kSeg;
+  int32_t* seg = reinterpret_cast<int32_t*>(scratch);
+  const unsigned blocks = (unsigned)((U + 3) / 4);
+  profile_begin("dispatch_hist", s);
+  hipLaunchKernelGGL(dispatch_hist_kernel, dim3(blocks), dim3(256), 0, s, ids, P, E, U, seg);
+  profile_end(s);
+  profile_begin("dispatch_scan", s);
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, seg, U, E, P, counts, offsets);
+  profile_end(s);
+  profile_begin("dispatch_scatter", s);
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(blocks), dim3(256), 0, s, ids, w, P, k, E, U, seg, offsets,
+                     perm, inv, packed_ids, packed_w);
+  profile_end(s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

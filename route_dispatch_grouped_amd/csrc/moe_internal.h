@@ -1,0 +1,74 @@
+// Internal declarations shared by the HIP translation units of libmoe_mi355x.
+// Nothing here is part of the C ABI (include/moe.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define MOE_MAX_GROUPS_INTERNAL 512
+
+namespace moe {
+
+// Launch record for optional per-kernel timing (see moe_profile_enable).
+void profile_begin(const char* name, hipStream_t s);
+void profile_end(hipStream_t s);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+// ---------------------------------------------------------------- GEMM (bf16)
+// Epilogue of the grouped MFMA GEMM.
+enum GemmEpilogue {
+  EPI_SWIGLU = 0,  // paired gate/up rows -> h = silu(g) * u, stored bf16
+  EPI_F32 = 1,     // plain fp32 store
+  EPI_ROUTER = 2,  // fp32 logits (+ bias), extra column -> gate logit
+};
+
+struct GemmArgs {
+  const uint16_t* A;        // bf16 activations, rows of length K
+  const int32_t* gather;    // A row of packed row p is gather[p] (NULL: row p)
+  const int32_t* offsets;   // [G+1] packed row ranges of the groups (NULL: one group of M rows)
+  int M;                    // total packed rows (upper bound of offsets[G])
+  int G;                    // groups (experts)
+  const uint16_t* B;        // bf16 weights, per group `b_rows` rows of length K
+  int64_t b_group_stride;   // elements between groups of B
+  const uint16_t* b_extra;  // EPI_ROUTER: weight row of output column N-1 (NULL: none)
+  int K;                    // reduction length, multiple of 64
+  int N;                    // output columns (EPI_SWIGLU: I, the h width)
+  int up_row0;              // EPI_SWIGLU: first up row inside a group (= I)
+  void* out;                // EPI_SWIGLU: bf16 h; EPI_F32: f32; EPI_ROUTER: f32 logits
+  int64_t ldo;              // output row stride in elements
+  const float* bias;        // EPI_ROUTER: per-column bias or NULL
+  float* extra_out;         // EPI_ROUTER: output of column N-1 when b_extra != NULL
+};
+
+hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, GemmEpilogue epi, hipStream_t s, const char* name);
+
+// ---------------------------------------------------------------- fp32 path
+hipError_t launch_router_logits_f32(const float* x, const float* wr, const float* bias,
+                                    const float* gate, int T, int H, int E,
+                                    float* logits, float* gate_logit, hipStream_t s);
+hipError_t launch_ffn_gate_up_f32(const float* x, const int32_t* gather, const int32_t* offsets,
+                                  const float* w13, int P, int H, int E, int I,
+                                  float* h, hipStream_t s);
+hipError_t launch_ffn_down_f32(const float* h, const int32_t* offsets, const float* w2,
+                               int P, int H, int E, int I, float* y, hipStream_t s);
+
+// ---------------------------------------------------------------- router top-k
+hipError_t launch_topk(const float* logits, int T, int E, int k, int renormalize,
+                       int32_t* ids, float* weights, float* probs, hipStream_t s);
+
+// ---------------------------------------------------------------- dispatch
+constexpr int kDispatchSegment = 256;  // assignments per wave-segment
+size_t dispatch_scratch_bytes(int64_t P, int64_t E);
+hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int E,
+                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                           int32_t* packed_ids, float* packed_w, void* scratch, hipStream_t s);
+
+// ---------------------------------------------------------------- combine
+hipError_t launch_combine(const float* y, const int32_t* inv, const float* w,
+                          const float* shared, const float* shared_gate_logit,
+                          int T, int H, int k, int out_bf16, void* out, hipStream_t s);
+
+}  // namespace moe

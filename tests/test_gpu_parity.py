@@ -1,0 +1,305 @@
+"""GPU parity of every stage against the float64 oracle, through the C ABI.
+
+Staged checks feed each GPU stage the oracle's (or the GPU's own) previous
+stage, so a near-tie routing flip cannot cascade:
+  router  : GPU logits within the rigorous fp32 dot-product bound of the oracle
+            logits; GPU top-k ids == oracle selection on the GPU logits,
+            bit-exact; weights within 1e-5 relative.
+  dispatch: GPU plan == oracle plan, bit-exact (ids from the oracle and from
+            the GPU, edge cases, determinism).
+  experts : packed expert outputs within tol * rms (tol 2e-2 bf16, 1e-4 f32).
+  combine : GPU combine of GPU expert outputs == oracle combine of the same
+            values within fp32 rounding.
+  forward : end to end; ids equal outside the near-tie window; the output is
+            within tol * rms of the oracle fed the GPU routing.
+Small cases are compared element by element; the full workloads are compared
+on sampled tokens/rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_common import (device_inputs, full_inputs, gpu_forward, log, logit_error_bound, near_tie_tokens,
+                        rel_max_err, tol_for, to_device)
+
+pytestmark = pytest.mark.gpu
+
+rdg = pytest.importorskip("route_dispatch_grouped_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    rdg.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+# Small cases that span several m-tiles, n-blocks and ragged tails.
+SMALL = {
+    "tiny_fp32": workloads.config("tiny_fp32"),
+    "bf16_multi_tile": workloads.config("qwen3_30b_a3b_prefill").scaled(
+        name="bf16_multi_tile", num_tokens=1000, hidden_size=512, num_experts=8, top_k=2, intermediate_size=384),
+    "bf16_decode_shared": workloads.config("qwen15_moe_decode").scaled(
+        name="bf16_decode_shared", num_tokens=16, hidden_size=256, num_experts=60, top_k=4, intermediate_size=192,
+        shared_intermediate_size=320),
+    "bf16_mid_rows": workloads.config("qwen3_30b_a3b_prefill").scaled(
+        name="bf16_mid_rows", num_tokens=333, hidden_size=128, num_experts=16, top_k=3, intermediate_size=128),
+    "bf16_zipf_small": workloads.config("qwen3_30b_a3b_prefill_zipf").scaled(
+        name="bf16_zipf_small", num_tokens=700, hidden_size=256, intermediate_size=128),
+    "f32_ragged": workloads.config("tiny_fp32").scaled(
+        name="f32_ragged", num_tokens=77, hidden_size=40, num_experts=12, top_k=5, intermediate_size=48),
+}
+
+
+def check_router(cfg, inp, dev, tokens=None):
+    r = rdg.moe_router_topk(dev["x"], dev["router_weight"], cfg.top_k, router_bias=dev.get("router_bias"),
+                            shared_gate=dev.get("shared_gate"), renormalize=cfg.renormalize, return_probs=True)
+    Lg = r["logits"].cpu().numpy().astype(np.float64)
+    ids = r["topk_ids"].cpu().numpy()
+    w = r["topk_weights"].cpu().numpy().astype(np.float64)
+    probs = r["probs"].cpu().numpy().astype(np.float64)
+    # 1. top-k on the GPU's own logits: bit-exact
+    assert (ids == oracle.select_topk(Lg, cfg.top_k)).all()
+    # 2. weights/probs from the GPU logits
+    w_ref = oracle.routing_weights(Lg, ids, cfg.renormalize)
+    assert np.max(np.abs(w - w_ref) / np.maximum(w_ref, 1e-30)) <= 1e-5
+    p_ref = oracle.routing_probs(Lg)
+    assert np.max(np.abs(probs - p_ref)) <= 1e-5 * np.max(p_ref)
+    # 3. logits against the fp64 oracle within the rigorous fp32 bound
+    rows = np.arange(cfg.num_tokens) if tokens is None else tokens
+    L = oracle.router_logits(inp["x"][rows], inp["router_weight"], inp.get("router_bias"))
+    err = np.abs(Lg[rows] - L)
+    assert (err <= logit_error_bound(inp, rows)).all(), float(err.max())
+    if "shared_gate" in inp:
+        gl = r["shared_gate_logit"].cpu().numpy().astype(np.float64)[rows]
+        gl_ref = oracle.shared_gate_logit(inp["x"][rows], inp["shared_gate"])
+        bound = (cfg.hidden_size + 2) * 2.0 ** -24 * (np.abs(oracle.widen(inp["x"][rows])) @
+                                                       np.abs(oracle.widen(inp["shared_gate"])))
+        assert (np.abs(gl - gl_ref) <= bound + 1e-30).all()
+    return r, float(err.max())
+
+
+def check_plan_equal(gpu, ref):
+    for key in ("counts", "offsets", "perm", "inv", "packed_ids"):
+        g = gpu[key].cpu().numpy()
+        assert g.dtype == np.int32
+        assert (g == ref[key]).all(), key
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_staged_and_end_to_end(name):
+    cfg = SMALL[name]
+    log(f"[parity] {name}: {cfg}")
+    inp = workloads.generate(cfg, seed=0)
+    dev = device_inputs(inp)
+    tol = tol_for(cfg)
+
+    # router
+    r, eps = check_router(cfg, inp, dev)
+
+    # dispatch on the oracle's ids and on the GPU's ids
+    L = oracle.router_logits(inp["x"], inp["router_weight"], inp.get("router_bias"))
+    ids_o = oracle.select_topk(L, cfg.top_k)
+    w_o = oracle.routing_weights(L, ids_o, cfg.renormalize).astype(np.float32)
+    plan_o = oracle.dispatch_plan(ids_o, w_o, cfg.num_experts)
+    g = rdg.moe_dispatch_plan(to_device(ids_o), to_device(w_o), cfg.num_experts)
+    check_plan_equal(g, plan_o)
+    assert (g["packed_w"].cpu().numpy() == w_o.reshape(-1)[plan_o["perm"]]).all()
+    ids_g = r["topk_ids"].cpu().numpy()
+    plan_g = oracle.dispatch_plan(ids_g, r["topk_weights"].cpu().numpy(), cfg.num_experts)
+    g2 = rdg.moe_dispatch_plan(r["topk_ids"], r["topk_weights"], cfg.num_experts)
+    check_plan_equal(g2, plan_g)
+
+    # experts on the oracle plan
+    y = rdg.moe_grouped_ffn(dev["x"], g["packed_ids"], g["offsets"], dev["w13"], dev["w2"], cfg.top_k)
+    y_ref = oracle.expert_ffn(inp["x"], plan_o["packed_ids"], plan_o["offsets"], inp["w13"], inp["w2"])
+    err, rms = rel_max_err(y.cpu().numpy().astype(np.float64), y_ref)
+    log(f"[parity] {name}: experts max|err|/rms = {err / rms:.3e}")
+    assert err <= tol * rms
+
+    # combine of the GPU expert outputs
+    out_c = rdg.moe_combine(y, g["inv"], to_device(w_o))
+    ref_c = oracle.combine(y.cpu().numpy().astype(np.float64), plan_o["inv"], w_o.astype(np.float64))
+    err_c, rms_c = rel_max_err(out_c.cpu().numpy().astype(np.float64), ref_c)
+    assert err_c <= 1e-5 * rms_c + 1e-30
+
+    # end to end
+    f = gpu_forward(cfg, dev)
+    ids_f = f["topk_ids"].cpu().numpy()
+    w_f = f["topk_weights"].cpu().numpy().astype(np.float64)
+    assert (f["logits"].cpu().numpy() == r["logits"].cpu().numpy()).all()
+    tie = near_tie_tokens(L, max(eps, 1e-30), cfg.top_k)
+    outside = np.setdiff1d(np.arange(cfg.num_tokens), tie)
+    assert (ids_f[outside] == ids_o[outside]).all()
+    res = oracle.forward(inp, cfg.top_k, cfg.renormalize, ids=ids_f, weights=w_f)
+    err_o, rms_o = rel_max_err(f["out"].cpu().numpy().astype(np.float64), res["out"])
+    log(f"[parity] {name}: forward max|err|/rms = {err_o / rms_o:.3e}  eps={eps:.2e} near-ties={len(tie)}")
+    assert err_o <= tol * rms_o
+    # the oracle's own routing gives the same answer outside near ties
+    res_o = oracle.forward(inp, cfg.top_k, cfg.renormalize)
+    if len(tie) == 0:
+        e2, r2 = rel_max_err(f["out"].cpu().numpy().astype(np.float64), res_o["out"])
+        assert e2 <= tol * r2
+
+
+FULL = ["tiny_fp32", "qwen15_moe_decode", "qwen3_30b_a3b_prefill", "qwen3_30b_a3b_prefill_zipf",
+        "dwdp_h4096_e64"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_forward_sampled(name):
+    cfg, inp = full_inputs(name)
+    log(f"[parity-full] {name}: generated")
+    dev = device_inputs(inp)
+    tol = tol_for(cfg)
+    T = cfg.num_tokens
+    rng = np.random.default_rng(123)
+    n_s = min(T, 64)
+    tokens = np.unique(np.concatenate([np.arange(min(8, T)), np.arange(max(0, T - 8), T),
+                                       rng.choice(T, size=n_s, replace=False)]))
+    f = gpu_forward(cfg, dev)
+    torch.cuda.synchronize()
+    log(f"[parity-full] {name}: GPU forward done")
+    ids_f = f["topk_ids"].cpu().numpy()
+    w_f = f["topk_weights"].cpu().numpy().astype(np.float64)
+    Lg = f["logits"].cpu().numpy().astype(np.float64)
+    # routing: bit-exact top-k on the GPU logits (all tokens)
+    assert (ids_f == oracle.select_topk(Lg, cfg.top_k)).all()
+    L = oracle.router_logits(inp["x"][tokens], inp["router_weight"], inp.get("router_bias"))
+    err_l = np.abs(Lg[tokens] - L)
+    assert (err_l <= logit_error_bound(inp, tokens)).all()
+    eps = float(err_l.max())
+    ids_o = oracle.select_topk(L, cfg.top_k)
+    tie = set(near_tie_tokens(L, max(eps, 1e-30), cfg.top_k).tolist())
+    mism = [i for i in range(len(tokens)) if i not in tie and not (ids_o[i] == ids_f[tokens[i]]).all()]
+    assert not mism
+    # output on sampled tokens against the oracle fed the GPU routing
+    ref = oracle.token_outputs(inp, tokens, ids_f, w_f)
+    got = f["out"].cpu().numpy().astype(np.float64)[tokens]
+    err, rms = rel_max_err(got, ref)
+    log(f"[parity-full] {name}: sampled {len(tokens)} tokens max|err|/rms = {err / rms:.3e}, "
+        f"eps={eps:.2e}, near-ties={len(tie)}")
+    assert err <= tol * rms
+    # dispatch of the GPU ids: bit-exact against the oracle (full size)
+    g = rdg.moe_dispatch_plan(f["topk_ids"], f["topk_weights"], cfg.num_experts)
+    plan = oracle.dispatch_plan(ids_f, f["topk_weights"].cpu().numpy(), cfg.num_experts)
+    check_plan_equal(g, plan)
+    del dev
+    torch.cuda.empty_cache()
+
+
+def test_dispatch_edge_cases():
+    cases = []
+    rng = np.random.default_rng(5)
+    # printed inputs of the ep_dispatch.rs mixed test with 512 experts
+    cases.append((np.array([[10, 300], [255, 256], [400, 500]]), 512))
+    # single assignment, k = E, every token to the same experts, max experts
+    cases.append((np.array([[3]]), 4))
+    cases.append((np.stack([rng.permutation(6) for _ in range(37)]), 6))
+    cases.append((np.tile(np.arange(4), (1000, 1)), 9))
+    cases.append((np.stack([rng.choice(512, 8, replace=False) for _ in range(300)]), 512))
+    # ragged P around the 256-assignment segments and 64-lane rounds
+    for T in (31, 32, 33, 255, 257, 4097):
+        cases.append((np.stack([rng.choice(128, 8, replace=False) for _ in range(T)]), 128))
+    for ids, E in cases:
+        ids = ids.astype(np.int32)
+        w = rng.random(ids.shape).astype(np.float32)
+        ref = oracle.dispatch_plan(ids, w, E)
+        g = rdg.moe_dispatch_plan(to_device(ids), to_device(w), E)
+        check_plan_equal(g, ref)
+        assert (g["packed_w"].cpu().numpy() == w.reshape(-1)[ref["perm"]]).all()
+        g_again = rdg.moe_dispatch_plan(to_device(ids), to_device(w), E)
+        for key in g:
+            assert torch.equal(g[key], g_again[key])
+
+
+def test_router_ties_and_special_logits():
+    # all-zero input -> all logits 0 -> experts 0..k-1, equal weights
+    cfg = workloads.config("qwen3_30b_a3b_prefill").scaled(num_tokens=40, hidden_size=64, num_experts=128, top_k=8)
+    inp = workloads.generate(cfg, seed=2)
+    inp["x"][:] = 0
+    inp["x"][5:10] = workloads.round_to_bf16_bits(-0.0 * np.ones((5, 64), np.float32))  # -0.0 inputs
+    dev = device_inputs(inp)
+    r = rdg.moe_router_topk(dev["x"], dev["router_weight"], 8)
+    ids = r["topk_ids"].cpu().numpy()
+    assert (ids == np.arange(8)[None, :]).all()
+    assert np.allclose(r["topk_weights"].cpu().numpy(), 1 / 8, rtol=1e-6)
+    # duplicate router rows: exact ties go to the lower id
+    inp = workloads.generate(cfg, seed=3)
+    inp["router_weight"][77] = inp["router_weight"][12]
+    inp["router_weight"][100] = inp["router_weight"][3]
+    dev = device_inputs(inp)
+    r = rdg.moe_router_topk(dev["x"], dev["router_weight"], 8)
+    Lg = r["logits"].cpu().numpy()
+    assert (Lg[:, 77] == Lg[:, 12]).all()
+    ids = r["topk_ids"].cpu().numpy()
+    assert (ids == oracle.select_topk(Lg.astype(np.float64), 8)).all()
+    for t in range(40):
+        row = list(ids[t])
+        if 77 in row:
+            assert 12 in row and row.index(12) < row.index(77)
+
+
+@pytest.mark.parametrize("k,E", [(1, 1), (4, 4), (1, 7), (3, 512)])
+def test_forward_degenerate_shapes(k, E):
+    cfg = workloads.config("qwen3_30b_a3b_prefill").scaled(num_tokens=50, hidden_size=128, num_experts=E, top_k=k,
+                                                           intermediate_size=64)
+    inp = workloads.generate(cfg, seed=k * 100 + E)
+    dev = device_inputs(inp)
+    f = gpu_forward(cfg, dev)
+    ids = f["topk_ids"].cpu().numpy()
+    w = f["topk_weights"].cpu().numpy().astype(np.float64)
+    res = oracle.forward(inp, k, True, ids=ids, weights=w)
+    err, rms = rel_max_err(f["out"].cpu().numpy().astype(np.float64), res["out"])
+    assert err <= 2e-2 * rms
+    if k == 1:
+        assert (w == 1.0).all()
+
+
+def test_forward_zero_tokens_and_one_token():
+    cfg = workloads.config("qwen3_30b_a3b_prefill").scaled(num_tokens=1, hidden_size=128, num_experts=16,
+                                                           intermediate_size=64)
+    inp = workloads.generate(cfg, seed=9)
+    dev = device_inputs(inp)
+    f = gpu_forward(cfg, dev)
+    res = oracle.forward(inp, cfg.top_k, True, ids=f["topk_ids"].cpu().numpy(),
+                         weights=f["topk_weights"].cpu().numpy().astype(np.float64))
+    err, rms = rel_max_err(f["out"].cpu().numpy().astype(np.float64), res["out"])
+    assert err <= 2e-2 * rms
+    empty = dev["x"][:0]
+    out = rdg.moe_forward(empty, dev["router_weight"], dev["w13"], dev["w2"], cfg.top_k)
+    torch.cuda.synchronize()
+    assert out.shape == (0, cfg.hidden_size)
+
+
+def test_forward_bf16_output_and_determinism():
+    cfg = SMALL["bf16_multi_tile"]
+    inp = workloads.generate(cfg, seed=1)
+    dev = device_inputs(inp)
+    a = gpu_forward(cfg, dev)
+    b = gpu_forward(cfg, dev)
+    assert torch.equal(a["out"], b["out"])
+    assert torch.equal(a["topk_ids"], b["topk_ids"])
+    c = gpu_forward(cfg, dev, out_dtype=torch.bfloat16)
+    # the bf16 output is the fp32 output rounded to nearest even
+    assert torch.equal(c["out"], a["out"].to(torch.bfloat16))
+
+
+def test_no_renormalize():
+    cfg = SMALL["bf16_mid_rows"].scaled(renormalize=False)
+    inp = workloads.generate(cfg, seed=4)
+    dev = device_inputs(inp)
+    f = gpu_forward(cfg, dev)
+    Lg = f["logits"].cpu().numpy().astype(np.float64)
+    ids = f["topk_ids"].cpu().numpy()
+    w = f["topk_weights"].cpu().numpy().astype(np.float64)
+    ref_w = oracle.routing_weights(Lg, ids, False)
+    assert np.max(np.abs(w - ref_w) / ref_w) <= 1e-5
+    assert (w.sum(1) < 1.0 + 1e-6).all()
+    res = oracle.forward(inp, cfg.top_k, False, ids=ids, weights=w)
+    err, rms = rel_max_err(f["out"].cpu().numpy().astype(np.float64), res["out"])
+    assert err <= 2e-2 * rms
