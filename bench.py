@@ -1,0 +1,276 @@
+"""Throughput of the MI355X MoE layer forward (router -> dispatch -> grouped
+SwiGLU experts -> combine) on a seeded synthetic Qwen-MoE-shaped layer.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line.  A step is one whole ``moe_forward`` over the batch
+(all stages, inputs already resident in HBM).  ``value`` is tokens/s.  Two
+timed regions run back to back: a clean one for ``value`` and one with HIP
+events bracketing every library kernel (recorded on the stream each kernel is
+launched on) for the per-kernel durations and the roofline of the dominant
+kernel.  The float64 oracle is timed on a bounded token sample on the host
+cores as ``cpu_baseline`` (a reported baseline only).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "MoE-layer tokens/sec at Qwen3-30B-A3B shape; grouped-GEMM % bf16 peak"
+DEFAULT_WORKLOAD = "qwen3_30b_a3b_prefill"
+
+# MI355X published peaks (dense)
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_work(name, cfg, touched, touched_shared=True):
+    """Algorithmic FLOPs and HBM bytes of ONE launch of a library kernel.
+
+    Bytes count each tensor the kernel must move once: weights of touched
+    experts only, activations read/written once; tile padding and re-reads are
+    not counted."""
+    T, H, E, k, I = cfg.num_tokens, cfg.hidden_size, cfg.num_experts, cfg.top_k, cfg.intermediate_size
+    Is = cfg.shared_intermediate_size
+    P = T * k
+    es = 2 if cfg.dtype == "bf16" else 4
+    if name in ("ffn_gate_up_bf16", "ffn_gate_up_f32"):
+        return 4.0 * P * H * I, touched * 2 * I * H * es + P * H * es + P * I * es
+    if name in ("ffn_down_bf16", "ffn_down_f32"):
+        return 2.0 * P * H * I, touched * H * I * es + P * I * es + P * H * 4
+    if name == "shared_gate_up_bf16":
+        return 4.0 * T * H * Is, 2 * Is * H * es + T * H * es + T * Is * es
+    if name == "shared_down_bf16":
+        return 2.0 * T * H * Is, H * Is * es + T * Is * es + T * H * 4
+    if name in ("router_logits_bf16", "router_logits_f32"):
+        C = E + (1 if Is else 0)
+        return 2.0 * T * H * C, T * H * es + C * H * es + T * C * 4
+    if name == "router_topk":
+        return 0.0, T * E * 4 + 2 * P * 4
+    if name == "dispatch_hist":
+        return 0.0, P * 4
+    if name == "dispatch_scan":
+        return 0.0, 2 * E * 4
+    if name == "dispatch_scatter":
+        return 0.0, P * 4 + 3 * P * 4
+    if name == "combine":
+        return 0.0, P * H * 4 + P * 8 + T * H * 4 + (T * H * 4 if Is else 0)
+    return 0.0, 0.0
+
+
+def roofline_entry(name, cfg, avg_s, touched):
+    flops, nbytes = kernel_work(name, cfg, touched)
+    peak_f = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    t_f = flops / (peak_f * 1e12)
+    t_b = nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_f >= t_b and flops > 0:
+        ach = flops / avg_s / 1e12
+        return {"bound": "mfma" if cfg.dtype == "bf16" else "alu", "achieved": round(ach, 2), "peak": peak_f,
+                "unit": "TFLOP/s", "frac": round(ach / peak_f, 4), "traffic": None,
+                "kernel": name, "avg_us": round(avg_s * 1e6, 2), "algorithmic_flops": flops,
+                "algorithmic_bytes": nbytes}
+    ach = nbytes / avg_s / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": name,
+            "avg_us": round(avg_s * 1e6, 2), "algorithmic_flops": flops, "algorithmic_bytes": nbytes}
+
+
+def cpu_baseline(cfg, inp, sample_tokens, target_s):
+    """Time the float64 oracle on the first `sample_tokens` tokens of the workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    S = min(sample_tokens, cfg.num_tokens)
+    sub = dict(inp)
+    sub["x"] = inp["x"][:S]
+    t0 = time.perf_counter()
+    oracle.forward(sub, cfg.top_k, cfg.renormalize)
+    dt = time.perf_counter() - t0
+    # grow the sample once if it was far below the target duration
+    if dt < target_s / 3 and S < cfg.num_tokens:
+        S2 = min(cfg.num_tokens, int(S * min(8.0, target_s / max(dt, 1e-3))))
+        if S2 > S:
+            S = S2
+            sub["x"] = inp["x"][:S]
+            t0 = time.perf_counter()
+            oracle.forward(sub, cfg.top_k, cfg.renormalize)
+            dt = time.perf_counter() - t0
+    return {"value": round(S / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 NumPy oracle forward (router, top-k, dispatch plan, per-expert SwiGLU, combine) "
+                      f"over the first {S} of {cfg.num_tokens} tokens with the full layer weights; {dt:.2f} s",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(workloads.CONFIGS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-target-seconds", type=float, default=15.0)
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event region")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the steps, run one plain device copy of this many MiB (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU: the single-GPU MoE layer forward has no "
+                                   "multi-GPU path (expert/tensor parallel designs are not part of it); "
+                                   "run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import route_dispatch_grouped_amd as rdg
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    cfg = workloads.config(args.workload)
+    log(f"[bench] generating {cfg.name} (seed {args.seed})")
+    t0 = time.perf_counter()
+    inp = workloads.generate(cfg, seed=args.seed)
+    log(f"[bench] generated in {time.perf_counter() - t0:.1f} s")
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    d = {kk: dev(v) for kk, v in inp.items()}
+    layer = rdg.MoeLayer(d["router_weight"], d["w13"], d["w2"], cfg.top_k, router_bias=d.get("router_bias"),
+                         shared_w13=d.get("shared_w13"), shared_w2=d.get("shared_w2"),
+                         shared_gate=d.get("shared_gate"), renormalize=cfg.renormalize)
+    x = d["x"]
+    layer.reserve(cfg.num_tokens, x.device)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        layer(x)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+
+    # ---- timed region A: value
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        layer(x)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall * 1e3 / args.steps
+    value = cfg.num_tokens * args.steps / wall
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (events {ev_ms / args.steps:.3f} ms)")
+
+    # routing statistics of this batch (outside the timed regions)
+    r = rdg.moe_router_topk(x, d["router_weight"], cfg.top_k, router_bias=d.get("router_bias"),
+                            renormalize=cfg.renormalize)
+    plan = rdg.moe_dispatch_plan(r["topk_ids"], None, cfg.num_experts)
+    counts = plan["counts"].cpu().numpy()
+    touched = int((counts > 0).sum())
+
+    # ---- timed region B: per-kernel HIP events
+    kernels = {}
+    if not args.no_profile:
+        rdg.profile_enable(True)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            layer(x)
+        torch.cuda.synchronize()
+        rdg.profile_enable(False)
+        kernels = rdg.profile_collect()
+        log("[bench] per-kernel: " + ", ".join(f"{n} {ms / c * 1e3:.1f}us" for n, (ms, c) in kernels.items()))
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    per_kernel = {}
+    roof = None
+    dominant = None
+    for n, (ms, c) in kernels.items():
+        avg_s = ms / c / 1e3
+        ent = roofline_entry(n, cfg, avg_s, touched)
+        per_kernel[n] = {"avg_us": round(avg_s * 1e6, 2), "launches_per_step": c // max(args.steps, 1),
+                         "bound": ent["bound"], "achieved": ent["achieved"], "unit": ent["unit"],
+                         "frac": ent["frac"]}
+        if dominant is None or ms > kernels[dominant][0]:
+            dominant = n
+    if dominant is not None:
+        ms, c = kernels[dominant]
+        roof = roofline_entry(dominant, cfg, ms / c / 1e3, touched)
+
+    # grouped FFN (gate/up + down) as a fraction of bf16 peak
+    ffn = None
+    if "ffn_gate_up_bf16" in kernels and "ffn_down_bf16" in kernels:
+        t_ffn = sum(kernels[n][0] / kernels[n][1] for n in ("ffn_gate_up_bf16", "ffn_down_bf16")) / 1e3
+        fl = 6.0 * cfg.num_tokens * cfg.top_k * cfg.hidden_size * cfg.intermediate_size
+        ffn = {"tflops": round(fl / t_ffn / 1e12, 2), "frac_bf16_peak": round(fl / t_ffn / 1e12 / PEAK_BF16_TFLOPS, 4),
+               "us": round(t_ffn * 1e6, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        cpu = cpu_baseline(cfg, inp, args.cpu_sample_tokens, args.cpu_target_seconds)
+        log(f"[bench] oracle: {cpu['value']} tokens/s ({cpu['sample']})")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "num_tokens": cfg.num_tokens, "hidden_size": cfg.hidden_size,
+                   "num_experts": cfg.num_experts, "top_k": cfg.top_k, "intermediate_size": cfg.intermediate_size,
+                   "shared_intermediate_size": cfg.shared_intermediate_size, "renormalize": cfg.renormalize,
+                   "seed": args.seed, "experts_touched": touched, "max_expert_rows": int(counts.max()),
+                   "inputs": "x~N(0,1), weights~N(0,0.02), bf16 RNE; seeded PCG64 streams"},
+        "roofline": roof,
+        "grouped_ffn": ffn,
+        "kernels": per_kernel,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
