@@ -59,6 +59,16 @@ moe_status check_sizes(int64_t T, int64_t H, int64_t E, int64_t k, int dtype, bo
   return MOE_OK;
 }
 
+// The bf16 kernels address every operand with 32-bit byte offsets from a
+// buffer base (one expert's weights, the activations, h).
+moe_status check_buffer_bytes(int64_t T, int64_t H, int64_t k, int64_t I, int dtype) {
+  if (dtype != MOE_DTYPE_BF16) return MOE_OK;
+  const int64_t lim = ((int64_t)1 << 31) - 1;
+  if (T * H * 2 > lim || T * k * I * 2 > lim || 2 * I * H * 2 > lim)
+    return fail(MOE_ERR_UNSUPPORTED, "a bf16 operand exceeds 2 GiB (32-bit buffer offsets)");
+  return MOE_OK;
+}
+
 moe_status check_inter(int64_t I, int dtype, const char* name) {
   if (I < 1) return fail(MOE_ERR_INVALID_ARG, std::string(name) + " must be >= 1");
   if (dtype == MOE_DTYPE_BF16 && I % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, std::string("bf16 needs ") + name + " % 64 == 0");
@@ -149,12 +159,13 @@ hipError_t run_router(const void* x, const void* wr, const float* bias, const vo
     moe::GemmArgs a = gemm_args();
     a.A = static_cast<const uint16_t*>(x);
     a.M = T;
+    a.a_rows = T;
     a.G = 1;
     a.B = static_cast<const uint16_t*>(wr);
     a.b_group_stride = 0;
     a.b_extra = static_cast<const uint16_t*>(gate);
     a.K = H;
-    a.N = E + (gate ? 1 : 0);
+    a.N = E;
     a.out = logits;
     a.ldo = E;
     a.bias = bias;
@@ -169,7 +180,8 @@ hipError_t run_router(const void* x, const void* wr, const float* bias, const vo
 }
 
 hipError_t run_ffn(const void* x, const int32_t* gather, const int32_t* offsets, const void* w13, const void* w2,
-                   int P, int H, int E, int I, int dtype, void* h, float* y, hipStream_t s, bool shared) {
+                   int T_rows, int P, int H, int E, int I, int dtype, void* h, float* y, hipStream_t s,
+                   bool shared) {
   hipError_t e;
   if (dtype == MOE_DTYPE_BF16) {
     moe::GemmArgs a = gemm_args();
@@ -177,6 +189,7 @@ hipError_t run_ffn(const void* x, const int32_t* gather, const int32_t* offsets,
     a.gather = gather;
     a.offsets = offsets;
     a.M = P;
+    a.a_rows = T_rows;
     a.G = E;
     a.B = static_cast<const uint16_t*>(w13);
     a.b_group_stride = (int64_t)2 * I * H;
@@ -192,6 +205,7 @@ hipError_t run_ffn(const void* x, const int32_t* gather, const int32_t* offsets,
     b.gather = nullptr;
     b.offsets = offsets;
     b.M = P;
+    b.a_rows = P;
     b.G = E;
     b.B = static_cast<const uint16_t*>(w2);
     b.b_group_stride = (int64_t)H * I;
@@ -281,6 +295,7 @@ moe_status moe_router_topk(const void* hidden_states, const void* router_weight,
                            int64_t top_k, int renormalize, int dtype, float* router_logits, float* routing_probs,
                            int32_t* topk_ids, float* topk_weights, float* shared_gate_logit, void* stream) {
   RETURN_IF_ERR(check_sizes(num_tokens, hidden_size, num_experts, top_k, dtype, true));
+  RETURN_IF_ERR(check_buffer_bytes(num_tokens, hidden_size, 1, 1, dtype));
   if (num_tokens == 0) return succeed();
   REQUIRE_PTR(hidden_states);
   REQUIRE_PTR(router_weight);
@@ -341,6 +356,7 @@ moe_status moe_grouped_ffn(const void* hidden_states, const int32_t* packed_toke
                            void* stream) {
   RETURN_IF_ERR(check_sizes(num_tokens, hidden_size, num_experts, top_k, dtype, true));
   RETURN_IF_ERR(check_inter(intermediate_size, dtype, "intermediate_size"));
+  RETURN_IF_ERR(check_buffer_bytes(num_tokens, hidden_size, top_k, intermediate_size, dtype));
   if (num_tokens == 0) return succeed();
   REQUIRE_PTR(hidden_states);
   REQUIRE_PTR(w13);
@@ -359,7 +375,8 @@ moe_status moe_grouped_ffn(const void* hidden_states, const int32_t* packed_toke
   REQUIRE_ALIGNED(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int P = (int)(num_tokens * top_k);
-  return hip_status(run_ffn(hidden_states, packed_token_indices, expert_offsets, w13, w2, P, (int)hidden_size,
+  return hip_status(run_ffn(hidden_states, packed_token_indices, expert_offsets, w13, w2, (int)num_tokens, P,
+                            (int)hidden_size,
                             (int)num_experts, (int)intermediate_size, dtype, workspace, packed_expert_outputs, s,
                             false),
                     "moe_grouped_ffn");
@@ -416,6 +433,8 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
     return fail(MOE_ERR_INVALID_ARG, "shared_w13, shared_w2 and shared_gate must be given together");
   const int64_t Is = nshared ? shared_intermediate_size : 0;
   if (nshared) RETURN_IF_ERR(check_inter(Is, dtype, "shared_intermediate_size"));
+  RETURN_IF_ERR(check_buffer_bytes(num_tokens, hidden_size, top_k, intermediate_size, dtype));
+  if (nshared) RETURN_IF_ERR(check_buffer_bytes(num_tokens, hidden_size, 1, Is, dtype));
   if (out_dtype != MOE_DTYPE_F32 && out_dtype != MOE_DTYPE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "out_dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
   if (num_tokens == 0) return succeed();
@@ -453,10 +472,11 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
                            L.dispatch_scratch, s);
   if (e != hipSuccess) return hip_status(e, "moe_forward(dispatch)");
   if (Is) {
-    e = run_ffn(hidden_states, nullptr, nullptr, shared_w13, shared_w2, T, H, 1, (int)Is, dtype, L.hs, L.ys, s, true);
+    e = run_ffn(hidden_states, nullptr, nullptr, shared_w13, shared_w2, T, T, H, 1, (int)Is, dtype, L.hs, L.ys, s,
+                true);
     if (e != hipSuccess) return hip_status(e, "moe_forward(shared expert)");
   }
-  e = run_ffn(hidden_states, L.packed_ids, L.offsets, w13, w2, P, H, E, I, dtype, L.h, L.y, s, false);
+  e = run_ffn(hidden_states, L.packed_ids, L.offsets, w13, w2, T, P, H, E, I, dtype, L.h, L.y, s, false);
   if (e != hipSuccess) return hip_status(e, "moe_forward(experts)");
   e = moe::launch_combine(L.y, L.inv, weights, Is ? L.ys : nullptr, Is ? L.gate_logit : nullptr, T, H, k,
                           out_dtype == MOE_DTYPE_BF16, output, s);

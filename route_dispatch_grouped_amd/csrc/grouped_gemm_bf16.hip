@@ -6,29 +6,39 @@
 //               the modelexpress refit test lays them out) and writes
 //               h = silu(g) * u as bf16.               [DWDP README "Executor Module"]
 //   EPI_F32     down projection y = W2[e] h, fp32 out.  [DWDP README "Executor Module"]
-//   EPI_ROUTER  router logits x Wr^T (+ bias) with an optional extra weight row
-//               (the shared expert's gate vector).      [DWDP README "Router Module"]
+//   EPI_ROUTER  router logits x Wr^T (+ bias).          [DWDP README "Router Module"]
 //
 // Scheduling: the packed rows of each group (expert) form expert-major execution
 // ranges [offsets[g], offsets[g+1]) ([DWDP README "Scheduler Module"]).  Every
 // range is cut into BM-row m-tiles; m-tiles x n-blocks form a linear tile list,
-// expert-major.  The grid is persistent; each workgroup derives the tile list
-// itself from `offsets` (a block-wide scan in LDS), so no host sync and no
-// separate schedule kernel is needed.  Tiles are handed out XCD-aware: MI355X
-// places workgroup b on XCD b % 8, so XCD x owns the contiguous tile range
-// [x*per, (x+1)*per) and its 4 MB L2 sees all n-blocks of an m-tile and all
-// m-tiles of an expert close together in time.
+// expert-major, n-block fastest.  The grid is persistent; each workgroup derives
+// the tile list itself from `offsets` (a block-wide scan in LDS), so no host
+// sync and no separate schedule kernel is needed.  Tiles are handed out
+// XCD-aware: MI355X places workgroup b on XCD b % 8, so XCD x owns the
+// contiguous tile range [x*per, (x+1)*per) and its 4 MB L2 serves all n-blocks
+// of an m-tile and all m-tiles of an expert close together in time.
 //
-// Tile: BM rows x (4 waves x 64 B-rows); BK = 64.  The A tile (gathered
-// activation rows, shared by the 4 waves) is staged through LDS, double
-// buffered, with a 16-byte-chunk XOR swizzle (chunk c of row r sits at c ^ (r & 7))
-// so that both the row-wise stores and the fragment loads are bank-conflict
-// free.  B rows belong to exactly one wave, so each wave loads its B fragments
-// straight from global memory into registers, one stage ahead.
+// Tile: BM rows x 256 weight rows (EPI_SWIGLU: 128 gate + the matching 128 up
+// rows; otherwise 256 output columns), BK = 64 (128 bytes per row).  Both
+// operands stream through an NS-stage LDS ring filled by direct global->LDS
+// DMA (buffer_load_dwordx4 ... lds): no staging registers, NS-1 K-steps in
+// flight.  Each stage is its own __shared__ object, so the compiler tracks the
+// DMA of each stage separately and waits only for the stage being read.  One
+// workgroup barrier per K-step: each wave first waits for its own DMA of the
+// stage, the barrier then publishes the whole stage and also proves that every
+// wave has finished reading the buffer the next DMA will overwrite.
 //
-// Rows past the end of a group are computed on a clamped (valid) row and never
-// stored; 16-row sub-tiles that lie wholly past the end skip their MFMAs, so a
-// ragged last tile costs MFMA time in proportion to its real rows.
+// LDS layout: row r of a tile holds eight 16-byte chunks; chunk c sits at
+// position c ^ (r & 7), so the row-wise DMA writes and the fragment reads (16
+// rows, one chunk column) are both bank-conflict free.  The DMA writes lane l
+// of an instruction to slot base + l; each lane therefore fetches the global
+// chunk that belongs at its slot.
+//
+// Wave w computes all BM rows against its 64 weight rows (EPI_SWIGLU: gate
+// rows 32w..32w+31 and the same up rows, so gate and up of one h column meet
+// in the same lane of the accumulators).  Rows past the end of a group read a
+// clamped (valid) row and are never stored; 16-row sub-tiles wholly past the
+// end skip their MFMAs (a straight-line K loop per live sub-tile count).
 #include "moe_internal.h"
 
 namespace moe {
@@ -40,12 +50,24 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int BK = 64;
+constexpr int kBRows = 256;
 constexpr int kMaxGroups = MOE_MAX_GROUPS_INTERNAL;
 constexpr int kXcds = 8;
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource, 32-bit data
 
-__device__ __forceinline__ u32x4_t ldg16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4_t*>(p);
-}
+template <int BM>
+struct Tile {
+  static constexpr int MSUB = BM / 16;
+  static constexpr int NS = (BM >= 64) ? 3 : 4;            // LDS ring depth
+  static constexpr int SLOTS = (BM + kBRows) * 8;          // 16-byte slots per stage
+  static constexpr int A_INSTR = BM / 8;                   // wave-instructions (64 slots each)
+  static constexpr int B_INSTR = kBRows / 8;               // 32
+  static constexpr int A_MAX = (A_INSTR + 3) / 4;          // per wave
+  static constexpr int A_MIN = A_INSTR / 4;
+  static constexpr int B_PER = B_INSTR / 4;                // 8 per wave
+  // outstanding DMA instructions allowed while waiting for the oldest stage
+  static constexpr int VM_WAIT = (NS - 2) * (A_MIN + B_PER);
+};
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -53,13 +75,119 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Per-tile DMA addressing: byte offsets of every slot this lane fetches.
+template <int BM>
+struct DmaPlan {
+  uint32_t a_off[Tile<BM>::A_MAX];
+  uint32_t b_off[Tile<BM>::B_PER];
+};
+
+// Raw buffer resource (gfx9 V#): 48-bit base, stride 0, size in bytes; loads
+// past `bytes` return zero instead of faulting.
+__device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, (uint32_t)kBufferWord3};
+}
+
+// One 16-byte-per-lane DMA from global (buffer + voff + soff) to LDS: lane l
+// lands at lds_dst + 16*l.  Issued as inline asm so that the compiler neither
+// tracks nor waits for it: the K loop waits with explicit vmcnt counts.  The
+// instruction has no register result, so nothing can be overwritten in flight.
+__device__ __forceinline__ void dma16(const u32x4_t* lds_dst, u32x4_t rsrc, uint32_t voff, int soff) {
+  const uint32_t m0v =
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)lds_dst);
+  uint32_t saved;  // m0 is restored, so the compiler's own use of it is unaffected
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+template <int BM>
+__device__ __forceinline__ void issue_stage(u32x4_t* buf, const DmaPlan<BM>& d, u32x4_t ra, u32x4_t rb, int wave,
+                                            int kbytes) {
+  using C = Tile<BM>;
+#pragma unroll
+  for (int qi = 0; qi < C::A_MAX; ++qi) {
+    const int q = qi * 4 + wave;
+    if (qi < C::A_MIN || q < C::A_INSTR) dma16(buf + q * 64, ra, d.a_off[qi], kbytes);
+  }
+#pragma unroll
+  for (int qi = 0; qi < C::B_PER; ++qi) {
+    const int q = qi * 4 + wave;
+    dma16(buf + BM * 8 + q * 64, rb, d.b_off[qi], kbytes);
+  }
+}
+
+// One K-step from one stage: LIVE row sub-tiles x 4 weight sub-tiles x 2 k32.
+template <int BM, int LIVE>
+__device__ __forceinline__ void mma_stage(f32x4_t (&acc)[BM / 16][4], const u32x4_t* __restrict__ buf,
+                                          const int (&brow)[4], int lane) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int sw = (kk * 4 + (lane >> 4)) ^ (lane & 7);
+    bf16x8_t b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = __builtin_bit_cast(bf16x8_t, buf[BM * 8 + (brow[j] + (lane & 15)) * 8 + sw]);
+#pragma unroll
+    for (int i = 0; i < LIVE; ++i) {
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, buf[(16 * i + (lane & 15)) * 8 + sw]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
+// K loop over an NS-stage ring; the loop body is unrolled NS times so that
+// every stage buffer has a static role.
+template <int BM, int LIVE>
+__device__ __forceinline__ void kloop(f32x4_t (&acc)[BM / 16][4], u32x4_t* s0, u32x4_t* s1, u32x4_t* s2,
+                                      u32x4_t* s3, const DmaPlan<BM>& d, u32x4_t ra, u32x4_t rb, int wave,
+                                      int lane, int KT, bool wave_live,
+                                      const int (&brow)[4]) {
+  using C = Tile<BM>;
+  constexpr int NS = C::NS;
+  // prologue: stages 0 .. NS-2 in flight
+  issue_stage<BM>(s0, d, ra, rb, wave, 0);
+  if (KT > 1) issue_stage<BM>(s1, d, ra, rb, wave, BK * 2);
+  if (NS == 4 && KT > 2) issue_stage<BM>(s2, d, ra, rb, wave, 2 * BK * 2);
+  u32x4_t* bufs[4] = {s0, s1, s2, s3};
+  for (int kt0 = 0; kt0 < KT; kt0 += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int kt = kt0 + u;
+      if (kt >= KT) break;
+      // wait for this wave's DMA of stage kt (later stages may stay in flight)
+      if (kt + NS - 2 < KT) wait_vmcnt<C::VM_WAIT>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (kt + NS - 1 < KT) issue_stage<BM>(bufs[(u + NS - 1) % NS], d, ra, rb, wave, (kt + NS - 1) * BK * 2);
+      if (wave_live) mma_stage<BM, LIVE>(acc, bufs[u], brow, lane);
+    }
+  }
+}
+
 template <int BM, int EPI>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p) {
-  constexpr int MSUB = BM / 16;
-  constexpr int A_SLOTS = (BM * 8 + kThreads - 1) / kThreads;  // 16-byte A chunks per thread
-  constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;      // output columns per tile
+  using C = Tile<BM>;
+  constexpr int MSUB = C::MSUB;
+  constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;  // output columns per tile
 
-  __shared__ u32x4_t sA[2][BM * 8];
+  __shared__ u32x4_t st0[C::SLOTS];
+  __shared__ u32x4_t st1[C::SLOTS];
+  __shared__ u32x4_t st2[C::SLOTS];
+  __shared__ u32x4_t st3[C::NS == 4 ? C::SLOTS : 1];
   __shared__ int s_off[kMaxGroups + 1];
   __shared__ int s_tb[kMaxGroups + 1];
   __shared__ int s_wsum[kThreads / 64];
@@ -84,9 +212,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
     const int sum = t0 + t1;
     int incl = sum;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += v;
+    for (int dd = 1; dd < 64; dd <<= 1) {
+      const int v = __shfl_up(incl, dd, 64);
+      if (lane >= dd) incl += v;
     }
     if (lane == 63) s_wsum[wave] = incl;
     __syncthreads();
@@ -113,6 +241,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
   const int t_begin = xcd * per;
   const int t_end = min(total, t_begin + per);
   const int KT = p.K / BK;
+  const uint32_t row_bytes = (uint32_t)p.K * 2u;
+
+  // weight rows of this wave inside the 256-row B tile (sub-tile bases)
+  int brow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    brow[j] = (EPI == EPI_SWIGLU) ? ((j < 2) ? 32 * wave + 16 * j : 128 + 32 * wave + 16 * (j - 2))
+                                  : 64 * wave + 16 * j;
 
   for (int t = t_begin + slot; t < t_end; t += nslots) {
     const int mt = t / nblk;
@@ -129,41 +265,36 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
     const int n0 = nb * BN_OUT;
     const uint16_t* Bg = p.B + (int64_t)g * p.b_group_stride;
 
-    // A source rows (gathered), one 16-byte chunk per slot
-    const int a_chunk = tid & 7;
-    const uint16_t* a_src[A_SLOTS];
-    int a_row[A_SLOTS];
+    // DMA plan of this lane: slot s = q*64 + lane holds row s/8, chunk (s%8)^(row%8)
+    DmaPlan<BM> d;
 #pragma unroll
-    for (int i = 0; i < A_SLOTS; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      a_row[i] = r;
+    for (int qi = 0; qi < C::A_MAX; ++qi) {
+      const int q = qi * 4 + wave;
+      const int r = min(q * 8 + (lane >> 3), BM - 1);
+      const int c = (lane & 7) ^ (r & 7);
       const int rr = min(r, rows - 1);
-      const int64_t grow = p.gather ? (int64_t)p.gather[m0 + rr] : (int64_t)(m0 + rr);
-      a_src[i] = p.A + grow * p.K + a_chunk * 8;
+      const int grow = p.gather ? p.gather[m0 + rr] : (m0 + rr);
+      d.a_off[qi] = (uint32_t)grow * row_bytes + (uint32_t)c * 16u;
     }
-
-    // B fragment rows of this wave: 4 sub-tiles of 16 rows
-    const uint16_t* b_src[4];
-    bool sub_live[4];
-    int wave_col0;
-    if (EPI == EPI_SWIGLU) wave_col0 = n0 + 32 * wave;
-    else wave_col0 = n0 + 64 * wave;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int col0, brow;
+    for (int qi = 0; qi < C::B_PER; ++qi) {
+      const int q = qi * 4 + wave;
+      const int r = q * 8 + (lane >> 3);  // B tile row
+      const int c = (lane & 7) ^ (r & 7);
+      int wr;
       if (EPI == EPI_SWIGLU) {
-        col0 = wave_col0 + 16 * (j & 1);
-        const int c = min(col0 + (lane & 15), p.N - 1);
-        brow = (j < 2) ? c : p.up_row0 + c;
+        const int col = min(n0 + (r & 127), p.N - 1);
+        wr = (r < 128) ? col : p.up_row0 + col;
       } else {
-        col0 = wave_col0 + 16 * j;
-        brow = min(col0 + (lane & 15), p.N - 1);
+        wr = min(n0 + r, p.N - 1);
       }
-      sub_live[j] = col0 < p.N;
-      const uint16_t* rp = Bg + (int64_t)brow * p.K;
-      if (EPI == EPI_ROUTER && p.b_extra != nullptr && brow == p.N - 1) rp = p.b_extra;
-      b_src[j] = rp + (lane >> 4) * 8;
+      d.b_off[qi] = (uint32_t)wr * row_bytes + (uint32_t)c * 16u;
     }
+    const u32x4_t ra = make_rsrc(p.A, (uint32_t)p.a_rows * row_bytes);
+    const int b_rows_total = (EPI == EPI_SWIGLU) ? 2 * p.up_row0 : p.N;
+    const u32x4_t rb = make_rsrc(Bg, (uint32_t)b_rows_total * row_bytes);
+
+    const int wave_col0 = (EPI == EPI_SWIGLU) ? n0 + 32 * wave : n0 + 64 * wave;
     const bool wave_live = wave_col0 < p.N;
 
     f32x4_t acc[MSUB][4];
@@ -172,63 +303,19 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    u32x4_t a_reg[A_SLOTS];
-    u32x4_t b_cur[4][2], b_nxt[4][2];
-
-#pragma unroll
-    for (int i = 0; i < A_SLOTS; ++i)
-      if (a_row[i] < BM) a_reg[i] = ldg16(a_src[i]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) b_cur[j][kk] = ldg16(b_src[j] + kk * 32);
-#pragma unroll
-    for (int i = 0; i < A_SLOTS; ++i)
-      if (a_row[i] < BM) sA[0][a_row[i] * 8 + (a_chunk ^ (a_row[i] & 7))] = a_reg[i];
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-      const int buf = kt & 1;
-      const bool more = kt + 1 < KT;
-      if (more) {
-        const int ko = (kt + 1) * BK;
-#pragma unroll
-        for (int i = 0; i < A_SLOTS; ++i)
-          if (a_row[i] < BM) a_reg[i] = ldg16(a_src[i] + ko);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) b_nxt[j][kk] = ldg16(b_src[j] + ko + kk * 32);
-      }
-      if (wave_live) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-          for (int i = 0; i < MSUB; ++i) {
-            if (i < msub_live) {
-              const int row = 16 * i + (lane & 15);
-              const int chunk = kk * 4 + (lane >> 4);
-              const bf16x8_t a = __builtin_bit_cast(bf16x8_t, sA[buf][row * 8 + (chunk ^ (row & 7))]);
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                if (sub_live[j])
-                  acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                      a, __builtin_bit_cast(bf16x8_t, b_cur[j][kk]), acc[i][j], 0, 0, 0);
-            }
-          }
-        }
-      }
-      if (more) {
-#pragma unroll
-        for (int i = 0; i < A_SLOTS; ++i)
-          if (a_row[i] < BM) sA[buf ^ 1][a_row[i] * 8 + (a_chunk ^ (a_row[i] & 7))] = a_reg[i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) b_cur[j][kk] = b_nxt[j][kk];
-      }
-      __syncthreads();
+    switch (msub_live) {
+#define MOE_LIVE_CASE(n)                                                                                      \
+  case n:                                                                                                     \
+    if (n <= MSUB)                                                                                            \
+      kloop<BM, (n <= MSUB ? n : MSUB)>(acc, st0, st1, st2, st3, d, ra, rb, wave, lane, KT, wave_live, brow); \
+    break;
+      MOE_LIVE_CASE(1) MOE_LIVE_CASE(2) MOE_LIVE_CASE(3) MOE_LIVE_CASE(4)
+      MOE_LIVE_CASE(5) MOE_LIVE_CASE(6) MOE_LIVE_CASE(7) MOE_LIVE_CASE(8)
+#undef MOE_LIVE_CASE
+      default: break;
     }
+    // every wave is done reading the ring before the next tile's DMA starts
+    lds_barrier();
 
     // ---- epilogue.  C fragment: lane holds column (lane & 15), rows 4*(lane>>4)+r
     if (wave_live) {
@@ -263,13 +350,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
               const int row = 16 * i + 4 * (lane >> 4) + r;
               if (row < rows) {
                 float v = acc[i][j][r];
-                if (EPI == EPI_ROUTER) {
-                  if (p.b_extra != nullptr && col == p.N - 1) {
-                    p.extra_out[m0 + row] = v;
-                    continue;
-                  }
-                  if (p.bias) v += p.bias[col];
-                }
+                if (EPI == EPI_ROUTER && p.bias) v += p.bias[col];
                 out[(int64_t)(m0 + row) * p.ldo + col] = v;
               }
             }
@@ -278,6 +359,25 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
       }
     }
   }
+}
+
+// Shared-expert gate logits x . g (one wave per token, fp32 accumulation of
+// exact bf16 products).
+__global__ __launch_bounds__(256) void gate_logit_bf16_kernel(const uint16_t* __restrict__ x,
+                                                              const uint16_t* __restrict__ g, int T, int H,
+                                                              float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float acc = 0.f;
+  for (int h = lane; h < H; h += 64) {
+    const float xv = __uint_as_float((uint32_t)x[(int64_t)t * H + h] << 16);
+    const float gv = __uint_as_float((uint32_t)g[h] << 16);
+    acc = fmaf(xv, gv, acc);
+  }
+#pragma unroll
+  for (int dd = 32; dd >= 1; dd >>= 1) acc += __shfl_xor(acc, dd, 64);
+  if (lane == 0) out[t] = acc;
 }
 
 // Resident workgroups per CU for one instantiation (the persistent grid must
@@ -298,15 +398,13 @@ int resident_blocks_per_cu() {
 }
 
 template <int BM, int EPI>
-hipError_t launch_bm(const GemmArgs& a, hipStream_t s, const char* name, int max_occupancy) {
-  int occupancy = resident_blocks_per_cu<BM, EPI>();
-  if (occupancy > max_occupancy) occupancy = max_occupancy;
+hipError_t launch_bm(const GemmArgs& a, hipStream_t s, const char* name) {
   constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
   const int64_t nblk = (a.N + BN_OUT - 1) / BN_OUT;
   int64_t ub_m = (a.M + BM - 1) / BM;
   if (a.offsets) ub_m += (a.G < a.M ? a.G : a.M);
   const int64_t ub = ub_m * nblk;
-  int64_t grid = (int64_t)device_cu_count() * occupancy;
+  int64_t grid = (int64_t)device_cu_count() * resident_blocks_per_cu<BM, EPI>();
   if (ub < grid) grid = ub;
   grid = ((grid + kXcds - 1) / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
@@ -321,10 +419,10 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s, const char* name) {
   // rows per group on average decides the m-tile height
   const int64_t groups = a.offsets ? (a.G < a.M ? a.G : a.M) : 1;
   const int64_t avg = groups > 0 ? (a.M + groups - 1) / groups : a.M;
-  if (avg <= 16) return launch_bm<16, EPI>(a, s, name, 4);
-  if (avg <= 32) return launch_bm<32, EPI>(a, s, name, 4);
-  if (avg <= 64) return launch_bm<64, EPI>(a, s, name, 2);
-  return launch_bm<128, EPI>(a, s, name, 1);
+  if (avg <= 16) return launch_bm<16, EPI>(a, s, name);
+  if (avg <= 32) return launch_bm<32, EPI>(a, s, name);
+  if (avg <= 64) return launch_bm<64, EPI>(a, s, name);
+  return launch_bm<128, EPI>(a, s, name);
 }
 
 }  // namespace
@@ -334,7 +432,15 @@ hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, GemmEpilogue epi, hipStre
   switch (epi) {
     case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(a, s, name);
     case EPI_F32: return launch_epi<EPI_F32>(a, s, name);
-    case EPI_ROUTER: return launch_bm<32, EPI_ROUTER>(a, s, name, 4);
+    case EPI_ROUTER: {
+      hipError_t e = launch_bm<32, EPI_ROUTER>(a, s, name);
+      if (e != hipSuccess || a.b_extra == nullptr) return e;
+      profile_begin("router_gate_logit_bf16", s);
+      hipLaunchKernelGGL(gate_logit_bf16_kernel, dim3((a.M + 3) / 4), dim3(256), 0, s, a.A, a.b_extra, a.M, a.K,
+                         a.extra_out);
+      profile_end(s);
+      return hipGetLastError();
+    }
   }
   return hipErrorInvalidValue;
 }

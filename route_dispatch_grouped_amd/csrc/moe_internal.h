@@ -30,17 +30,18 @@ struct GemmArgs {
   const int32_t* gather;    // A row of packed row p is gather[p] (NULL: row p)
   const int32_t* offsets;   // [G+1] packed row ranges of the groups (NULL: one group of M rows)
   int M;                    // total packed rows (upper bound of offsets[G])
+  int a_rows;               // rows of A (bounds the DMA: reads past it return 0)
   int G;                    // groups (experts)
   const uint16_t* B;        // bf16 weights, per group `b_rows` rows of length K
   int64_t b_group_stride;   // elements between groups of B
-  const uint16_t* b_extra;  // EPI_ROUTER: weight row of output column N-1 (NULL: none)
+  const uint16_t* b_extra;  // EPI_ROUTER: shared-expert gate vector [K] (NULL: none)
   int K;                    // reduction length, multiple of 64
   int N;                    // output columns (EPI_SWIGLU: I, the h width)
   int up_row0;              // EPI_SWIGLU: first up row inside a group (= I)
   void* out;                // EPI_SWIGLU: bf16 h; EPI_F32: f32; EPI_ROUTER: f32 logits
   int64_t ldo;              // output row stride in elements
   const float* bias;        // EPI_ROUTER: per-column bias or NULL
-  float* extra_out;         // EPI_ROUTER: output of column N-1 when b_extra != NULL
+  float* extra_out;         // EPI_ROUTER: x . b_extra per row, when b_extra != NULL
 };
 
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, GemmEpilogue epi, hipStream_t s, const char* name);
