@@ -75,13 +75,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]); issued through the builtin so that the compiler's
+// own wait tracking sees them.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// All of this wave's LDS reads are complete, then a workgroup barrier.  The
+// barrier itself is an asm statement with a memory clobber so that no LDS
+// access moves across it.
 __device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // Per-tile DMA addressing: byte offsets of every slot this lane fetches.
@@ -178,26 +186,12 @@ __device__ __forceinline__ void kloop(f32x4_t (&acc)[BM / 16][4], u32x4_t* s0, u
   }
 }
 
-template <int BM, int EPI>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p) {
-  using C = Tile<BM>;
-  constexpr int MSUB = C::MSUB;
-  constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;  // output columns per tile
-
-  __shared__ u32x4_t st0[C::SLOTS];
-  __shared__ u32x4_t st1[C::SLOTS];
-  __shared__ u32x4_t st2[C::SLOTS];
-  __shared__ u32x4_t st3[C::NS == 4 ? C::SLOTS : 1];
-  __shared__ int s_off[kMaxGroups + 1];
-  __shared__ int s_tb[kMaxGroups + 1];
-  __shared__ int s_wsum[kThreads / 64];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+// Tile schedule shared by every workgroup: s_off <- offsets (E+1), s_tb[g] <-
+// first m-tile of group g (exclusive scan of ceil(rows/BM)), s_tb[G] = total.
+template <int BM>
+__device__ __forceinline__ void build_schedule(const GemmArgs& p, int* s_off, int* s_tb, int* s_wsum, int tid,
+                                               int lane, int wave) {
   const int G = p.G;
-
-  // ---- tile schedule: m-tiles per group, exclusive scan -----------------
   if (p.offsets) {
     for (int g = tid; g <= G; g += kThreads) s_off[g] = p.offsets[g];
   } else if (tid == 0) {
@@ -230,6 +224,29 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
     }
   }
   __syncthreads();
+
+}
+
+template <int BM, int EPI>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p) {
+  using C = Tile<BM>;
+  constexpr int MSUB = C::MSUB;
+  constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;  // output columns per tile
+
+  __shared__ u32x4_t st0[C::SLOTS];
+  __shared__ u32x4_t st1[C::SLOTS];
+  __shared__ u32x4_t st2[C::SLOTS];
+  __shared__ u32x4_t st3[C::NS == 4 ? C::SLOTS : 1];
+  __shared__ int s_off[kMaxGroups + 1];
+  __shared__ int s_tb[kMaxGroups + 1];
+  __shared__ int s_wsum[kThreads / 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = p.G;
+
+  build_schedule<BM>(p, s_off, s_tb, s_wsum, tid, lane, wave);
 
   const int total_m = s_tb[G];
   const int nblk = (p.N + BN_OUT - 1) / BN_OUT;
@@ -361,6 +378,324 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-group variant (groups of hundreds of rows, e.g. prefill): 256 x 256
+// tiles, BK = 32 per stage, a 4-stage ring (32 KB per stage), 2 x 2 waves of
+// 128 x 128 computed with v_mfma_f32_32x32x16_bf16 (4 x 4 sub-tiles of 32 x 32).
+// On gfx950 the 32x32x16 shape sustains about 1.5x the rate of 16x16x32 and
+// does so at one wave per SIMD.  Per stage a wave issues 16 fragment reads for
+// 32 MFMAs, and the CU streams 64 KB per 2 x 256 x 256 x 64 flops, about 31
+// bytes per clock at the MFMA rate, below the ~52 B/clk/CU that the
+// L2 -> LDS DMA path sustains.
+//
+// LDS layout: a row holds four 16-byte chunks (64 bytes); chunk c of row r sits
+// at position c ^ (((r >> 1) ^ (r >> 3)) & 3), which keeps 32-row fragment
+// reads conflict free whether the LDS serves 8 or 16 lanes per cycle.
+//
+// The MFMA operands are swapped (weight fragment first), so the accumulator
+// holds the transpose: lane l owns output row (l & 31) of a 32 x 32 sub-tile
+// and the columns 8g + 4*(l >> 5) + {0..3}, g = 0..3 (value 4g + c).  The
+// epilogue therefore writes 8 (h, bf16) or 16 (y, fp32) contiguous bytes per
+// lane and group.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+struct Big {
+  static constexpr int BM = 256;
+  static constexpr int KB = 32;                   // k elements per stage
+  static constexpr int A_SLOTS = 256 * 4;         // 16-byte slots of the A tile
+  static constexpr int SLOTS = 2 * A_SLOTS;       // A tile then B tile
+  static constexpr int PER_WAVE = 8;              // DMA instructions per wave per stage
+};
+
+__device__ __forceinline__ int big_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+struct BigPlan {
+  uint32_t a_off[4];
+  uint32_t b_off[4];
+};
+
+__device__ __forceinline__ void big_issue(u32x4_t* buf, const BigPlan& d, u32x4_t ra, u32x4_t rb, int wave,
+                                          int kbytes) {
+#pragma unroll
+  for (int qi = 0; qi < 4; ++qi) dma16(buf + (qi * 4 + wave) * 64, ra, d.a_off[qi], kbytes);
+#pragma unroll
+  for (int qi = 0; qi < 4; ++qi) dma16(buf + Big::A_SLOTS + (qi * 4 + wave) * 64, rb, d.b_off[qi], kbytes);
+}
+
+// Fragments of one stage for one wave: [k16 half][sub-tile].
+struct BigFrags {
+  bf16x8_t a[2][4];
+  bf16x8_t b[2][4];
+};
+
+// Slot offset of weight sub-tile j from the wave's first weight row (the
+// SwiGLU tile holds 2 gate sub-tiles, then the matching up rows 128 further on).
+template <int EPI>
+__device__ __forceinline__ constexpr int big_b_off(int j) {
+  return (EPI == EPI_SWIGLU) ? ((j < 2) ? 128 * j : 512 + 128 * (j - 2)) : 128 * j;
+}
+
+template <int EPI, int LIVE>
+__device__ __forceinline__ void big_read(BigFrags& f, const u32x4_t* __restrict__ buf, const int (&a_slot)[2],
+                                         const int (&b_slot)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.b[h][j] = __builtin_bit_cast(bf16x8_t, buf[b_slot[h] + big_b_off<EPI>(j)]);
+#pragma unroll
+    for (int i = 0; i < LIVE; ++i) f.a[h][i] = __builtin_bit_cast(bf16x8_t, buf[a_slot[h] + 128 * i]);
+  }
+}
+
+template <int LIVE>
+__device__ __forceinline__ void big_mma(f32x16_t (&acc)[4][4], const BigFrags& f) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < LIVE; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[h][j], f.a[h][i], acc[i][j], 0, 0, 0);
+}
+
+// Waits until this wave's DMA of stage `st` has landed, given that stages up
+// to `issued - 1` have been issued (each later stage may stay in flight).
+__device__ __forceinline__ void big_wait(int st, int issued) {
+  const int later = issued - 1 - st;
+  if (later >= 2) wait_vmcnt<2 * Big::PER_WAVE>();
+  else if (later == 1) wait_vmcnt<Big::PER_WAVE>();
+  else wait_vmcnt<0>();
+}
+
+// One K-step for a wave with all four row sub-tiles live: the 32 MFMAs of
+// stage `cur` are issued in eight groups of four, and after each group one DMA
+// instruction of stage kt+4 and two fragment reads of stage kt+1.  Issue is in
+// order, so a long run of DMA or LDS instructions would hold the MFMA pipe
+// idle while the texture and LDS queues drain; spreading them keeps the pipe
+// fed.  Scheduling barriers pin this order.
+template <int EPI>
+__device__ __forceinline__ void big_step_full(f32x16_t (&acc)[4][4], const BigFrags& cur, BigFrags& nxt,
+                                              u32x4_t* refill, const u32x4_t* __restrict__ next_buf, bool dma,
+                                              int kbytes, const BigPlan& d, u32x4_t ra, u32x4_t rb, int wave,
+                                              const int (&a_slot)[2], const int (&b_slot)[2]) {
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    const int h = g >> 2, i = g & 3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[h][j], cur.a[h][i], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (dma) {
+      if (g < 4) dma16(refill + (g * 4 + wave) * 64, ra, d.a_off[g], kbytes);
+      else dma16(refill + Big::A_SLOTS + ((g - 4) * 4 + wave) * 64, rb, d.b_off[g - 4], kbytes);
+    }
+    // fragment reads of the next stage: g = 0..3 weight (h = g>>1), g = 4..7 rows
+    if (g < 4) {
+      const int hh = g >> 1, jj = (g & 1) * 2;
+      nxt.b[hh][jj] = __builtin_bit_cast(bf16x8_t, next_buf[b_slot[hh] + big_b_off<EPI>(jj)]);
+      nxt.b[hh][jj + 1] = __builtin_bit_cast(bf16x8_t, next_buf[b_slot[hh] + big_b_off<EPI>(jj + 1)]);
+    } else {
+      const int hh = (g - 4) >> 1, ii = ((g - 4) & 1) * 2;
+      nxt.a[hh][ii] = __builtin_bit_cast(bf16x8_t, next_buf[a_slot[hh] + 128 * ii]);
+      nxt.a[hh][ii + 1] = __builtin_bit_cast(bf16x8_t, next_buf[a_slot[hh] + 128 * (ii + 1)]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// K loop: a 4-deep LDS ring filled by DMA three stages ahead and two register
+// sets of fragments.  Step kt: wait for stage kt+1 and barrier (which also
+// proves every wave has read stage kt out of LDS), refill that buffer with
+// stage kt+4, read stage kt+1's fragments into the spare register set, and run
+// stage kt's MFMAs, which hide the latency of those reads.  The last step
+// reads a stale (in-bounds) buffer that is never used, so every path reaches
+// the MFMAs with the same, fully waited, fragment reads.
+template <int EPI, int LIVE>
+__device__ __forceinline__ void big_kloop(f32x16_t (&acc)[4][4], u32x4_t* s0, u32x4_t* s1, u32x4_t* s2,
+                                          u32x4_t* s3, const BigPlan& d, u32x4_t ra, u32x4_t rb, int wave, int KT,
+                                          const int (&a_slot)[2], const int (&b_slot)[2]) {
+  u32x4_t* bufs[4] = {s0, s1, s2, s3};
+  int issued = 0;
+#pragma unroll
+  for (int st = 0; st < 3; ++st)
+    if (st < KT) {
+      big_issue(bufs[st], d, ra, rb, wave, st * Big::KB * 2);
+      ++issued;
+    }
+  big_wait(0, issued);
+  lds_barrier();
+  if (3 < KT) {
+    big_issue(s3, d, ra, rb, wave, 3 * Big::KB * 2);
+    ++issued;
+  }
+  BigFrags fx, fy;
+  big_read<EPI, LIVE>(fx, s0, a_slot, b_slot);
+  for (int kt0 = 0; kt0 < KT; kt0 += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kt = kt0 + u;
+      if (kt >= KT) break;
+      BigFrags& cur = (u & 1) ? fy : fx;
+      BigFrags& nxt = (u & 1) ? fx : fy;
+      big_wait(kt + 1, issued);
+      lds_barrier();
+      const bool dma = kt + 4 < KT;
+      if (LIVE == 4) {
+        big_step_full<EPI>(acc, cur, nxt, bufs[u], bufs[(u + 1) & 3], dma, (kt + 4) * Big::KB * 2, d, ra, rb,
+                           wave, a_slot, b_slot);
+      } else {
+        if (dma) big_issue(bufs[u], d, ra, rb, wave, (kt + 4) * Big::KB * 2);
+        big_read<EPI, LIVE>(nxt, bufs[(u + 1) & 3], a_slot, b_slot);
+        big_mma<LIVE>(acc, cur);
+      }
+      if (dma) ++issued;
+    }
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_big_kernel(GemmArgs p) {
+  constexpr int BM = Big::BM;
+  constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
+
+  __shared__ u32x4_t st0[Big::SLOTS];
+  __shared__ u32x4_t st1[Big::SLOTS];
+  __shared__ u32x4_t st2[Big::SLOTS];
+  __shared__ u32x4_t st3[Big::SLOTS];
+  __shared__ int s_off[kMaxGroups + 1];
+  __shared__ int s_tb[kMaxGroups + 1];
+  __shared__ int s_wsum[kThreads / 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int G = p.G;
+  build_schedule<BM>(p, s_off, s_tb, s_wsum, tid, lane, wave);
+
+  const int total_m = s_tb[G];
+  const int nblk = (p.N + BN_OUT - 1) / BN_OUT;
+  const int total = total_m * nblk;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int nslots = gridDim.x / kXcds;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int t_begin = xcd * per;
+  const int t_end = min(total, t_begin + per);
+  const int KT = p.K / Big::KB;
+  const uint32_t row_bytes = (uint32_t)p.K * 2u;
+
+  // fragment slots: lane reads row (l & 31) of a 32-row sub-tile, chunk
+  // 2h + (l >> 5) of the stage for k16 half h
+  const int rin = lane & 31;
+  int a_slot[2], b_slot[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int pos = (2 * h + (lane >> 5)) ^ big_swz(rin);
+    a_slot[h] = (128 * wm + rin) * 4 + pos;
+    b_slot[h] = Big::A_SLOTS + (((EPI == EPI_SWIGLU) ? 64 : 128) * wn + rin) * 4 + pos;
+  }
+
+  for (int t = t_begin + slot; t < t_end; t += nslots) {
+    const int mt = t / nblk;
+    const int nb = t - mt * nblk;
+    int lo = 0, hi = G;  // s_tb[lo] <= mt < s_tb[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_tb[mid] <= mt) lo = mid; else hi = mid;
+    }
+    const int g = __builtin_amdgcn_readfirstlane(lo);
+    const int m0 = __builtin_amdgcn_readfirstlane(s_off[g] + (mt - s_tb[g]) * BM);
+    const int rows = __builtin_amdgcn_readfirstlane(min(BM, s_off[g + 1] - m0));
+    const int n0 = nb * BN_OUT;
+    const uint16_t* Bg = p.B + (int64_t)g * p.b_group_stride;
+
+    // DMA plan: slot s = q*64 + lane holds row s/4 (16 rows per instruction)
+    BigPlan d;
+#pragma unroll
+    for (int qi = 0; qi < 4; ++qi) {
+      const int q = qi * 4 + wave;
+      const int r = q * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ big_swz(r);
+      if (r < rows) {
+        const int grow = p.gather ? p.gather[m0 + r] : (m0 + r);
+        d.a_off[qi] = (uint32_t)grow * row_bytes + (uint32_t)c * 16u;
+      } else {
+        d.a_off[qi] = 0x80000000u;  // past the buffer: reads zero, moves no data
+      }
+      int wr;
+      if (EPI == EPI_SWIGLU) {
+        const int col = min(n0 + (r & 127), p.N - 1);
+        wr = (r < 128) ? col : p.up_row0 + col;
+      } else {
+        wr = min(n0 + r, p.N - 1);
+      }
+      d.b_off[qi] = (uint32_t)wr * row_bytes + (uint32_t)c * 16u;
+    }
+    const u32x4_t ra = make_rsrc(p.A, (uint32_t)p.a_rows * row_bytes);
+    const int b_rows_total = (EPI == EPI_SWIGLU) ? 2 * p.up_row0 : p.N;
+    const u32x4_t rb = make_rsrc(Bg, (uint32_t)b_rows_total * row_bytes);
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+
+    const int live = __builtin_amdgcn_readfirstlane(min(4, max(0, (rows - 128 * wm + 31) >> 5)));
+    switch (live) {
+#define MOE_BIG_CASE(n) \
+  case n: big_kloop<EPI, n>(acc, st0, st1, st2, st3, d, ra, rb, wave, KT, a_slot, b_slot); break;
+      MOE_BIG_CASE(0) MOE_BIG_CASE(1) MOE_BIG_CASE(2) MOE_BIG_CASE(3) MOE_BIG_CASE(4)
+#undef MOE_BIG_CASE
+      default: break;
+    }
+    lds_barrier();
+
+    // ---- epilogue: lane owns row (l & 31) and columns 8g + 4*(l>>5) + {0..3}
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= live) break;
+      const int row = 128 * wm + 32 * i + rin;
+      if (row >= rows) continue;
+      if (EPI == EPI_SWIGLU) {
+        uint16_t* out = reinterpret_cast<uint16_t*>(p.out) + (int64_t)(m0 + row) * p.ldo;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int col = n0 + 64 * wn + 32 * j + 8 * gq + 4 * (lane >> 5);
+            if (col >= p.N) continue;
+            uint32_t hb[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float gv = acc[i][j][4 * gq + c];
+              const float uv = acc[i][j + 2][4 * gq + c];
+              hb[c] = f32_to_bf16_rne(gv / (1.0f + __expf(-gv)) * uv);
+            }
+            uint2 v;
+            v.x = hb[0] | (hb[1] << 16);
+            v.y = hb[2] | (hb[3] << 16);
+            *reinterpret_cast<uint2*>(out + col) = v;
+          }
+        }
+      } else {
+        float* out = reinterpret_cast<float*>(p.out) + (int64_t)(m0 + row) * p.ldo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int col = n0 + 128 * wn + 32 * j + 8 * gq + 4 * (lane >> 5);
+            if (col >= p.N) continue;
+            *reinterpret_cast<f32x4_t*>(out + col) =
+                f32x4_t{acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]};
+          }
+        }
+      }
+    }
+  }
+}
+
 // Shared-expert gate logits x . g (one wave per token, fp32 accumulation of
 // exact bf16 products).
 __global__ __launch_bounds__(256) void gate_logit_bf16_kernel(const uint16_t* __restrict__ x,
@@ -415,6 +750,38 @@ hipError_t launch_bm(const GemmArgs& a, hipStream_t s, const char* name) {
 }
 
 template <int EPI>
+int resident_big_per_cu() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grouped_gemm_bf16_big_kernel<EPI>, kThreads, 0) !=
+            hipSuccess || n < 1)
+      n = 1;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int EPI>
+hipError_t launch_big(const GemmArgs& a, hipStream_t s, const char* name) {
+  constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
+  const int64_t nblk = (a.N + BN_OUT - 1) / BN_OUT;
+  int64_t ub_m = (a.M + Big::BM - 1) / Big::BM;
+  if (a.offsets) ub_m += (a.G < a.M ? a.G : a.M);
+  const int64_t ub = ub_m * nblk;
+  int64_t grid = (int64_t)device_cu_count() * resident_big_per_cu<EPI>();
+  if (ub < grid) grid = ub;
+  grid = ((grid + kXcds - 1) / kXcds) * kXcds;
+  if (grid < kXcds) grid = kXcds;
+  profile_begin(name, s);
+  hipLaunchKernelGGL((grouped_gemm_bf16_big_kernel<EPI>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  profile_end(s);
+  return hipGetLastError();
+}
+
+template <int EPI>
 hipError_t launch_epi(const GemmArgs& a, hipStream_t s, const char* name) {
   // rows per group on average decides the m-tile height
   const int64_t groups = a.offsets ? (a.G < a.M ? a.G : a.M) : 1;
@@ -422,7 +789,8 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s, const char* name) {
   if (avg <= 16) return launch_bm<16, EPI>(a, s, name);
   if (avg <= 32) return launch_bm<32, EPI>(a, s, name);
   if (avg <= 64) return launch_bm<64, EPI>(a, s, name);
-  return launch_bm<128, EPI>(a, s, name);
+  if (avg < 192) return launch_bm<128, EPI>(a, s, name);
+  return launch_big<EPI>(a, s, name);
 }
 
 }  // namespace

@@ -52,6 +52,13 @@ SMALL = {
         name="bf16_zipf_small", num_tokens=700, hidden_size=256, intermediate_size=128),
     "f32_ragged": workloads.config("tiny_fp32").scaled(
         name="f32_ragged", num_tokens=77, hidden_size=40, num_experts=12, top_k=5, intermediate_size=48),
+    # hundreds of rows per expert: the 256-row tile path, ragged in rows and in
+    # both column blocks (I = 192 = 128 + 64, H = 320 = 256 + 64)
+    "bf16_big_tiles": workloads.config("qwen3_30b_a3b_prefill").scaled(
+        name="bf16_big_tiles", num_tokens=1200, hidden_size=320, num_experts=4, top_k=2, intermediate_size=192),
+    # 256-row tiles with a K loop of two steps
+    "bf16_big_short_k": workloads.config("qwen3_30b_a3b_prefill").scaled(
+        name="bf16_big_short_k", num_tokens=600, hidden_size=64, num_experts=2, top_k=1, intermediate_size=64),
 }
 
 
