@@ -119,6 +119,7 @@ struct ForwardLayout {
   float* y;
   void* hs;
   float* ys;
+  int* counters;  // tile counters of the four grouped GEMMs (routed, shared)
   size_t bytes;
 };
 
@@ -140,6 +141,7 @@ ForwardLayout carve_forward(void* ws, int64_t T, int64_t H, int64_t E, int64_t k
   L.y = c.take<float>((size_t)(P * H));
   L.hs = c.take<char>((size_t)(Is > 0 ? T * Is : 0) * dtype_size(dtype));
   L.ys = c.take<float>((size_t)(Is > 0 ? T * H : 0));
+  L.counters = c.take<int>(4 * moe::kTileCounterInts);
   L.bytes = c.off;
   return L;
 }
@@ -179,9 +181,10 @@ hipError_t run_router(const void* x, const void* wr, const float* bias, const vo
   return moe::launch_topk(logits, T, E, k, renorm, ids, weights, probs, s);
 }
 
+// counters: 2 * kTileCounterInts zeroed ints (gate/up, down) or NULL.
 hipError_t run_ffn(const void* x, const int32_t* gather, const int32_t* offsets, const void* w13, const void* w2,
                    int T_rows, int P, int H, int E, int I, int dtype, void* h, float* y, hipStream_t s,
-                   bool shared) {
+                   bool shared, int* counters) {
   hipError_t e;
   if (dtype == MOE_DTYPE_BF16) {
     moe::GemmArgs a = gemm_args();
@@ -198,6 +201,7 @@ hipError_t run_ffn(const void* x, const int32_t* gather, const int32_t* offsets,
     a.up_row0 = I;
     a.out = h;
     a.ldo = I;
+    a.tile_counter = counters;
     e = moe::launch_grouped_gemm_bf16(a, moe::EPI_SWIGLU, s, shared ? "shared_gate_up_bf16" : "ffn_gate_up_bf16");
     if (e != hipSuccess) return e;
     moe::GemmArgs b = gemm_args();
@@ -213,6 +217,7 @@ hipError_t run_ffn(const void* x, const int32_t* gather, const int32_t* offsets,
     b.N = H;
     b.out = y;
     b.ldo = H;
+    b.tile_counter = counters ? counters + moe::kTileCounterInts : nullptr;
     return moe::launch_grouped_gemm_bf16(b, moe::EPI_F32, s, shared ? "shared_down_bf16" : "ffn_down_bf16");
   }
   e = moe::launch_ffn_gate_up_f32(static_cast<const float*>(x), gather, offsets, static_cast<const float*>(w13), P,
@@ -346,7 +351,8 @@ size_t moe_grouped_ffn_workspace_size(int64_t num_tokens, int64_t top_k, int64_t
                                       int64_t intermediate_size, int dtype) {
   (void)num_experts;
   if (num_tokens < 0 || top_k < 1 || intermediate_size < 1) return 0;
-  return align_up((size_t)(num_tokens * top_k * intermediate_size) * dtype_size(dtype));
+  // tile counters of the two GEMMs, then h
+  return kAlign + align_up((size_t)(num_tokens * top_k * intermediate_size) * dtype_size(dtype));
 }
 
 moe_status moe_grouped_ffn(const void* hidden_states, const int32_t* packed_token_indices,
@@ -375,10 +381,15 @@ moe_status moe_grouped_ffn(const void* hidden_states, const int32_t* packed_toke
   REQUIRE_ALIGNED(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int P = (int)(num_tokens * top_k);
+  int* counters = static_cast<int*>(workspace);
+  void* h = static_cast<char*>(workspace) + kAlign;
+  if (dtype == MOE_DTYPE_BF16) {
+    hipError_t ez = moe::launch_zero_ints(counters, 2 * moe::kTileCounterInts, s);
+    if (ez != hipSuccess) return hip_status(ez, "moe_grouped_ffn");
+  }
   return hip_status(run_ffn(hidden_states, packed_token_indices, expert_offsets, w13, w2, (int)num_tokens, P,
-                            (int)hidden_size,
-                            (int)num_experts, (int)intermediate_size, dtype, workspace, packed_expert_outputs, s,
-                            false),
+                            (int)hidden_size, (int)num_experts, (int)intermediate_size, dtype, h,
+                            packed_expert_outputs, s, false, dtype == MOE_DTYPE_BF16 ? counters : nullptr),
                     "moe_grouped_ffn");
 }
 
@@ -468,15 +479,17 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
   hipError_t e = run_router(hidden_states, router_weight, router_bias, Is ? shared_gate : nullptr, T, H, E, k,
                             renormalize ? 1 : 0, dtype, logits, nullptr, ids, weights, Is ? L.gate_logit : nullptr, s);
   if (e != hipSuccess) return hip_status(e, "moe_forward(router)");
+  // the dispatch scan also zeroes the tile counters of the grouped GEMMs below
   e = moe::launch_dispatch(ids, nullptr, T, k, E, L.counts, L.offsets, L.perm, L.inv, L.packed_ids, nullptr,
-                           L.dispatch_scratch, s);
+                           L.dispatch_scratch, s, L.counters, 4 * moe::kTileCounterInts);
   if (e != hipSuccess) return hip_status(e, "moe_forward(dispatch)");
   if (Is) {
     e = run_ffn(hidden_states, nullptr, nullptr, shared_w13, shared_w2, T, T, H, 1, (int)Is, dtype, L.hs, L.ys, s,
-                true);
+                true, L.counters + 2 * moe::kTileCounterInts);
     if (e != hipSuccess) return hip_status(e, "moe_forward(shared expert)");
   }
-  e = run_ffn(hidden_states, L.packed_ids, L.offsets, w13, w2, T, P, H, E, I, dtype, L.h, L.y, s, false);
+  e = run_ffn(hidden_states, L.packed_ids, L.offsets, w13, w2, T, P, H, E, I, dtype, L.h, L.y, s, false,
+              L.counters);
   if (e != hipSuccess) return hip_status(e, "moe_forward(experts)");
   e = moe::launch_combine(L.y, L.inv, weights, Is ? L.ys : nullptr, Is ? L.gate_logit : nullptr, T, H, k,
                           out_dtype == MOE_DTYPE_BF16, output, s);

@@ -58,9 +58,12 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 }
 
 // Single workgroup of 1024 threads (16 waves).
+// Also zeroes `zero_ints` (the tile counters of the grouped GEMMs that follow).
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ seg, int U, int E, int P,
                                                              int32_t* __restrict__ counts,
-                                                             int32_t* __restrict__ offsets) {
+                                                             int32_t* __restrict__ offsets, int* zero_ints,
+                                                             int n_zero) {
+  if (zero_ints != nullptr && (int)threadIdx.x < n_zero) zero_ints[threadIdx.x] = 0;
   __shared__ int tot[kMaxE];
   __shared__ int wsum[16];
   const int lane = threadIdx.x & 63;
@@ -142,7 +145,7 @@ size_t dispatch_scratch_bytes(int64_t P, int64_t E) {
 
 hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int E, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* packed_ids, float* packed_w,
-                           void* scratch, hipStream_t s) {
+                           void* scratch, hipStream_t s, int* zero_ints, int n_zero) {
   const int P = T * k;
   if (P == 0) return hipSuccess;
   const int U = (P + kSeg - 1) / kSeg;
@@ -152,7 +155,8 @@ hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int
   hipLaunchKernelGGL(dispatch_hist_kernel, dim3(blocks), dim3(256), 0, s, ids, P, E, U, seg);
   profile_end(s);
   profile_begin("dispatch_scan", s);
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, seg, U, E, P, counts, offsets);
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, seg, U, E, P, counts, offsets, zero_ints,
+                     n_zero);
   profile_end(s);
   profile_begin("dispatch_scatter", s);
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(blocks), dim3(256), 0, s, ids, w, P, k, E, U, seg, offsets,

@@ -381,7 +381,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
 // ---------------------------------------------------------------------------
 // Large-group variant (groups of hundreds of rows, e.g. prefill): 256 x 256
 // tiles, BK = 32 per stage, a 4-stage ring (32 KB per stage), 2 x 2 waves of
-// 128 x 128 computed with v_mfma_f32_32x32x16_bf16 (4 x 4 sub-tiles of 32 x 32).
+// 128 x 128 computed with v_mfma_f32_32x32x16_bf16 (4 x 4 sub-tiles of 32 x 32;
+// wave row wm owns the tile's 32-row sub-tiles wm, wm+2, wm+4, wm+6).
 // On gfx950 the 32x32x16 shape sustains about 1.5x the rate of 16x16x32 and
 // does so at one wave per SIMD.  Per stage a wave issues 16 fragment reads for
 // 32 MFMAs, and the CU streams 64 KB per 2 x 256 x 256 x 64 flops, about 31
@@ -443,7 +444,7 @@ __device__ __forceinline__ void big_read(BigFrags& f, const u32x4_t* __restrict_
 #pragma unroll
     for (int j = 0; j < 4; ++j) f.b[h][j] = __builtin_bit_cast(bf16x8_t, buf[b_slot[h] + big_b_off<EPI>(j)]);
 #pragma unroll
-    for (int i = 0; i < LIVE; ++i) f.a[h][i] = __builtin_bit_cast(bf16x8_t, buf[a_slot[h] + 128 * i]);
+    for (int i = 0; i < LIVE; ++i) f.a[h][i] = __builtin_bit_cast(bf16x8_t, buf[a_slot[h] + 256 * i]);
   }
 }
 
@@ -489,15 +490,17 @@ __device__ __forceinline__ void big_step_full(f32x16_t (&acc)[4][4], const BigFr
       if (g < 4) dma16(refill + (g * 4 + wave) * 64, ra, d.a_off[g], kbytes);
       else dma16(refill + Big::A_SLOTS + ((g - 4) * 4 + wave) * 64, rb, d.b_off[g - 4], kbytes);
     }
-    // fragment reads of the next stage: g = 0..3 weight (h = g>>1), g = 4..7 rows
-    if (g < 4) {
-      const int hh = g >> 1, jj = (g & 1) * 2;
-      nxt.b[hh][jj] = __builtin_bit_cast(bf16x8_t, next_buf[b_slot[hh] + big_b_off<EPI>(jj)]);
-      nxt.b[hh][jj + 1] = __builtin_bit_cast(bf16x8_t, next_buf[b_slot[hh] + big_b_off<EPI>(jj + 1)]);
-    } else {
-      const int hh = (g - 4) >> 1, ii = ((g - 4) & 1) * 2;
-      nxt.a[hh][ii] = __builtin_bit_cast(bf16x8_t, next_buf[a_slot[hh] + 128 * ii]);
-      nxt.a[hh][ii + 1] = __builtin_bit_cast(bf16x8_t, next_buf[a_slot[hh] + 128 * (ii + 1)]);
+    // fragment reads of the next stage, all in the first half of the step so
+    // that they have landed by the time the step ends at the next barrier:
+    // g = 0, 1 weight sub-tiles (h = g), g = 2, 3 row sub-tiles (h = g - 2)
+    if (g < 2) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        nxt.b[g][jj] = __builtin_bit_cast(bf16x8_t, next_buf[b_slot[g] + big_b_off<EPI>(jj)]);
+    } else if (g < 4) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        nxt.a[g - 2][ii] = __builtin_bit_cast(bf16x8_t, next_buf[a_slot[g - 2] + 256 * ii]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -592,11 +595,26 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_big_kernel(GemmArg
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int pos = (2 * h + (lane >> 5)) ^ big_swz(rin);
-    a_slot[h] = (128 * wm + rin) * 4 + pos;
+    a_slot[h] = (32 * wm + rin) * 4 + pos;
     b_slot[h] = Big::A_SLOTS + (((EPI == EPI_SWIGLU) ? 64 : 128) * wn + rin) * 4 + pos;
   }
 
-  for (int t = t_begin + slot; t < t_end; t += nslots) {
+  // Tile loop.  With p.tile_counter the tiles of this XCD's range are handed
+  // out dynamically: a free workgroup takes the next tile in list order, which
+  // balances ragged tiles and keeps neighbouring tiles close in time.  The grab
+  // for the following tile is issued when a tile starts and its result is
+  // consumed only after the K loop, when no DMA is in flight.
+  __shared__ int s_grab;
+  int t_local = slot;
+  if (p.tile_counter) {
+    if (tid == 0) s_grab = atomicAdd(&p.tile_counter[xcd], 1);
+    __syncthreads();
+    t_local = s_grab;
+  }
+  while (t_begin + t_local < t_end) {
+    const int t = t_begin + t_local;
+    int next_grab = 0;
+    if (p.tile_counter && tid == 0) next_grab = atomicAdd(&p.tile_counter[xcd], 1);
     const int mt = t / nblk;
     const int nb = t - mt * nblk;
     int lo = 0, hi = G;  // s_tb[lo] <= mt < s_tb[hi]
@@ -642,7 +660,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_big_kernel(GemmArg
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
-    const int live = __builtin_amdgcn_readfirstlane(min(4, max(0, (rows - 128 * wm + 31) >> 5)));
+    // 32-row sub-tiles of the tile alternate between the two wave rows, so a
+    // ragged tile keeps both halves of the SIMDs busy
+    const int units = (rows + 31) >> 5;
+    const int live = __builtin_amdgcn_readfirstlane(min(4, (units - wm + 1) >> 1));
     switch (live) {
 #define MOE_BIG_CASE(n) \
   case n: big_kloop<EPI, n>(acc, st0, st1, st2, st3, d, ra, rb, wave, KT, a_slot, b_slot); break;
@@ -650,13 +671,15 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_big_kernel(GemmArg
 #undef MOE_BIG_CASE
       default: break;
     }
+    if (p.tile_counter && tid == 0) s_grab = next_grab;
     lds_barrier();
+    t_local = p.tile_counter ? s_grab : t_local + nslots;
 
     // ---- epilogue: lane owns row (l & 31) and columns 8g + 4*(l>>5) + {0..3}
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (i >= live) break;
-      const int row = 128 * wm + 32 * i + rin;
+      const int row = 32 * (2 * i + wm) + rin;
       if (row >= rows) continue;
       if (EPI == EPI_SWIGLU) {
         uint16_t* out = reinterpret_cast<uint16_t*>(p.out) + (int64_t)(m0 + row) * p.ldo;
@@ -713,6 +736,10 @@ __global__ __launch_bounds__(256) void gate_logit_bf16_kernel(const uint16_t* __
 #pragma unroll
   for (int dd = 32; dd >= 1; dd >>= 1) acc += __shfl_xor(acc, dd, 64);
   if (lane == 0) out[t] = acc;
+}
+
+__global__ void zero_ints_kernel(int* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
 }
 
 // Resident workgroups per CU for one instantiation (the persistent grid must
@@ -794,6 +821,18 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s, const char* name) {
 }
 
 }  // namespace
+
+hipError_t launch_zero_ints(int* p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(64), 0, s, p, n);
+  return hipGetLastError();
+}
+
+bool grouped_gemm_uses_counter(const GemmArgs& a) {
+  if (!a.offsets) return a.M >= 192;
+  const int64_t groups = a.G < a.M ? a.G : a.M;
+  return groups > 0 && (a.M + groups - 1) / groups >= 192;
+}
 
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, GemmEpilogue epi, hipStream_t s, const char* name) {
   if (a.M <= 0) return hipSuccess;

@@ -42,7 +42,14 @@ struct GemmArgs {
   int64_t ldo;              // output row stride in elements
   const float* bias;        // EPI_ROUTER: per-column bias or NULL
   float* extra_out;         // EPI_ROUTER: x . b_extra per row, when b_extra != NULL
+  int* tile_counter;        // large-group kernel: 8 zeroed ints (per-XCD tile grabs) or NULL
 };
+
+constexpr int kTileCounterInts = 8;
+// True when the grouped GEMM for `a` runs the large-group kernel (which uses
+// a.tile_counter when given).
+bool grouped_gemm_uses_counter(const GemmArgs& a);
+hipError_t launch_zero_ints(int* p, int n, hipStream_t s);
 
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, GemmEpilogue epi, hipStream_t s, const char* name);
 
@@ -65,7 +72,8 @@ constexpr int kDispatchSegment = 256;  // assignments per wave-segment
 size_t dispatch_scratch_bytes(int64_t P, int64_t E);
 hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int E,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                           int32_t* packed_ids, float* packed_w, void* scratch, hipStream_t s);
+                           int32_t* packed_ids, float* packed_w, void* scratch, hipStream_t s,
+                           int* zero_ints = nullptr, int n_zero = 0);
 
 // ---------------------------------------------------------------- combine
 hipError_t launch_combine(const float* y, const int32_t* inv, const float* w,

@@ -100,7 +100,8 @@ def test_grouped_ffn_validation(lib):
     assert ffn(lib, off=NULL) == INVALID and "expert_offsets" in last(lib)
     assert ffn(lib, gather=NULL) == INVALID and "packed_token_indices" in last(lib)
     need = lib.moe_grouped_ffn_workspace_size(4, 2, 8, 64, BF16)
-    assert need == 4 * 2 * 64 * 2 + (256 - (4 * 2 * 64 * 2) % 256) % 256
+    # 256 bytes of tile counters, then h [P, I] bf16 rounded up to 256 bytes
+    assert need == 256 + 4 * 2 * 64 * 2 + (256 - (4 * 2 * 64 * 2) % 256) % 256
     assert ffn(lib, wsb=need - 1) == WS
     assert ffn(lib, T=0) == OK
 
