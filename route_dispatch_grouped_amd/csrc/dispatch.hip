@@ -7,16 +7,18 @@
 // The P = T*k assignments are cut into segments of 256 consecutive indices, one
 // wavefront per segment.
 //   1. hist    each wave counts its segment per expert in LDS and writes
-//              seg[e][u] (expert-major, U = number of segments).
-//   2. scan    one workgroup: per expert, an exclusive scan of seg[e][0..U) in
-//              place (wave-parallel over u); totals -> counts; an exclusive
-//              scan over experts -> offsets (offsets[E] = P).
-//   3. scatter each wave re-reads its segment 64 assignments at a time, in
+//              cnt[e][u] (expert-major, U = number of segments).
+//   2. scan    one workgroup: per expert, an exclusive scan of cnt[e][0..U)
+//              into base[e][u] (all loads of a lane issued before any store);
+//              totals -> counts; an exclusive scan over experts -> offsets
+//              (offsets[E] = P).
+//   3. scatter each wave stages offsets[e] + base[e][u] for every expert in
+//              LDS, then re-reads its segment 64 assignments at a time, in
 //              index order.  Lanes holding the same expert id find each other
 //              with ballots; a lane's rank among them plus the wave's running
-//              count for that expert plus seg[e][u] plus offsets[e] is the
-//              assignment's position p.  Equal ids therefore keep index order
-//              (stability), and no position depends on the timing of atomics.
+//              count for that expert plus the staged base is the assignment's
+//              position p.  Equal ids therefore keep index order (stability),
+//              and no position depends on the timing of atomics.
 #include "moe_internal.h"
 
 namespace moe {
@@ -26,26 +28,27 @@ constexpr int kSeg = kDispatchSegment;  // 256 assignments per wave
 constexpr int kMaxE = MOE_MAX_GROUPS_INTERNAL;
 
 __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __restrict__ ids, int P, int E, int U,
-                                                            int32_t* __restrict__ seg) {
-  __shared__ int cnt[4][kMaxE];
+                                                            int32_t* __restrict__ cnt) {
+  __shared__ int h[4][kMaxE];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int u = blockIdx.x * 4 + w;
-  for (int e = lane; e < E; e += 64) cnt[w][e] = 0;
+  for (int e = lane; e < E; e += 64) h[w][e] = 0;
   __syncthreads();
   if (u < U) {
+    int id[kSeg / 64];
 #pragma unroll
     for (int r = 0; r < kSeg / 64; ++r) {
       const int a = u * kSeg + r * 64 + lane;
-      if (a < P) {
-        const int id = ids[a];
-        if ((unsigned)id < (unsigned)E) atomicAdd(&cnt[w][id], 1);  // ids outside [0, E) are a caller error
-      }
+      id[r] = (a < P) ? ids[a] : -1;
     }
+#pragma unroll
+    for (int r = 0; r < kSeg / 64; ++r)
+      if ((unsigned)id[r] < (unsigned)E) atomicAdd(&h[w][id[r]], 1);  // ids outside [0, E) are a caller error
   }
   __syncthreads();
   if (u < U)
-    for (int e = lane; e < E; e += 64) seg[(int64_t)e * U + u] = cnt[w][e];
+    for (int e = lane; e < E; e += 64) cnt[(int64_t)e * U + u] = h[w][e];
 }
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
@@ -57,24 +60,41 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-// Single workgroup of 1024 threads (16 waves).
+// Single workgroup of 1024 threads (16 waves); VPL consecutive segments per lane.
 // Also zeroes `zero_ints` (the tile counters of the grouped GEMMs that follow).
-__global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ seg, int U, int E, int P,
+template <int VPL>
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ cnt,
+                                                             int32_t* __restrict__ base, int U, int E, int P,
                                                              int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ offsets, int* zero_ints,
                                                              int n_zero) {
-  if (zero_ints != nullptr && (int)threadIdx.x < n_zero) zero_ints[threadIdx.x] = 0;
   __shared__ int tot[kMaxE];
   __shared__ int wsum[16];
+  if (zero_ints != nullptr && (int)threadIdx.x < n_zero) zero_ints[threadIdx.x] = 0;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   for (int e = w; e < E; e += 16) {
+    const int32_t* src = cnt + (int64_t)e * U;
+    int32_t* dst = base + (int64_t)e * U;
     int carry = 0;
-    for (int u0 = 0; u0 < U; u0 += 64) {
-      const int u = u0 + lane;
-      const int c = (u < U) ? seg[(int64_t)e * U + u] : 0;
-      const int incl = wave_incl_scan(c, lane);
-      if (u < U) seg[(int64_t)e * U + u] = carry + incl - c;
+    for (int u0 = 0; u0 < U; u0 += 64 * VPL) {
+      int v[VPL];
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int u = u0 + lane * VPL + i;
+        v[i] = (u < U) ? src[u] : 0;
+      }
+      int s = 0;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) s += v[i];
+      const int incl = wave_incl_scan(s, lane);
+      int run = carry + incl - s;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int u = u0 + lane * VPL + i;
+        if (u < U) dst[u] = run;
+        run += v[i];
+      }
       carry += __shfl(incl, 63, 64);
     }
     if (lane == 0) tot[e] = carry;
@@ -86,46 +106,54 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
   const int incl = wave_incl_scan(v, lane);
   if (lane == 63) wsum[w] = incl;
   __syncthreads();
-  int base = 0;
-  for (int q = 0; q < w; ++q) base += wsum[q];
+  int b = 0;
+  for (int q = 0; q < w; ++q) b += wsum[q];
   if (i < E) {
     counts[i] = v;
-    offsets[i] = base + incl - v;
+    offsets[i] = b + incl - v;
   }
   if (i == 0) offsets[E] = P;
 }
 
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ wts, int P, int k, int E, int U,
-    const int32_t* __restrict__ seg, const int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    const int32_t* __restrict__ base, const int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv, int32_t* __restrict__ packed_ids, float* __restrict__ packed_w) {
-  __shared__ int run[4][kMaxE];
+  __shared__ int pos0[4][kMaxE];  // offsets[e] + base[e][u], advanced as the wave places assignments
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int u = blockIdx.x * 4 + w;
-  for (int e = lane; e < E; e += 64) run[w][e] = 0;
-  __syncthreads();
-  if (u >= U) return;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-#pragma unroll 1
+  if (u >= U) return;  // no workgroup barrier below: the waves are independent
+  int id[kSeg / 64];
+#pragma unroll
   for (int r = 0; r < kSeg / 64; ++r) {
     const int a = u * kSeg + r * 64 + lane;
-    int id = (a < P) ? ids[a] : -1;
-    const bool valid = (unsigned)id < (unsigned)E;
-    if (!valid) id = -1;
+    id[r] = (a < P) ? ids[a] : -1;
+  }
+  for (int e = lane; e < E; e += 64) pos0[w][e] = offsets[e] + base[(int64_t)e * U + u];
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes land before its reads below
+  __builtin_amdgcn_wave_barrier();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+#pragma unroll
+  for (int r = 0; r < kSeg / 64; ++r) {
+    const int a = u * kSeg + r * 64 + lane;
+    const bool valid = (unsigned)id[r] < (unsigned)E;
+    const int my = valid ? id[r] : -1;
     uint64_t todo = __ballot(valid);
     uint64_t peers = 0;
     while (todo) {
       const int leader = __builtin_ctzll(todo);
-      const int lid = __builtin_amdgcn_readlane(id, leader);
-      const uint64_t m = __ballot(id == lid);
-      if (id == lid) peers = m;
+      const int lid = __builtin_amdgcn_readlane(my, leader);
+      const uint64_t m = __ballot(my == lid);
+      if (my == lid) peers = m;
       todo &= ~m;
     }
     int pos = 0;
-    if (valid) pos = offsets[id] + seg[(int64_t)id * U + u] + run[w][id] + __popcll(peers & lt_mask);
+    if (valid) pos = pos0[w][my] + __popcll(peers & lt_mask);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
-    if (valid && lane == __builtin_ctzll(peers)) run[w][id] += __popcll(peers);
+    if (valid && lane == __builtin_ctzll(peers)) pos0[w][my] += __popcll(peers);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
     if (valid) {
       perm[pos] = a;
@@ -140,7 +168,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 
 size_t dispatch_scratch_bytes(int64_t P, int64_t E) {
   const int64_t U = (P + kSeg - 1) / kSeg;
-  return (size_t)(U * E * (int64_t)sizeof(int32_t));
+  return (size_t)(2 * U * E * (int64_t)sizeof(int32_t));  // counts, then bases
 }
 
 hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int E, int32_t* counts,
@@ -149,17 +177,25 @@ hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int
   const int P = T * k;
   if (P == 0) return hipSuccess;
   const int U = (P + kSeg - 1) / kSeg;
-  int32_t* seg = reinterpret_cast<int32_t*>(scratch);
+  int32_t* cnt = reinterpret_cast<int32_t*>(scratch);
+  int32_t* base = cnt + (int64_t)U * E;
   const unsigned blocks = (unsigned)((U + 3) / 4);
   profile_begin("dispatch_hist", s);
-  hipLaunchKernelGGL(dispatch_hist_kernel, dim3(blocks), dim3(256), 0, s, ids, P, E, U, seg);
+  hipLaunchKernelGGL(dispatch_hist_kernel, dim3(blocks), dim3(256), 0, s, ids, P, E, U, cnt);
   profile_end(s);
   profile_begin("dispatch_scan", s);
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, seg, U, E, P, counts, offsets, zero_ints,
-                     n_zero);
+  if (U <= 64)
+    hipLaunchKernelGGL(dispatch_scan_kernel<1>, dim3(1), dim3(1024), 0, s, cnt, base, U, E, P, counts, offsets,
+                       zero_ints, n_zero);
+  else if (U <= 256)
+    hipLaunchKernelGGL(dispatch_scan_kernel<4>, dim3(1), dim3(1024), 0, s, cnt, base, U, E, P, counts, offsets,
+                       zero_ints, n_zero);
+  else
+    hipLaunchKernelGGL(dispatch_scan_kernel<16>, dim3(1), dim3(1024), 0, s, cnt, base, U, E, P, counts, offsets,
+                       zero_ints, n_zero);
   profile_end(s);
   profile_begin("dispatch_scatter", s);
-  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(blocks), dim3(256), 0, s, ids, w, P, k, E, U, seg, offsets,
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(blocks), dim3(256), 0, s, ids, w, P, k, E, U, base, offsets,
                      perm, inv, packed_ids, packed_w);
   profile_end(s);
   return hipGetLastError();

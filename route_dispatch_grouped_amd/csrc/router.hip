@@ -40,21 +40,52 @@ __device__ __forceinline__ float order_value(uint32_t o) {
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const uint32_t hi = __shfl_xor((unsigned)(v >> 32), d, 64);
-    const uint32_t lo = __shfl_xor((unsigned)(v & 0xFFFFFFFFu), d, 64);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+// One step of a max-reduction through a DPP lane permutation (within 16-lane rows).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+  const int hi = (int)(v >> 32), lo = (int)(v & 0xFFFFFFFFu);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > v ? o : v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+// Wave-wide maximum of a 64-bit key, returned wave-uniform: DPP exchanges
+// (xor 1, xor 2, half-row mirror, row mirror) leave every lane of a 16-lane
+// row holding the row maximum; the four row maxima are then read out with
+// readlane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_step<0xB1>(v);   // quad_perm(1,0,3,2)
+  v = dpp_max_step<0x4E>(v);   // quad_perm(2,3,0,1)
+  v = dpp_max_step<0x141>(v);  // row_half_mirror
+  v = dpp_max_step<0x140>(v);  // row_mirror
+  uint64_t best = 0;
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-  return v;
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), 16 * r);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(v & 0xFFFFFFFFu), 16 * r);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    best = o > best ? o : best;
+  }
+  return best;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add_step(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF,
+                                                         false));
+}
+
+// Wave-wide float sum, wave-uniform (same exchange pattern as wave_max_u64).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_add_step<0xB1>(v);
+  v = dpp_add_step<0x4E>(v);
+  v = dpp_add_step<0x141>(v);
+  v = dpp_add_step<0x140>(v);
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+  return s;
 }
 
 // One wavefront per token.  Lane l holds the logits of experts l, l+64, ...
