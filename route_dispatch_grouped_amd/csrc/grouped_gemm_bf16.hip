@@ -227,6 +227,43 @@ __device__ __forceinline__ void build_schedule(const GemmArgs& p, int* s_off, in
 
 }
 
+// Tile t -> (group g, first packed row m0, rows in the tile, n-block nb).
+// The tiles of group g occupy [s_tb[g]*nblk, s_tb[g+1]*nblk) of the tile list.
+// Inside a group they are numbered in chunks of kChunkM m-tiles, and inside a
+// chunk the m-tile index runs fastest: the tiles that read one weight block
+// are handed out back to back, and the tiles that read one block of activation
+// rows are at most kChunkM apart, close enough in time for the XCD's L2 to
+// serve both reuses.
+constexpr int kChunkM = 4;
+
+struct TileCoord {
+  int g, m0, rows, nb;
+};
+
+template <int BM>
+__device__ __forceinline__ TileCoord tile_coord(int t, int nblk, int G, const int* s_tb, const int* s_off) {
+  const int mt = t / nblk;
+  int lo = 0, hi = G;  // s_tb[lo] <= mt < s_tb[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_tb[mid] <= mt) lo = mid; else hi = mid;
+  }
+  const int mbase = s_tb[lo];
+  const int mcount = s_tb[lo + 1] - mbase;
+  const int local = t - mbase * nblk;
+  const int c = local / (kChunkM * nblk);
+  const int rem = local - c * kChunkM * nblk;
+  const int cs = min(kChunkM, mcount - c * kChunkM);
+  const int nb = rem / cs;
+  const int mi = c * kChunkM + (rem - nb * cs);
+  TileCoord tc;
+  tc.g = __builtin_amdgcn_readfirstlane(lo);
+  tc.m0 = __builtin_amdgcn_readfirstlane(s_off[lo] + mi * BM);
+  tc.rows = __builtin_amdgcn_readfirstlane(min(BM, s_off[lo + 1] - tc.m0));
+  tc.nb = __builtin_amdgcn_readfirstlane(nb);
+  return tc;
+}
+
 template <int BM, int EPI>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p) {
   using C = Tile<BM>;
@@ -268,16 +305,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
                                   : 64 * wave + 16 * j;
 
   for (int t = t_begin + slot; t < t_end; t += nslots) {
-    const int mt = t / nblk;
-    const int nb = t - mt * nblk;
-    int lo = 0, hi = G;  // s_tb[lo] <= mt < s_tb[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_tb[mid] <= mt) lo = mid; else hi = mid;
-    }
-    const int g = __builtin_amdgcn_readfirstlane(lo);
-    const int m0 = __builtin_amdgcn_readfirstlane(s_off[g] + (mt - s_tb[g]) * BM);
-    const int rows = __builtin_amdgcn_readfirstlane(min(BM, s_off[g + 1] - m0));
+    const TileCoord tc = tile_coord<BM>(t, nblk, G, s_tb, s_off);
+    const int g = tc.g, m0 = tc.m0, rows = tc.rows, nb = tc.nb;
     const int msub_live = (rows + 15) >> 4;
     const int n0 = nb * BN_OUT;
     const uint16_t* Bg = p.B + (int64_t)g * p.b_group_stride;
@@ -602,8 +631,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_big_kernel(GemmArg
   // Tile loop.  With p.tile_counter the tiles of this XCD's range are handed
   // out dynamically: a free workgroup takes the next tile in list order, which
   // balances ragged tiles and keeps neighbouring tiles close in time.  The grab
-  // for the following tile is issued when a tile starts and its result is
-  // consumed only after the K loop, when no DMA is in flight.
+  // for the following tile is issued after the K loop (no DMA in flight then)
+  // and consumed after the epilogue, which hides its latency; grabbing any
+  // earlier lets tiles start out of list order, and the weight and row blocks
+  // that neighbouring tiles share then drop out of L2 between their uses.
   __shared__ int s_grab;
   int t_local = slot;
   if (p.tile_counter) {
@@ -614,17 +645,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_big_kernel(GemmArg
   while (t_begin + t_local < t_end) {
     const int t = t_begin + t_local;
     int next_grab = 0;
-    if (p.tile_counter && tid == 0) next_grab = atomicAdd(&p.tile_counter[xcd], 1);
-    const int mt = t / nblk;
-    const int nb = t - mt * nblk;
-    int lo = 0, hi = G;  // s_tb[lo] <= mt < s_tb[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_tb[mid] <= mt) lo = mid; else hi = mid;
-    }
-    const int g = __builtin_amdgcn_readfirstlane(lo);
-    const int m0 = __builtin_amdgcn_readfirstlane(s_off[g] + (mt - s_tb[g]) * BM);
-    const int rows = __builtin_amdgcn_readfirstlane(min(BM, s_off[g + 1] - m0));
+    const TileCoord tc = tile_coord<BM>(t, nblk, G, s_tb, s_off);
+    const int g = tc.g, m0 = tc.m0, rows = tc.rows, nb = tc.nb;
     const int n0 = nb * BN_OUT;
     const uint16_t* Bg = p.B + (int64_t)g * p.b_group_stride;
 
@@ -671,9 +693,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_big_kernel(GemmArg
 #undef MOE_BIG_CASE
       default: break;
     }
-    if (p.tile_counter && tid == 0) s_grab = next_grab;
-    lds_barrier();
-    t_local = p.tile_counter ? s_grab : t_local + nslots;
+    if (p.tile_counter && tid == 0) next_grab = atomicAdd(&p.tile_counter[xcd], 1);
 
     // ---- epilogue: lane owns row (l & 31) and columns 8g + 4*(l>>5) + {0..3}
 #pragma unroll
@@ -716,6 +736,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_big_kernel(GemmArg
         }
       }
     }
+    if (p.tile_counter && tid == 0) s_grab = next_grab;
+    lds_barrier();  // also: every wave is done with the ring before the next tile's DMA
+    t_local = p.tile_counter ? s_grab : t_local + nslots;
   }
 }
 

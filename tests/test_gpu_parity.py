@@ -310,3 +310,30 @@ def test_no_renormalize():
     res = oracle.forward(inp, cfg.top_k, False, ids=ids, weights=w)
     err, rms = rel_max_err(f["out"].cpu().numpy().astype(np.float64), res["out"])
     assert err <= 2e-2 * rms
+
+
+@pytest.mark.parametrize("T,H,k", [(5, 4160, 2), (9, 24, 10), (3, 8, 1), (17, 1032, 9)])
+def test_combine_shapes(T, H, k):
+    """Combine over row widths that need several column passes (H = 4160),
+    partial column groups (H = 24, 8, 1032) and more slots than one gather pass
+    holds (k = 9, 10), with and without the gated shared term."""
+    log(f"[parity] combine T={T} H={H} k={k}")
+    rng = np.random.default_rng(T * 1000 + H + k)
+    P = T * k
+    y = rng.standard_normal((P, H)).astype(np.float32)
+    perm = rng.permutation(P).astype(np.int32)
+    inv = np.empty(P, dtype=np.int32)
+    inv[perm] = np.arange(P, dtype=np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    shared = rng.standard_normal((T, H)).astype(np.float32)
+    gl = rng.standard_normal(T).astype(np.float32)
+    ref = oracle.combine(y.astype(np.float64), inv, w.astype(np.float64))
+    out = rdg.moe_combine(to_device(y), to_device(inv), to_device(w)).cpu().numpy().astype(np.float64)
+    err, rms = rel_max_err(out, ref)
+    assert err <= 1e-5 * rms + 1e-30
+    sig = 1.0 / (1.0 + np.exp(-gl.astype(np.float64)))
+    ref_s = ref + sig[:, None] * shared.astype(np.float64)
+    out_s = rdg.moe_combine(to_device(y), to_device(inv), to_device(w), shared_output=to_device(shared),
+                            shared_gate_logit=to_device(gl)).cpu().numpy().astype(np.float64)
+    err_s, rms_s = rel_max_err(out_s, ref_s)
+    assert err_s <= 1e-5 * rms_s + 1e-30
