@@ -122,6 +122,18 @@ __device__ __forceinline__ void dma16(const u32x4_t* lds_dst, u32x4_t rsrc, uint
       : "memory");
 }
 
+// One 4-byte-per-lane DMA from global to LDS: lane l lands at lds_dst + 4*l.
+__device__ __forceinline__ void dma4(const int* lds_dst, u32x4_t rsrc, uint32_t voff, int soff) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)lds_dst);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "buffer_load_dword %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
 template <int BM>
 __device__ __forceinline__ void issue_stage(u32x4_t* buf, const DmaPlan<BM>& d, u32x4_t ra, u32x4_t rb, int wave,
                                             int kbytes) {
@@ -419,8 +431,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
 // L2 -> LDS DMA path sustains.
 //
 // LDS layout: a row holds four 16-byte chunks (64 bytes); chunk c of row r sits
-// at position c ^ (((r >> 1) ^ (r >> 3)) & 3), which keeps 32-row fragment
-// reads conflict free whether the LDS serves 8 or 16 lanes per cycle.
+// at position c ^ ((r >> 2) & 3).  For the 32-row fragment reads (lane l: row
+// l & 31, chunk 2h + (l >> 5)) this is the placement that gfx950's LDS serves
+// without bank conflicts: measured with the SQ_LDS_BANK_CONFLICT counter on a
+// read-only probe, where XOR patterns built from r & 3, (r >> 1) & 3 or
+// ((r >> 1) ^ (r >> 3)) & 3 all cost 4 extra cycles per ds_read_b128.
 //
 // The MFMA operands are swapped (weight fragment first), so the accumulator
 // holds the transpose: lane l owns output row (l & 31) of a 32 x 32 sub-tile
@@ -437,7 +452,7 @@ struct Big {
   static constexpr int PER_WAVE = 8;              // DMA instructions per wave per stage
 };
 
-__device__ __forceinline__ int big_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int big_swz(int r) { return (r >> 2) & 3; }
 
 struct BigPlan {
   uint32_t a_off[4];
@@ -742,6 +757,300 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_big_kernel(GemmArg
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined variant of the large-group kernel (same tiles, ring, fragments and
+// MFMA schedule) for K loops of at least 8 stages, a multiple of 4.  The ring
+// never drains between tiles: the last four K steps of a tile fill the ring
+// with stages 0..3 of the workgroup's next tile, so that tile's first DMA
+// latency and the epilogue stores of the current tile overlap.
+//
+//  * Tiles are assigned statically (round robin inside the XCD's range), so
+//    the next tile is known without a memory round trip.
+//  * The next tile's gathered row indices are fetched by a 4-byte DMA into LDS
+//    at step KT-8 and read back at step KT-4, after the barrier that follows
+//    the wait which covers that DMA; the compiler therefore never has to wait
+//    for a global load while stage DMAs are in flight.
+//  * vmcnt retires in issue order.  Every stage is 8 DMA instructions per
+//    wave; the epilogue issues exactly kEpiStores buffer stores per wave (rows
+//    and columns outside the output get an offset past the buffer, which the
+//    hardware drops), so each wait below is an exact count of the operations
+//    issued after the stage it needs (an extra index DMA only makes a wait
+//    stricter).  Counts above 63 are clamped: vmcnt cannot exceed 63, so once
+//    more than 63 operations follow a stage, that stage has retired.
+template <int EPI>
+struct PipeEpi {
+  static constexpr int kStores = (EPI == EPI_SWIGLU) ? 32 : 64;
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_clamped() {
+  wait_vmcnt<(N > 63 ? 63 : N)>();
+}
+
+// Next-tile DMA plan from the row indices staged in LDS (gathered rows) or
+// the packed row numbers (contiguous rows).
+template <int EPI>
+__device__ __forceinline__ void pipe_plan(BigPlan& d, const GemmArgs& p, const int* s_gidx, int rows, int m0,
+                                          int n0, int wave, int lane, uint32_t row_bytes) {
+#pragma unroll
+  for (int qi = 0; qi < 4; ++qi) {
+    const int q = qi * 4 + wave;
+    const int r = q * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ big_swz(r);
+    if (r < rows) {
+      const int grow = p.gather ? s_gidx[r] : (m0 + r);
+      d.a_off[qi] = (uint32_t)grow * row_bytes + (uint32_t)c * 16u;
+    } else {
+      d.a_off[qi] = 0x80000000u;
+    }
+    int wr;
+    if (EPI == EPI_SWIGLU) {
+      const int col = min(n0 + (r & 127), p.N - 1);
+      wr = (r < 128) ? col : p.up_row0 + col;
+    } else {
+      wr = min(n0 + r, p.N - 1);
+    }
+    d.b_off[qi] = (uint32_t)wr * row_bytes + (uint32_t)c * 16u;
+  }
+}
+
+struct PipeNext {
+  bool has;
+  int g, m0, rows, n0;
+};
+
+// One tile's K loop.  On entry stages 0..3 of this tile are in flight (or
+// landed); `after_epi` says whether the previous tile's epilogue stores were
+// issued after them.  With nx.has, the loop stages the next tile's row
+// indices, builds its plan into `dn` and issues its stages 0..3.
+template <int EPI, int LIVE>
+__device__ __forceinline__ void pipe_kloop(f32x16_t (&acc)[4][4], u32x4_t* s0, u32x4_t* s1, u32x4_t* s2,
+                                           u32x4_t* s3, int* s_gidx, const GemmArgs& p, const BigPlan& d,
+                                           u32x4_t ra, u32x4_t rb, BigPlan& dn, u32x4_t rbn, const PipeNext& nx,
+                                           bool after_epi, int wave, int lane, int KT, uint32_t row_bytes,
+                                           const int (&a_slot)[2], const int (&b_slot)[2]) {
+  constexpr int S = PipeEpi<EPI>::kStores;
+  u32x4_t* bufs[4] = {s0, s1, s2, s3};
+  if (after_epi) wait_vmcnt_clamped<3 * Big::PER_WAVE + S>();
+  else wait_vmcnt<3 * Big::PER_WAVE>();
+  lds_barrier();
+  BigFrags fx, fy;
+  big_read<EPI, LIVE>(fx, s0, a_slot, b_slot);
+  for (int kt0 = 0; kt0 < KT; kt0 += 4) {
+    const bool last = kt0 + 4 == KT;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kt = kt0 + u;
+      BigFrags& cur = (u & 1) ? fy : fx;
+      BigFrags& nxt = (u & 1) ? fx : fy;
+      // wait for stage kt+1 (the next tile's stage 0 at the last step)
+      if (last && !nx.has) {
+        if (u == 0) wait_vmcnt<2 * Big::PER_WAVE>();
+        else if (u == 1) wait_vmcnt<Big::PER_WAVE>();
+        else wait_vmcnt<0>();
+      } else if (kt0 == 0 && u < 3 && after_epi) {
+        wait_vmcnt_clamped<2 * Big::PER_WAVE + S>();
+      } else {
+        wait_vmcnt<2 * Big::PER_WAVE>();
+      }
+      lds_barrier();
+      if (u == 0 && kt0 + 8 == KT && nx.has && p.gather) {
+        // next tile's row indices -> s_gidx (row 64*wave + lane)
+        const int r = 64 * wave + lane;
+        const uint32_t voff = (r < nx.rows) ? (uint32_t)(nx.m0 + r) * 4u : 0x80000000u;
+        dma4(s_gidx + 64 * wave, make_rsrc(p.gather, (uint32_t)p.M * 4u), voff, 0);
+      }
+      if (u == 0 && last && nx.has) pipe_plan<EPI>(dn, p, s_gidx, nx.rows, nx.m0, nx.n0, wave, lane, row_bytes);
+      bool dma;
+      int kbytes;
+      if (!last) {
+        dma = true;
+        kbytes = (kt + 4) * Big::KB * 2;
+      } else {
+        dma = nx.has;
+        kbytes = u * Big::KB * 2;
+      }
+      const BigPlan& dd = last ? dn : d;
+      const u32x4_t rbs = last ? rbn : rb;
+      if (LIVE == 4) {
+        big_step_full<EPI>(acc, cur, nxt, bufs[u], bufs[(u + 1) & 3], dma, kbytes, dd, ra, rbs, wave, a_slot,
+                           b_slot);
+      } else {
+        if (dma) big_issue(bufs[u], dd, ra, rbs, wave, kbytes);
+        big_read<EPI, LIVE>(nxt, bufs[(u + 1) & 3], a_slot, b_slot);
+        big_mma<LIVE>(acc, cur);
+      }
+    }
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmArgs p) {
+  constexpr int BM = Big::BM;
+  constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
+
+  __shared__ u32x4_t st0[Big::SLOTS];
+  __shared__ u32x4_t st1[Big::SLOTS];
+  __shared__ u32x4_t st2[Big::SLOTS];
+  __shared__ u32x4_t st3[Big::SLOTS];
+  __shared__ int s_off[kMaxGroups + 1];
+  __shared__ int s_tb[kMaxGroups + 1];
+  __shared__ int s_wsum[kThreads / 64];
+  __shared__ int s_gidx[BM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int G = p.G;
+  build_schedule<BM>(p, s_off, s_tb, s_wsum, tid, lane, wave);
+
+  const int total_m = s_tb[G];
+  const int nblk = (p.N + BN_OUT - 1) / BN_OUT;
+  const int total = total_m * nblk;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int nslots = gridDim.x / kXcds;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int t_begin = xcd * per;
+  const int t_end = min(total, t_begin + per);
+  const int KT = p.K / Big::KB;
+  const uint32_t row_bytes = (uint32_t)p.K * 2u;
+  int t = t_begin + slot;
+  if (t >= t_end) return;  // whole workgroup, after the last barrier it takes part in
+
+  const int rin = lane & 31;
+  int a_slot[2], b_slot[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int pos = (2 * h + (lane >> 5)) ^ big_swz(rin);
+    a_slot[h] = (32 * wm + rin) * 4 + pos;
+    b_slot[h] = Big::A_SLOTS + (((EPI == EPI_SWIGLU) ? 64 : 128) * wn + rin) * 4 + pos;
+  }
+  const u32x4_t ra = make_rsrc(p.A, (uint32_t)p.a_rows * row_bytes);
+  const int b_rows_total = (EPI == EPI_SWIGLU) ? 2 * p.up_row0 : p.N;
+  const uint32_t b_bytes = (uint32_t)b_rows_total * row_bytes;
+  const size_t out_elt = (EPI == EPI_SWIGLU) ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc(p.out, (short)0, (int)((size_t)p.M * p.ldo * out_elt), kBufferWord3);
+
+  // first tile: plan from global row indices (nothing is in flight yet)
+  TileCoord tc = tile_coord<BM>(t, nblk, G, s_tb, s_off);
+  BigPlan d;
+  {
+    const int n0 = tc.nb * BN_OUT;
+#pragma unroll
+    for (int qi = 0; qi < 4; ++qi) {
+      const int q = qi * 4 + wave;
+      const int r = q * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ big_swz(r);
+      if (r < tc.rows) {
+        const int grow = p.gather ? p.gather[tc.m0 + r] : (tc.m0 + r);
+        d.a_off[qi] = (uint32_t)grow * row_bytes + (uint32_t)c * 16u;
+      } else {
+        d.a_off[qi] = 0x80000000u;
+      }
+      int wr;
+      if (EPI == EPI_SWIGLU) {
+        const int col = min(n0 + (r & 127), p.N - 1);
+        wr = (r < 128) ? col : p.up_row0 + col;
+      } else {
+        wr = min(n0 + r, p.N - 1);
+      }
+      d.b_off[qi] = (uint32_t)wr * row_bytes + (uint32_t)c * 16u;
+    }
+  }
+  u32x4_t rb = make_rsrc(p.B + (int64_t)tc.g * p.b_group_stride, b_bytes);
+  big_issue(st0, d, ra, rb, wave, 0);
+  big_issue(st1, d, ra, rb, wave, 1 * Big::KB * 2);
+  big_issue(st2, d, ra, rb, wave, 2 * Big::KB * 2);
+  big_issue(st3, d, ra, rb, wave, 3 * Big::KB * 2);
+
+  bool after_epi = false;
+  while (true) {
+    const int g = tc.g, m0 = tc.m0, rows = tc.rows, n0 = tc.nb * BN_OUT;
+    PipeNext nx;
+    const int tn = t + nslots;
+    nx.has = tn < t_end;
+    TileCoord tcn = tc;
+    if (nx.has) tcn = tile_coord<BM>(tn, nblk, G, s_tb, s_off);
+    nx.g = tcn.g;
+    nx.m0 = tcn.m0;
+    nx.rows = tcn.rows;
+    nx.n0 = tcn.nb * BN_OUT;
+    const u32x4_t rbn = make_rsrc(p.B + (int64_t)tcn.g * p.b_group_stride, b_bytes);
+    BigPlan dn = d;
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+
+    const int units = (rows + 31) >> 5;
+    const int live = __builtin_amdgcn_readfirstlane(min(4, (units - wm + 1) >> 1));
+    switch (live) {
+#define MOE_PIPE_CASE(n)                                                                                       \
+  case n:                                                                                                      \
+    pipe_kloop<EPI, n>(acc, st0, st1, st2, st3, s_gidx, p, d, ra, rb, dn, rbn, nx, after_epi, wave, lane, KT, \
+                       row_bytes, a_slot, b_slot);                                                             \
+    break;
+      MOE_PIPE_CASE(0) MOE_PIPE_CASE(1) MOE_PIPE_CASE(2) MOE_PIPE_CASE(3) MOE_PIPE_CASE(4)
+#undef MOE_PIPE_CASE
+      default: break;
+    }
+
+    // ---- epilogue: exactly PipeEpi<EPI>::kStores buffer stores per wave
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 32 * (2 * i + wm) + rin;
+      const bool row_ok = row < rows;
+      if (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int col = n0 + 64 * wn + 32 * j + 8 * gq + 4 * (lane >> 5);
+            uint32_t hb[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float gv = acc[i][j][4 * gq + c];
+              const float uv = acc[i][j + 2][4 * gq + c];
+              hb[c] = f32_to_bf16_rne(gv / (1.0f + __expf(-gv)) * uv);
+            }
+            typedef int i32x2_t __attribute__((ext_vector_type(2)));
+            const i32x2_t v = {(int)(hb[0] | (hb[1] << 16)), (int)(hb[2] | (hb[3] << 16))};
+            const uint32_t off = (row_ok && col < p.N) ? (uint32_t)(((int64_t)(m0 + row) * p.ldo + col) * 2)
+                                                       : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b64(v, ro, (int)off, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int col = n0 + 128 * wn + 32 * j + 8 * gq + 4 * (lane >> 5);
+            typedef float f32x4b_t __attribute__((ext_vector_type(4)));
+            const f32x4b_t v = {acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
+                                acc[i][j][4 * gq + 3]};
+            const uint32_t off = (row_ok && col < p.N) ? (uint32_t)(((int64_t)(m0 + row) * p.ldo + col) * 4)
+                                                       : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), ro, (int)off, 0, 0);
+          }
+        }
+      }
+    }
+    if (!nx.has) break;
+    (void)g;
+    t = tn;
+    tc = tcn;
+    d = dn;
+    rb = rbn;
+    after_epi = true;
+  }
+}
+
 // Shared-expert gate logits x . g (one wave per token, fp32 accumulation of
 // exact bf16 products).
 __global__ __launch_bounds__(256) void gate_logit_bf16_kernel(const uint16_t* __restrict__ x,
@@ -832,6 +1141,23 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s, const char* name) {
 }
 
 template <int EPI>
+hipError_t launch_pipe(const GemmArgs& a, hipStream_t s, const char* name) {
+  constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
+  const int64_t nblk = (a.N + BN_OUT - 1) / BN_OUT;
+  int64_t ub_m = (a.M + Big::BM - 1) / Big::BM;
+  if (a.offsets) ub_m += (a.G < a.M ? a.G : a.M);
+  const int64_t ub = ub_m * nblk;
+  int64_t grid = (int64_t)device_cu_count();
+  if (ub < grid) grid = ub;
+  grid = ((grid + kXcds - 1) / kXcds) * kXcds;
+  if (grid < kXcds) grid = kXcds;
+  profile_begin(name, s);
+  hipLaunchKernelGGL((grouped_gemm_bf16_pipe_kernel<EPI>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  profile_end(s);
+  return hipGetLastError();
+}
+
+template <int EPI>
 hipError_t launch_epi(const GemmArgs& a, hipStream_t s, const char* name) {
   // rows per group on average decides the m-tile height
   const int64_t groups = a.offsets ? (a.G < a.M ? a.G : a.M) : 1;
@@ -840,6 +1166,8 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s, const char* name) {
   if (avg <= 32) return launch_bm<32, EPI>(a, s, name);
   if (avg <= 64) return launch_bm<64, EPI>(a, s, name);
   if (avg < 192) return launch_bm<128, EPI>(a, s, name);
+  const int64_t KT = a.K / Big::KB;
+  if (KT >= 8 && KT % 4 == 0) return launch_pipe<EPI>(a, s, name);
   return launch_big<EPI>(a, s, name);
 }
 

@@ -59,6 +59,10 @@ SMALL = {
     # 256-row tiles with a K loop of two steps
     "bf16_big_short_k": workloads.config("qwen3_30b_a3b_prefill").scaled(
         name="bf16_big_short_k", num_tokens=600, hidden_size=64, num_experts=2, top_k=1, intermediate_size=64),
+    # the pipelined 256-row kernel (K loops of 16 and 8 stages) with about two
+    # tiles per workgroup, so the ring carries over from tile to tile
+    "bf16_pipe_tiles": workloads.config("qwen3_30b_a3b_prefill").scaled(
+        name="bf16_pipe_tiles", num_tokens=8192, hidden_size=512, num_experts=16, top_k=8, intermediate_size=256),
 }
 
 
