@@ -51,7 +51,8 @@ def kernel_work(name, cfg, touched, touched_shared=True):
     P = T * k
     es = 2 if cfg.dtype == "bf16" else 4
     if name in ("ffn_gate_up_bf16", "ffn_gate_up_f32"):
-        return 4.0 * P * H * I, touched * 2 * I * H * es + P * H * es + P * I * es
+        # weights of touched experts, every token row once, h written once
+        return 4.0 * P * H * I, touched * 2 * I * H * es + T * H * es + P * I * es
     if name in ("ffn_down_bf16", "ffn_down_f32"):
         return 2.0 * P * H * I, touched * H * I * es + P * I * es + P * H * 4
     if name == "shared_gate_up_bf16":
@@ -72,6 +73,45 @@ def kernel_work(name, cfg, touched, touched_shared=True):
     if name == "combine":
         return 0.0, P * H * 4 + P * 8 + T * H * 4 + (T * H * 4 if Is else 0)
     return 0.0, 0.0
+
+
+# rocprofv3 counter summaries: profiles/<kernel>_<workload>_traffic.txt holds
+# "key: value" lines, among them the SHA-256 of the kernel's source file at the
+# time the counters were taken.
+KERNEL_SOURCES = {
+    "ffn_gate_up_bf16": "route_dispatch_grouped_amd/csrc/grouped_gemm_bf16.hip",
+    "ffn_down_bf16": "route_dispatch_grouped_amd/csrc/grouped_gemm_bf16.hip",
+    "combine": "route_dispatch_grouped_amd/csrc/combine.hip",
+}
+
+
+def measured_traffic(name, workload):
+    """HBM bytes per launch of kernel `name` from its committed FETCH_SIZE and
+    WRITE_SIZE summary, each scaled by what the counter read for a plain device
+    copy of known size; None when there is no summary or the kernel's source
+    has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{name}_{workload}_traffic.txt")
+    src = KERNEL_SOURCES.get(name)
+    if src is None or not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    with open(os.path.join(ROOT, src), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if kv.get("source_sha256") != sha:
+        return None
+    try:
+        copy_bytes = float(kv["copy_bytes"])
+        fetch_scale = copy_bytes / (float(kv["copy_fetch_kib"]) * 1024.0)
+        write_scale = copy_bytes / (float(kv["copy_write_kib"]) * 1024.0)
+        return (float(kv["fetch_kib_per_launch"]) * 1024.0 * fetch_scale +
+                float(kv["write_kib_per_launch"]) * 1024.0 * write_scale)
+    except (KeyError, ValueError, ZeroDivisionError):
+        return None
 
 
 def roofline_entry(name, cfg, avg_s, touched):
@@ -231,6 +271,8 @@ def main():
     if dominant is not None:
         ms, c = kernels[dominant]
         roof = roofline_entry(dominant, cfg, ms / c / 1e3, touched)
+        tr = measured_traffic(dominant, cfg.name)
+        roof["traffic"] = None if tr is None else round(tr)
 
     # grouped FFN (gate/up + down) as a fraction of bf16 peak
     ffn = None
