@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_MAX_EXPERTS 512
 
 typedef enum moe_status {
@@ -160,10 +160,11 @@ moe_status moe_dispatch_plan(const int32_t* topk_ids, const float* topk_weights,
  * Numerics (bf16): fp32 accumulation, h rounded once to bf16 (it is the
  * operand of the second bf16 GEMM), outputs fp32.  f32: fp32 throughout.
  * Experts with no rows are skipped and their weights are not read.
- * workspace: moe_grouped_ffn_workspace_size(...) bytes (holds h).
+ * workspace: moe_grouped_ffn_workspace_size(...) bytes (tile counters, h,
+ * and for few rows per expert the fp32 partial sums of a split K loop).
  */
-size_t moe_grouped_ffn_workspace_size(int64_t num_tokens, int64_t top_k, int64_t num_experts,
-                                      int64_t intermediate_size, int dtype);
+size_t moe_grouped_ffn_workspace_size(int64_t num_tokens, int64_t hidden_size, int64_t top_k,
+                                      int64_t num_experts, int64_t intermediate_size, int dtype);
 moe_status moe_grouped_ffn(const void* hidden_states, const int32_t* packed_token_indices,
                            const int32_t* expert_offsets, const void* w13, const void* w2,
                            int64_t num_tokens, int64_t hidden_size, int64_t num_experts,

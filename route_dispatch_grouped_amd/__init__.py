@@ -59,7 +59,7 @@ _SIGNATURES = {
     "moe_dispatch_workspace_size": (_size, [_i64, _i64, _i64]),
     "moe_dispatch_plan": (_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
-    "moe_grouped_ffn_workspace_size": (_size, [_i64, _i64, _i64, _i64, _int]),
+    "moe_grouped_ffn_workspace_size": (_size, [_i64, _i64, _i64, _i64, _i64, _int]),
     "moe_grouped_ffn": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64,
                                _i64, _int, _c_void_p, _c_void_p, _size, _c_void_p]),
     "moe_combine": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _int,
@@ -236,7 +236,7 @@ def moe_grouped_ffn(hidden_states: torch.Tensor, packed_token_indices: Optional[
         _need(expert_offsets, "expert_offsets", (E + 1,), torch.int32)
     dev = hidden_states.device
     y = torch.empty((P, H), dtype=torch.float32, device=dev)
-    ws_bytes = lib.moe_grouped_ffn_workspace_size(T, top_k, E, I, _dtype_code(dt))
+    ws_bytes = lib.moe_grouped_ffn_workspace_size(T, H, top_k, E, I, _dtype_code(dt))
     ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
     st = lib.moe_grouped_ffn(_ptr(hidden_states), _ptr(packed_token_indices), _ptr(expert_offsets), _ptr(w13),
                              _ptr(w2), T, H, E, int(top_k), I, _dtype_code(dt), _ptr(y), _ptr(ws), ws.numel(),

@@ -8,6 +8,7 @@
 //   experts down -> combine.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -120,8 +121,23 @@ struct ForwardLayout {
   void* hs;
   float* ys;
   int* counters;  // tile counters of the four grouped GEMMs (routed, shared)
+  float* partial;  // split-K partial sums, shared by the grouped GEMMs (they run in order)
   size_t bytes;
 };
+
+// Split-K scratch of one FFN (gate/up then down) over P rows in E groups.
+size_t ffn_pair_partial_bytes(int64_t P, int64_t H, int64_t E, bool grouped, int64_t I, int dtype) {
+  if (dtype != MOE_DTYPE_BF16 || P <= 0 || I <= 0) return 0;
+  return std::max(moe::grouped_gemm_partial_bytes(P, E, grouped, I, H, moe::EPI_SWIGLU),
+                  moe::grouped_gemm_partial_bytes(P, E, grouped, H, I, moe::EPI_F32));
+}
+
+// Split-K scratch of the forward: routed experts and the shared expert.
+size_t ffn_partial_bytes(int64_t T, int64_t H, int64_t E, int64_t k, int64_t I, int64_t Is, int dtype) {
+  size_t b = ffn_pair_partial_bytes(T * k, H, E, true, I, dtype);
+  if (Is > 0) b = std::max(b, ffn_pair_partial_bytes(T, H, 1, false, Is, dtype));
+  return b;
+}
 
 ForwardLayout carve_forward(void* ws, int64_t T, int64_t H, int64_t E, int64_t k, int64_t I, int64_t Is, int dtype) {
   const int64_t P = T * k;
@@ -142,6 +158,7 @@ ForwardLayout carve_forward(void* ws, int64_t T, int64_t H, int64_t E, int64_t k
   L.hs = c.take<char>((size_t)(Is > 0 ? T * Is : 0) * dtype_size(dtype));
   L.ys = c.take<float>((size_t)(Is > 0 ? T * H : 0));
   L.counters = c.take<int>(4 * moe::kTileCounterInts);
+  L.partial = c.take<float>(ffn_partial_bytes(T, H, E, k, I, Is, dtype) / sizeof(float));
   L.bytes = c.off;
   return L;
 }
@@ -157,7 +174,10 @@ hipError_t run_router(const void* x, const void* wr, const float* bias, const vo
                       int renorm, int dtype, float* logits, float* probs, int32_t* ids, float* weights,
                       float* gate_logit, hipStream_t s) {
   hipError_t e;
-  if (dtype == MOE_DTYPE_BF16) {
+  if (dtype == MOE_DTYPE_BF16 && T <= moe::kRouterSmallT) {
+    e = moe::launch_router_small_t_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr), bias,
+                                        static_cast<const uint16_t*>(gate), T, H, E, logits, gate_logit, s);
+  } else if (dtype == MOE_DTYPE_BF16) {
     moe::GemmArgs a = gemm_args();
     a.A = static_cast<const uint16_t*>(x);
     a.M = T;
@@ -184,7 +204,7 @@ hipError_t run_router(const void* x, const void* wr, const float* bias, const vo
 // counters: 2 * kTileCounterInts zeroed ints (gate/up, down) or NULL.
 hipError_t run_ffn(const void* x, const int32_t* gather, const int32_t* offsets, const void* w13, const void* w2,
                    int T_rows, int P, int H, int E, int I, int dtype, void* h, float* y, hipStream_t s,
-                   bool shared, int* counters) {
+                   bool shared, int* counters, float* partial) {
   hipError_t e;
   if (dtype == MOE_DTYPE_BF16) {
     moe::GemmArgs a = gemm_args();
@@ -202,6 +222,7 @@ hipError_t run_ffn(const void* x, const int32_t* gather, const int32_t* offsets,
     a.out = h;
     a.ldo = I;
     a.tile_counter = counters;
+    a.partial = partial;
     e = moe::launch_grouped_gemm_bf16(a, moe::EPI_SWIGLU, s, shared ? "shared_gate_up_bf16" : "ffn_gate_up_bf16");
     if (e != hipSuccess) return e;
     moe::GemmArgs b = gemm_args();
@@ -218,6 +239,7 @@ hipError_t run_ffn(const void* x, const int32_t* gather, const int32_t* offsets,
     b.out = y;
     b.ldo = H;
     b.tile_counter = counters ? counters + moe::kTileCounterInts : nullptr;
+    b.partial = partial;
     return moe::launch_grouped_gemm_bf16(b, moe::EPI_F32, s, shared ? "shared_down_bf16" : "ffn_down_bf16");
   }
   e = moe::launch_ffn_gate_up_f32(static_cast<const float*>(x), gather, offsets, static_cast<const float*>(w13), P,
@@ -347,12 +369,21 @@ moe_status moe_dispatch_plan(const int32_t* topk_ids, const float* topk_weights,
                     "moe_dispatch_plan");
 }
 
-size_t moe_grouped_ffn_workspace_size(int64_t num_tokens, int64_t top_k, int64_t num_experts,
+// Split-K scratch of moe_grouped_ffn; with one expert the offsets may be
+// absent (one ungrouped block) or present, and the two can split differently.
+size_t grouped_ffn_partial_bytes(int64_t P, int64_t H, int64_t E, int64_t I, int dtype) {
+  size_t b = ffn_pair_partial_bytes(P, H, E, true, I, dtype);
+  if (E == 1) b = std::max(b, ffn_pair_partial_bytes(P, H, 1, false, I, dtype));
+  return b;
+}
+
+size_t moe_grouped_ffn_workspace_size(int64_t num_tokens, int64_t hidden_size, int64_t top_k, int64_t num_experts,
                                       int64_t intermediate_size, int dtype) {
-  (void)num_experts;
-  if (num_tokens < 0 || top_k < 1 || intermediate_size < 1) return 0;
-  // tile counters of the two GEMMs, then h
-  return kAlign + align_up((size_t)(num_tokens * top_k * intermediate_size) * dtype_size(dtype));
+  if (num_tokens < 0 || hidden_size < 1 || top_k < 1 || num_experts < 1 || intermediate_size < 1) return 0;
+  const int64_t P = num_tokens * top_k;
+  // tile counters of the two GEMMs, h, then the split-K partial sums
+  return kAlign + align_up((size_t)(P * intermediate_size) * dtype_size(dtype)) +
+         align_up(grouped_ffn_partial_bytes(P, hidden_size, num_experts, intermediate_size, dtype));
 }
 
 moe_status moe_grouped_ffn(const void* hidden_states, const int32_t* packed_token_indices,
@@ -376,20 +407,26 @@ moe_status moe_grouped_ffn(const void* hidden_states, const int32_t* packed_toke
   REQUIRE_ALIGNED(w13);
   REQUIRE_ALIGNED(w2);
   REQUIRE_ALIGNED(packed_expert_outputs);
-  const size_t need = moe_grouped_ffn_workspace_size(num_tokens, top_k, num_experts, intermediate_size, dtype);
+  const size_t need =
+      moe_grouped_ffn_workspace_size(num_tokens, hidden_size, top_k, num_experts, intermediate_size, dtype);
   if (workspace == nullptr || workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small");
   REQUIRE_ALIGNED(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int P = (int)(num_tokens * top_k);
   int* counters = static_cast<int*>(workspace);
   void* h = static_cast<char*>(workspace) + kAlign;
+  const size_t part_bytes = grouped_ffn_partial_bytes(P, hidden_size, num_experts, intermediate_size, dtype);
+  float* partial = part_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kAlign +
+                                                         align_up((size_t)P * intermediate_size * dtype_size(dtype)))
+                              : nullptr;
   if (dtype == MOE_DTYPE_BF16) {
     hipError_t ez = moe::launch_zero_ints(counters, 2 * moe::kTileCounterInts, s);
     if (ez != hipSuccess) return hip_status(ez, "moe_grouped_ffn");
   }
   return hip_status(run_ffn(hidden_states, packed_token_indices, expert_offsets, w13, w2, (int)num_tokens, P,
                             (int)hidden_size, (int)num_experts, (int)intermediate_size, dtype, h,
-                            packed_expert_outputs, s, false, dtype == MOE_DTYPE_BF16 ? counters : nullptr),
+                            packed_expert_outputs, s, false, dtype == MOE_DTYPE_BF16 ? counters : nullptr,
+                            partial),
                     "moe_grouped_ffn");
 }
 
@@ -485,11 +522,11 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
   if (e != hipSuccess) return hip_status(e, "moe_forward(dispatch)");
   if (Is) {
     e = run_ffn(hidden_states, nullptr, nullptr, shared_w13, shared_w2, T, T, H, 1, (int)Is, dtype, L.hs, L.ys, s,
-                true, L.counters + 2 * moe::kTileCounterInts);
+                true, L.counters + 2 * moe::kTileCounterInts, L.partial);
     if (e != hipSuccess) return hip_status(e, "moe_forward(shared expert)");
   }
   e = run_ffn(hidden_states, L.packed_ids, L.offsets, w13, w2, T, P, H, E, I, dtype, L.h, L.y, s, false,
-              L.counters);
+              L.counters, L.partial);
   if (e != hipSuccess) return hip_status(e, "moe_forward(experts)");
   e = moe::launch_combine(L.y, L.inv, weights, Is ? L.ys : nullptr, Is ? L.gate_logit : nullptr, T, H, k,
                           out_dtype == MOE_DTYPE_BF16, output, s);

@@ -174,14 +174,14 @@ __device__ __forceinline__ void mma_stage(f32x4_t (&acc)[BM / 16][4], const u32x
 template <int BM, int LIVE>
 __device__ __forceinline__ void kloop(f32x4_t (&acc)[BM / 16][4], u32x4_t* s0, u32x4_t* s1, u32x4_t* s2,
                                       u32x4_t* s3, const DmaPlan<BM>& d, u32x4_t ra, u32x4_t rb, int wave,
-                                      int lane, int KT, bool wave_live,
+                                      int lane, int KT, int kbase, bool wave_live,
                                       const int (&brow)[4]) {
   using C = Tile<BM>;
   constexpr int NS = C::NS;
-  // prologue: stages 0 .. NS-2 in flight
-  issue_stage<BM>(s0, d, ra, rb, wave, 0);
-  if (KT > 1) issue_stage<BM>(s1, d, ra, rb, wave, BK * 2);
-  if (NS == 4 && KT > 2) issue_stage<BM>(s2, d, ra, rb, wave, 2 * BK * 2);
+  // prologue: stages 0 .. NS-2 in flight (kbase: byte offset of this tile's K range)
+  issue_stage<BM>(s0, d, ra, rb, wave, kbase);
+  if (KT > 1) issue_stage<BM>(s1, d, ra, rb, wave, kbase + BK * 2);
+  if (NS == 4 && KT > 2) issue_stage<BM>(s2, d, ra, rb, wave, kbase + 2 * BK * 2);
   u32x4_t* bufs[4] = {s0, s1, s2, s3};
   for (int kt0 = 0; kt0 < KT; kt0 += NS) {
 #pragma unroll
@@ -192,7 +192,8 @@ __device__ __forceinline__ void kloop(f32x4_t (&acc)[BM / 16][4], u32x4_t* s0, u
       if (kt + NS - 2 < KT) wait_vmcnt<C::VM_WAIT>();
       else wait_vmcnt<0>();
       lds_barrier();
-      if (kt + NS - 1 < KT) issue_stage<BM>(bufs[(u + NS - 1) % NS], d, ra, rb, wave, (kt + NS - 1) * BK * 2);
+      if (kt + NS - 1 < KT)
+        issue_stage<BM>(bufs[(u + NS - 1) % NS], d, ra, rb, wave, kbase + (kt + NS - 1) * BK * 2);
       if (wave_live) mma_stage<BM, LIVE>(acc, bufs[u], brow, lane);
     }
   }
@@ -299,14 +300,19 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
 
   const int total_m = s_tb[G];
   const int nblk = (p.N + BN_OUT - 1) / BN_OUT;
-  const int total = total_m * nblk;
+  // split-K: the K range is cut into p.ksplit chunks of KTc stages; tile t
+  // covers (m-tile, n-block) t % total_mn and chunk t / total_mn
+  const int ksplit = (EPI != EPI_ROUTER && p.partial != nullptr && p.ksplit > 1) ? p.ksplit : 1;
+  const int total_mn = total_m * nblk;
+  const int total = total_mn * ksplit;
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int nslots = gridDim.x / kXcds;
   const int per = (total + kXcds - 1) / kXcds;
   const int t_begin = xcd * per;
   const int t_end = min(total, t_begin + per);
-  const int KT = p.K / BK;
+  const int KT_all = p.K / BK;
+  const int KTc = (KT_all + ksplit - 1) / ksplit;
   const uint32_t row_bytes = (uint32_t)p.K * 2u;
 
   // weight rows of this wave inside the 256-row B tile (sub-tile bases)
@@ -317,9 +323,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
                                   : 64 * wave + 16 * j;
 
   for (int t = t_begin + slot; t < t_end; t += nslots) {
-    const TileCoord tc = tile_coord<BM>(t, nblk, G, s_tb, s_off);
+    const int kc = __builtin_amdgcn_readfirstlane(t / total_mn);
+    const TileCoord tc = tile_coord<BM>(t - kc * total_mn, nblk, G, s_tb, s_off);
     const int g = tc.g, m0 = tc.m0, rows = tc.rows, nb = tc.nb;
     const int msub_live = (rows + 15) >> 4;
+    const int KT = min(KTc, KT_all - kc * KTc);
+    const int kbase = kc * KTc * BK * 2;
     const int n0 = nb * BN_OUT;
     const uint16_t* Bg = p.B + (int64_t)g * p.b_group_stride;
 
@@ -365,7 +374,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
 #define MOE_LIVE_CASE(n)                                                                                      \
   case n:                                                                                                     \
     if (n <= MSUB)                                                                                            \
-      kloop<BM, (n <= MSUB ? n : MSUB)>(acc, st0, st1, st2, st3, d, ra, rb, wave, lane, KT, wave_live, brow); \
+      kloop<BM, (n <= MSUB ? n : MSUB)>(acc, st0, st1, st2, st3, d, ra, rb, wave, lane, KT, kbase, wave_live, \
+                                        brow);                                                              \
     break;
       MOE_LIVE_CASE(1) MOE_LIVE_CASE(2) MOE_LIVE_CASE(3) MOE_LIVE_CASE(4)
       MOE_LIVE_CASE(5) MOE_LIVE_CASE(6) MOE_LIVE_CASE(7) MOE_LIVE_CASE(8)
@@ -376,7 +386,33 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
     lds_barrier();
 
     // ---- epilogue.  C fragment: lane holds column (lane & 15), rows 4*(lane>>4)+r
-    if (wave_live) {
+    if (wave_live && ksplit > 1) {
+      // raw fp32 sums of this K chunk: partial[kc][row][col] (SwiGLU: gate
+      // columns [0, N), up columns [N, 2N))
+      const int ldp = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;
+      float* part = p.partial + (int64_t)kc * p.M * ldp;
+#pragma unroll
+      for (int i = 0; i < MSUB; ++i) {
+        if (i >= msub_live) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          int col;
+          if (EPI == EPI_SWIGLU) {
+            const int c0 = wave_col0 + 16 * (j & 1) + (lane & 15);
+            if (c0 >= p.N) continue;
+            col = (j < 2) ? c0 : p.N + c0;
+          } else {
+            col = wave_col0 + 16 * j + (lane & 15);
+            if (col >= p.N) continue;
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 16 * i + 4 * (lane >> 4) + r;
+            if (row < rows) part[(int64_t)(m0 + row) * ldp + col] = acc[i][j][r];
+          }
+        }
+      }
+    } else if (wave_live) {
 #pragma unroll
       for (int i = 0; i < MSUB; ++i) {
         if (i >= msub_live) continue;
@@ -1051,6 +1087,37 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
   }
 }
 
+// Split-K reduction: the chunks' fp32 partial sums added in chunk order (so
+// the result does not depend on timing), then the epilogue of the unsplit
+// kernel: SwiGLU to bf16 h, or fp32 y.  One thread per 4 columns of a row.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int ksplit, int M,
+                                                            int N, void* __restrict__ out, int64_t ldo) {
+  const int ldp = (EPI == EPI_SWIGLU) ? 2 * N : N;
+  const int n4 = N >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)M * n4) return;
+  const int row = (int)(idx / n4);
+  const int col = (int)(idx - (int64_t)row * n4) * 4;
+  const int64_t plane = (int64_t)M * ldp;
+  const float* src = partial + (int64_t)row * ldp + col;
+  f32x4_t a = *reinterpret_cast<const f32x4_t*>(src);
+  for (int s = 1; s < ksplit; ++s) a += *reinterpret_cast<const f32x4_t*>(src + s * plane);
+  if (EPI == EPI_SWIGLU) {
+    f32x4_t u = *reinterpret_cast<const f32x4_t*>(src + N);
+    for (int s = 1; s < ksplit; ++s) u += *reinterpret_cast<const f32x4_t*>(src + N + s * plane);
+    uint32_t hb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) hb[c] = f32_to_bf16_rne(a[c] / (1.0f + __expf(-a[c])) * u[c]);
+    uint2 v;
+    v.x = hb[0] | (hb[1] << 16);
+    v.y = hb[2] | (hb[3] << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + row * ldo + col) = v;
+  } else {
+    *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + row * ldo + col) = a;
+  }
+}
+
 // Shared-expert gate logits x . g (one wave per token, fp32 accumulation of
 // exact bf16 products).
 __global__ __launch_bounds__(256) void gate_logit_bf16_kernel(const uint16_t* __restrict__ x,
@@ -1091,19 +1158,63 @@ int resident_blocks_per_cu() {
   return cached[dev];
 }
 
+// m-tile height the grouped GEMM picks for M rows in `groups` groups (0: the
+// 256-row kernels).  From 96 rows per group on average the 256-row tiles win
+// even when half their rows are padding: a weight block is read once per
+// m-tile, and with 128-row tiles a group of 100-150 rows already needs two.
+int pick_bm(int64_t M, int64_t groups) {
+  const int64_t avg = groups > 0 ? (M + groups - 1) / groups : M;
+  if (avg <= 16) return 16;
+  if (avg <= 32) return 32;
+  if (avg <= 64) return 64;
+  if (avg < 96) return 128;
+  return 0;
+}
+
+// Split-K for the weight-streaming regime (small m-tiles): with few
+// (m-tile, n-block) tiles the chip is not filled and each CU streams a long
+// weight panel alone; cutting K gives about kSplitTarget tiles, every chunk at
+// least kSplitMinStages K stages (shorter chunks are all DMA prologue).
+// Decided from the shapes and the tile upper bound only; the constants are
+// the best of a sweep on the Qwen1.5-MoE decode shape.
+constexpr int64_t kSplitTarget = 256;
+constexpr int64_t kSplitMinStages = 8;
+
+int ksplit_for(int64_t M, int64_t G, bool grouped, int64_t N, int64_t K, GemmEpilogue epi) {
+  if (epi == EPI_ROUTER || M <= 0) return 1;
+  const int64_t groups = grouped ? (G < M ? G : M) : 1;
+  const int bm = pick_bm(M, groups);
+  if (bm == 0) return 1;
+  const int64_t bn = (epi == EPI_SWIGLU) ? 128 : 256;
+  const int64_t tiles = ((M + bm - 1) / bm + (grouped ? groups : 0)) * ((N + bn - 1) / bn);
+  const int64_t KT = K / BK;
+  int64_t ks = (kSplitTarget + tiles - 1) / tiles;
+  if (ks > KT / kSplitMinStages) ks = KT / kSplitMinStages;
+  if (ks <= 1) return 1;
+  const int64_t ktc = (KT + ks - 1) / ks;
+  return (int)((KT + ktc - 1) / ktc);  // no empty chunk
+}
+
 template <int BM, int EPI>
-hipError_t launch_bm(const GemmArgs& a, hipStream_t s, const char* name) {
+hipError_t launch_bm(const GemmArgs& a_in, hipStream_t s, const char* name) {
   constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
+  GemmArgs a = a_in;
+  a.ksplit = (a.partial != nullptr) ? ksplit_for(a.M, a.G, a.offsets != nullptr, a.N, a.K, (GemmEpilogue)EPI) : 1;
   const int64_t nblk = (a.N + BN_OUT - 1) / BN_OUT;
   int64_t ub_m = (a.M + BM - 1) / BM;
   if (a.offsets) ub_m += (a.G < a.M ? a.G : a.M);
-  const int64_t ub = ub_m * nblk;
+  const int64_t ub = ub_m * nblk * a.ksplit;
   int64_t grid = (int64_t)device_cu_count() * resident_blocks_per_cu<BM, EPI>();
   if (ub < grid) grid = ub;
   grid = ((grid + kXcds - 1) / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
   profile_begin(name, s);
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, EPI>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  if (EPI != EPI_ROUTER && a.ksplit > 1) {
+    const int64_t n = (int64_t)a.M * (a.N / 4);
+    hipLaunchKernelGGL((splitk_reduce_kernel<EPI>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.partial,
+                       a.ksplit, a.M, a.N, a.out, a.ldo);
+  }
   profile_end(s);
   return hipGetLastError();
 }
@@ -1161,11 +1272,13 @@ template <int EPI>
 hipError_t launch_epi(const GemmArgs& a, hipStream_t s, const char* name) {
   // rows per group on average decides the m-tile height
   const int64_t groups = a.offsets ? (a.G < a.M ? a.G : a.M) : 1;
-  const int64_t avg = groups > 0 ? (a.M + groups - 1) / groups : a.M;
-  if (avg <= 16) return launch_bm<16, EPI>(a, s, name);
-  if (avg <= 32) return launch_bm<32, EPI>(a, s, name);
-  if (avg <= 64) return launch_bm<64, EPI>(a, s, name);
-  if (avg < 192) return launch_bm<128, EPI>(a, s, name);
+  switch (pick_bm(a.M, groups)) {
+    case 16: return launch_bm<16, EPI>(a, s, name);
+    case 32: return launch_bm<32, EPI>(a, s, name);
+    case 64: return launch_bm<64, EPI>(a, s, name);
+    case 128: return launch_bm<128, EPI>(a, s, name);
+    default: break;
+  }
   const int64_t KT = a.K / Big::KB;
   if (KT >= 8 && KT % 4 == 0) return launch_pipe<EPI>(a, s, name);
   return launch_big<EPI>(a, s, name);
@@ -1180,9 +1293,18 @@ hipError_t launch_zero_ints(int* p, int n, hipStream_t s) {
 }
 
 bool grouped_gemm_uses_counter(const GemmArgs& a) {
-  if (!a.offsets) return a.M >= 192;
-  const int64_t groups = a.G < a.M ? a.G : a.M;
-  return groups > 0 && (a.M + groups - 1) / groups >= 192;
+  return pick_bm(a.M, a.offsets ? (a.G < a.M ? a.G : a.M) : 1) == 0;
+}
+
+int grouped_gemm_ksplit(int64_t M, int64_t G, bool grouped, int64_t N, int64_t K, GemmEpilogue epi) {
+  return ksplit_for(M, G, grouped, N, K, epi);
+}
+
+size_t grouped_gemm_partial_bytes(int64_t M, int64_t G, bool grouped, int64_t N, int64_t K, GemmEpilogue epi) {
+  const int ks = ksplit_for(M, G, grouped, N, K, epi);
+  if (ks <= 1) return 0;
+  const int64_t ldp = (epi == EPI_SWIGLU) ? 2 * N : N;
+  return (size_t)ks * (size_t)M * (size_t)ldp * sizeof(float);
 }
 
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, GemmEpilogue epi, hipStream_t s, const char* name) {

@@ -43,6 +43,8 @@ struct GemmArgs {
   const float* bias;        // EPI_ROUTER: per-column bias or NULL
   float* extra_out;         // EPI_ROUTER: x . b_extra per row, when b_extra != NULL
   int* tile_counter;        // large-group kernel: 8 zeroed ints (per-XCD tile grabs) or NULL
+  float* partial;           // split-K scratch of grouped_gemm_partial_bytes() bytes, or NULL (no split)
+  int ksplit;               // set by launch_grouped_gemm_bf16 (callers leave it 0)
 };
 
 constexpr int kTileCounterInts = 8;
@@ -52,6 +54,20 @@ bool grouped_gemm_uses_counter(const GemmArgs& a);
 hipError_t launch_zero_ints(int* p, int n, hipStream_t s);
 
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, GemmEpilogue epi, hipStream_t s, const char* name);
+
+// Split-K factor the bf16 grouped GEMM uses for a problem of M packed rows in
+// G groups, N output columns and reduction length K (1: no split; the
+// router epilogue never splits), and the bytes of fp32 partial sums it then
+// needs in GemmArgs::partial (0 without a split).  Both depend on the shapes
+// only.
+int grouped_gemm_ksplit(int64_t M, int64_t G, bool grouped, int64_t N, int64_t K, GemmEpilogue epi);
+size_t grouped_gemm_partial_bytes(int64_t M, int64_t G, bool grouped, int64_t N, int64_t K, GemmEpilogue epi);
+
+// Router logits (+ shared-gate logit when gate != NULL) for T <= kRouterSmallT
+// bf16 tokens, without the GEMM tiling.
+constexpr int kRouterSmallT = 64;
+hipError_t launch_router_small_t_bf16(const uint16_t* x, const uint16_t* wr, const float* bias, const uint16_t* gate,
+                                      int T, int H, int E, float* logits, float* gate_logit, hipStream_t s);
 
 // ---------------------------------------------------------------- fp32 path
 hipError_t launch_router_logits_f32(const float* x, const float* wr, const float* bias,

@@ -173,7 +173,79 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   }
 }
 
+// Router logits for a handful of tokens (decode batches), bf16: workgroup
+// (r, b) computes row r of the router weight (r == E: the shared-expert gate
+// vector) against tokens [16b, 16b + 16).  Each thread owns 8 consecutive
+// hidden elements per pass (16-byte loads) and one fp32 partial dot product
+// per token; the exact bf16 products are summed in fp32, then across the wave
+// (DPP) and across the four waves (LDS).  The weight row is read once; the
+// token rows, 4 KB each at H = 2048, come from L2 for all but the first row.
+constexpr int kSmallT = 16;
+
+__device__ __forceinline__ void bf16x8_to_f32(const uint4 v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+__global__ __launch_bounds__(256) void router_small_t_bf16_kernel(const uint16_t* __restrict__ x,
+                                                                  const uint16_t* __restrict__ wr,
+                                                                  const float* __restrict__ bias,
+                                                                  const uint16_t* __restrict__ gate, int T, int H,
+                                                                  int E, float* __restrict__ logits,
+                                                                  float* __restrict__ gate_logit) {
+  const int r = blockIdx.x;
+  const int t0 = blockIdx.y * kSmallT;
+  const int nt = min(kSmallT, T - t0);
+  const uint16_t* w = (r < E) ? wr + (int64_t)r * H : gate;
+  float acc[kSmallT];
+#pragma unroll
+  for (int tt = 0; tt < kSmallT; ++tt) acc[tt] = 0.f;
+  for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
+    float wf[8];
+    bf16x8_to_f32(*reinterpret_cast<const uint4*>(w + h), wf);
+#pragma unroll
+    for (int tt = 0; tt < kSmallT; ++tt) {
+      if (tt < nt) {
+        float xf[8];
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(x + (int64_t)(t0 + tt) * H + h), xf);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[tt] = fmaf(xf[c], wf[c], acc[tt]);
+      }
+    }
+  }
+  __shared__ float red[4][kSmallT];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int tt = 0; tt < kSmallT; ++tt) {
+    const float v = wave_sum(acc[tt]);
+    if (lane == 0) red[wave][tt] = v;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < nt) {
+    const int tt = threadIdx.x;
+    const float v = (red[0][tt] + red[1][tt]) + (red[2][tt] + red[3][tt]);
+    if (r < E) logits[(int64_t)(t0 + tt) * E + r] = v + (bias ? bias[r] : 0.f);
+    else gate_logit[t0 + tt] = v;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_router_small_t_bf16(const uint16_t* x, const uint16_t* wr, const float* bias, const uint16_t* gate,
+                                      int T, int H, int E, float* logits, float* gate_logit, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((unsigned)(E + (gate ? 1 : 0)), (unsigned)((T + kSmallT - 1) / kSmallT));
+  profile_begin("router_logits_bf16", s);
+  hipLaunchKernelGGL(router_small_t_bf16_kernel, grid, dim3(256), 0, s, x, wr, bias, gate, T, H, E, logits,
+                     gate_logit);
+  profile_end(s);
+  return hipGetLastError();
+}
 
 hipError_t launch_router_logits_f32(const float* x, const float* wr, const float* bias, const float* gate,
                                     int T, int H, int E, float* logits, float* gate_logit, hipStream_t s) {

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     for code, text in [(0, b"MOE_OK"), (1, b"MOE_ERR_INVALID_ARG"), (2, b"MOE_ERR_UNSUPPORTED"),
                        (3, b"MOE_ERR_WORKSPACE"), (4, b"MOE_ERR_HIP")]:
         assert lib.moe_status_string(code) == text
@@ -99,11 +99,32 @@ def test_grouped_ffn_validation(lib):
     assert ffn(lib, I=96) == UNSUP
     assert ffn(lib, off=NULL) == INVALID and "expert_offsets" in last(lib)
     assert ffn(lib, gather=NULL) == INVALID and "packed_token_indices" in last(lib)
-    need = lib.moe_grouped_ffn_workspace_size(4, 2, 8, 64, BF16)
-    # 256 bytes of tile counters, then h [P, I] bf16 rounded up to 256 bytes
+    need = lib.moe_grouped_ffn_workspace_size(4, 64, 2, 8, 64, BF16)
+    # 256 bytes of tile counters, then h [P, I] bf16 rounded up to 256 bytes;
+    # K loops of one stage are never split, so no partial sums
     assert need == 256 + 4 * 2 * 64 * 2 + (256 - (4 * 2 * 64 * 2) % 256) % 256
     assert ffn(lib, wsb=need - 1) == WS
     assert ffn(lib, T=0) == OK
+
+
+def test_grouped_ffn_workspace_with_split_k(lib):
+    # Qwen1.5-MoE decode shape: 64 rows over 60 experts.  Tile upper bounds:
+    # gate/up (4 + 60) * 11 = 704 and down (4 + 60) * 8 = 512 tiles, both at
+    # least the split target of 256: no split, no partial sums.
+    h = 64 * 1408 * 2
+    assert lib.moe_grouped_ffn_workspace_size(16, 2048, 4, 60, 1408, BF16) == 256 + h
+    # its shared expert (one ungrouped block of 16 rows, I = 5632): gate/up
+    # 1 * 44 tiles, K = 2048 (32 stages) -> ceil(256 / 44) = 6, at most 32 / 8 = 4
+    # chunks of 8 stages; down 1 * 8 tiles, K = 5632 (88 stages) -> 32, at most
+    # 11 chunks of 8 stages.  Partial sums: max(4 * 16 * 2 * 5632, 11 * 16 * 2048).
+    need = lib.moe_grouped_ffn_workspace_size(16, 2048, 1, 1, 5632, BF16)
+    hs = 16 * 5632 * 2
+    assert need == 256 + hs + max(4 * 16 * 2 * 5632, 11 * 16 * 2048) * 4
+    # the f32 path never splits
+    assert lib.moe_grouped_ffn_workspace_size(16, 2048, 4, 60, 1408, F32) == 256 + 64 * 1408 * 4
+    # forward workspace grows by the larger of the routed and shared split scratch
+    base = lib.moe_forward_workspace_size(16, 2048, 60, 4, 1408, 5632, BF16)
+    assert base > 0
 
 
 def test_grouped_ffn_valid_f32_shape_is_not_rejected_for_size(lib):

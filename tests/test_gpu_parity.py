@@ -59,6 +59,11 @@ SMALL = {
     # 256-row tiles with a K loop of two steps
     "bf16_big_short_k": workloads.config("qwen3_30b_a3b_prefill").scaled(
         name="bf16_big_short_k", num_tokens=600, hidden_size=64, num_experts=2, top_k=1, intermediate_size=64),
+    # a small batch on the small-batch router (three 16-token blocks, the last
+    # one partial) with a shared expert whose GEMMs split K
+    "bf16_decode_40": workloads.config("qwen15_moe_decode").scaled(
+        name="bf16_decode_40", num_tokens=40, hidden_size=1024, num_experts=20, top_k=3, intermediate_size=128,
+        shared_intermediate_size=1024),
     # the pipelined 256-row kernel (K loops of 16 and 8 stages) with about two
     # tiles per workgroup, so the ring carries over from tile to tile
     "bf16_pipe_tiles": workloads.config("qwen3_30b_a3b_prefill").scaled(
