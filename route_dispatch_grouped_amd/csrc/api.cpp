@@ -121,7 +121,8 @@ struct ForwardLayout {
   void* hs;
   float* ys;
   int* counters;  // tile counters of the four grouped GEMMs (routed, shared)
-  float* partial;  // split-K partial sums, shared by the grouped GEMMs (they run in order)
+  float* partial;         // split-K partial sums of the routed GEMMs (they run in order)
+  float* partial_shared;  // same for the shared expert, which may run concurrently
   size_t bytes;
 };
 
@@ -132,12 +133,6 @@ size_t ffn_pair_partial_bytes(int64_t P, int64_t H, int64_t E, bool grouped, int
                   moe::grouped_gemm_partial_bytes(P, E, grouped, H, I, moe::EPI_F32));
 }
 
-// Split-K scratch of the forward: routed experts and the shared expert.
-size_t ffn_partial_bytes(int64_t T, int64_t H, int64_t E, int64_t k, int64_t I, int64_t Is, int dtype) {
-  size_t b = ffn_pair_partial_bytes(T * k, H, E, true, I, dtype);
-  if (Is > 0) b = std::max(b, ffn_pair_partial_bytes(T, H, 1, false, Is, dtype));
-  return b;
-}
 
 ForwardLayout carve_forward(void* ws, int64_t T, int64_t H, int64_t E, int64_t k, int64_t I, int64_t Is, int dtype) {
   const int64_t P = T * k;
@@ -158,7 +153,8 @@ ForwardLayout carve_forward(void* ws, int64_t T, int64_t H, int64_t E, int64_t k
   L.hs = c.take<char>((size_t)(Is > 0 ? T * Is : 0) * dtype_size(dtype));
   L.ys = c.take<float>((size_t)(Is > 0 ? T * H : 0));
   L.counters = c.take<int>(4 * moe::kTileCounterInts);
-  L.partial = c.take<float>(ffn_partial_bytes(T, H, E, k, I, Is, dtype) / sizeof(float));
+  L.partial = c.take<float>(ffn_pair_partial_bytes(P, H, E, true, I, dtype) / sizeof(float));
+  L.partial_shared = c.take<float>((Is > 0 ? ffn_pair_partial_bytes(T, H, 1, false, Is, dtype) : 0) / sizeof(float));
   L.bytes = c.off;
   return L;
 }
@@ -255,6 +251,35 @@ struct ProfRecord {
   hipEvent_t start;
   hipEvent_t stop;
 };
+// Second stream for the shared expert, which depends only on the input and
+// runs concurrently with the routed experts: created once per device on first
+// use, default priority, joined back through events (a pattern that HIP graph
+// capture records as a fork and a join).
+struct AuxStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr;
+  hipEvent_t join = nullptr;
+  bool ok = false;
+  bool tried = false;
+};
+std::mutex g_aux_mu;
+AuxStream g_aux[64];
+
+// Returns the device's aux stream (with g_aux_mu held by the caller), or
+// nullptr when it cannot be created: the caller then stays on one stream.
+AuxStream* aux_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  AuxStream& a = g_aux[dev];
+  if (!a.tried) {
+    a.tried = true;
+    a.ok = hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking) == hipSuccess &&
+           hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&a.join, hipEventDisableTiming) == hipSuccess;
+  }
+  return a.ok ? &a : nullptr;
+}
+
 std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<ProfRecord> g_prof;
@@ -520,14 +545,37 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
   e = moe::launch_dispatch(ids, nullptr, T, k, E, L.counts, L.offsets, L.perm, L.inv, L.packed_ids, nullptr,
                            L.dispatch_scratch, s, L.counters, 4 * moe::kTileCounterInts);
   if (e != hipSuccess) return hip_status(e, "moe_forward(dispatch)");
+  // shared expert on the aux stream (forked after the dispatch, which zeroes
+  // its tile counters), routed experts on the caller's stream, join before
+  // the combine
+  std::unique_lock<std::mutex> aux_lock(g_aux_mu, std::defer_lock);
+  AuxStream* aux = nullptr;
   if (Is) {
-    e = run_ffn(hidden_states, nullptr, nullptr, shared_w13, shared_w2, T, T, H, 1, (int)Is, dtype, L.hs, L.ys, s,
-                true, L.counters + 2 * moe::kTileCounterInts, L.partial);
+    aux_lock.lock();
+    aux = aux_stream();
+    hipStream_t ss = s;
+    if (aux != nullptr) {
+      e = hipEventRecord(aux->fork, s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(aux->stream, aux->fork, 0);
+      if (e != hipSuccess) return hip_status(e, "moe_forward(fork)");
+      ss = aux->stream;
+    }
+    e = run_ffn(hidden_states, nullptr, nullptr, shared_w13, shared_w2, T, T, H, 1, (int)Is, dtype, L.hs, L.ys, ss,
+                true, L.counters + 2 * moe::kTileCounterInts, L.partial_shared);
     if (e != hipSuccess) return hip_status(e, "moe_forward(shared expert)");
+    if (aux != nullptr) {
+      e = hipEventRecord(aux->join, aux->stream);
+      if (e != hipSuccess) return hip_status(e, "moe_forward(join)");
+    }
   }
   e = run_ffn(hidden_states, L.packed_ids, L.offsets, w13, w2, T, P, H, E, I, dtype, L.h, L.y, s, false,
               L.counters, L.partial);
   if (e != hipSuccess) return hip_status(e, "moe_forward(experts)");
+  if (aux != nullptr) {
+    e = hipStreamWaitEvent(s, aux->join, 0);
+    if (e != hipSuccess) return hip_status(e, "moe_forward(join)");
+  }
+  if (aux_lock.owns_lock()) aux_lock.unlock();
   e = moe::launch_combine(L.y, L.inv, weights, Is ? L.ys : nullptr, Is ? L.gate_logit : nullptr, T, H, k,
                           out_dtype == MOE_DTYPE_BF16, output, s);
   return hip_status(e, "moe_forward(combine)");

@@ -4,8 +4,9 @@
 // packed routing weights; metrale ep_dispatch.rs: assignments a = t*k + j are
 // kept in the order given]
 //
-// The P = T*k assignments are cut into segments of 256 consecutive indices, one
-// wavefront per segment.
+// For P <= kDispatchSmallP one workgroup does all of it in LDS
+// (dispatch_small_kernel).  Otherwise the P = T*k assignments are cut into
+// segments of 256 consecutive indices, one wavefront per segment.
 //   1. hist    each wave counts its segment per expert in LDS and writes
 //              cnt[e][u] (expert-major, U = number of segments).
 //   2. scan    one workgroup: per expert, an exclusive scan of cnt[e][0..U)
@@ -164,6 +165,92 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   }
 }
 
+// Whole plan in one workgroup for P <= kDispatchSmallP (decode batches):
+// the same three steps as above with the 16 waves as the segments and every
+// intermediate in LDS.  Wave w owns the contiguous chunk [w*C, (w+1)*C) of
+// the assignments, C = ceil(P / 16).
+constexpr int kSmallWaves = 16;
+
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __restrict__ ids,
+                                                              const float* __restrict__ wts, int P, int k, int E,
+                                                              int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                                              int32_t* __restrict__ packed_ids,
+                                                              float* __restrict__ packed_w, int* zero_ints,
+                                                              int n_zero) {
+  __shared__ int cnt[kSmallWaves][kMaxE];  // per-wave counts, then per-wave running positions
+  __shared__ int wsum[kSmallWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  if (zero_ints != nullptr && tid < n_zero) zero_ints[tid] = 0;
+  for (int i = tid; i < kSmallWaves * kMaxE; i += 1024) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  const int C = (P + kSmallWaves - 1) / kSmallWaves;
+  const int a0 = w * C;
+  const int a1 = min(P, a0 + C);
+  for (int a = a0 + lane; a < a1; a += 64) {
+    const int e = ids[a];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[w][e], 1);  // ids outside [0, E) are a caller error
+  }
+  __syncthreads();
+  // per expert: running sum over the waves (cnt[w][e] <- count of waves < w)
+  // and the total; then an exclusive scan of the totals over the experts
+  int tot = 0;
+  if (tid < E) {
+#pragma unroll
+    for (int q = 0; q < kSmallWaves; ++q) {
+      const int c = cnt[q][tid];
+      cnt[q][tid] = tot;
+      tot += c;
+    }
+  }
+  const int incl = wave_incl_scan(tot, lane);
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int q = 0; q < w; ++q) base += wsum[q];
+  if (tid < E) {
+    const int off = base + incl - tot;
+    counts[tid] = tot;
+    offsets[tid] = off;
+#pragma unroll
+    for (int q = 0; q < kSmallWaves; ++q) cnt[q][tid] += off;
+  }
+  if (tid == 0) offsets[E] = P;
+  __syncthreads();
+  // stable placement, 64 assignments at a time in index order
+  const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  for (int r0 = a0; r0 < a1; r0 += 64) {
+    const int a = r0 + lane;
+    const bool valid = a < a1 && (unsigned)ids[a] < (unsigned)E;
+    const int my = valid ? ids[a] : -1;
+    uint64_t todo = __ballot(valid);
+    uint64_t peers = 0;
+    while (todo) {
+      const int leader = __builtin_ctzll(todo);
+      const int lid = __builtin_amdgcn_readlane(my, leader);
+      const uint64_t m = __ballot(my == lid);
+      if (my == lid) peers = m;
+      todo &= ~m;
+    }
+    int pos = 0;
+    if (valid) pos = cnt[w][my] + __popcll(peers & lt_mask);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    if (valid && lane == __builtin_ctzll(peers)) cnt[w][my] += __popcll(peers);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      perm[pos] = a;
+      inv[a] = pos;
+      packed_ids[pos] = a / k;
+      if (packed_w != nullptr) packed_w[pos] = wts[a];
+    }
+  }
+}
+
 }  // namespace
 
 size_t dispatch_scratch_bytes(int64_t P, int64_t E) {
@@ -176,6 +263,13 @@ hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int
                            void* scratch, hipStream_t s, int* zero_ints, int n_zero) {
   const int P = T * k;
   if (P == 0) return hipSuccess;
+  if (P <= kDispatchSmallP) {
+    profile_begin("dispatch_small", s);
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, s, ids, w, P, k, E, counts, offsets, perm, inv,
+                       packed_ids, packed_w, zero_ints, n_zero);
+    profile_end(s);
+    return hipGetLastError();
+  }
   const int U = (P + kSeg - 1) / kSeg;
   int32_t* cnt = reinterpret_cast<int32_t*>(scratch);
   int32_t* base = cnt + (int64_t)U * E;

@@ -85,6 +85,7 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int renormalize
 
 // ---------------------------------------------------------------- dispatch
 constexpr int kDispatchSegment = 256;  // assignments per wave-segment
+constexpr int kDispatchSmallP = 4096;  // up to this many assignments: one workgroup, all in LDS
 size_t dispatch_scratch_bytes(int64_t P, int64_t E);
 hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int E,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,

@@ -221,6 +221,10 @@ def test_dispatch_edge_cases():
     # ragged P around the 256-assignment segments and 64-lane rounds
     for T in (31, 32, 33, 255, 257, 4097):
         cases.append((np.stack([rng.choice(128, 8, replace=False) for _ in range(T)]), 128))
+    # both sides of the one-workgroup plan (P <= 4096), and a P that leaves
+    # some of its 16 wave chunks empty
+    for T in (4096, 4097, 17):
+        cases.append((rng.integers(0, 7, size=(T, 1)), 7))
     for ids, E in cases:
         ids = ids.astype(np.int32)
         w = rng.random(ids.shape).astype(np.float32)
