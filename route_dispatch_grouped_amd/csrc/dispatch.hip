@@ -9,12 +9,12 @@
 // segments of 256 consecutive indices, one wavefront per segment.
 //   1. hist    each wave counts its segment per expert in LDS and writes
 //              cnt[e][u] (expert-major, U = number of segments).
-//   2. scan    one workgroup: per expert, an exclusive scan of cnt[e][0..U)
-//              into base[e][u] (all loads of a lane issued before any store);
-//              totals -> counts; an exclusive scan over experts -> offsets
-//              (offsets[E] = P).
-//   3. scatter each wave stages offsets[e] + base[e][u] for every expert in
-//              LDS, then re-reads its segment 64 assignments at a time, in
+//   2. scan    one wave per expert: an exclusive scan of cnt[e][0..U) into
+//              base[e][u]; the total -> counts[e].
+//   3. scatter every workgroup scans the expert totals into offsets (the first
+//              one writes them out, offsets[E] = P); each wave stages
+//              offsets[e] + base[e][u] for every expert in LDS, then re-reads
+//              its segment 64 assignments at a time, in
 //              index order.  Lanes holding the same expert id find each other
 //              with ballots; a lane's rank among them plus the wave's running
 //              count for that expert plus the staged base is the assignment's
@@ -61,77 +61,84 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-// Single workgroup of 1024 threads (16 waves); VPL consecutive segments per lane.
-// Also zeroes `zero_ints` (the tile counters of the grouped GEMMs that follow).
+// One wave per expert (4 per workgroup): exclusive scan of cnt[e][0..U) into
+// base[e][u] (VPL consecutive segments per lane, all loads of a lane issued
+// before any store) and the expert total into counts[e].  Workgroup 0 also
+// zeroes `zero_ints` (the tile counters of the grouped GEMMs that follow).
 template <int VPL>
-__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ cnt,
-                                                             int32_t* __restrict__ base, int U, int E, int P,
-                                                             int32_t* __restrict__ counts,
-                                                             int32_t* __restrict__ offsets, int* zero_ints,
-                                                             int n_zero) {
-  __shared__ int tot[kMaxE];
-  __shared__ int wsum[16];
-  if (zero_ints != nullptr && (int)threadIdx.x < n_zero) zero_ints[threadIdx.x] = 0;
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* __restrict__ cnt,
+                                                            int32_t* __restrict__ base, int U, int E,
+                                                            int32_t* __restrict__ counts, int* zero_ints,
+                                                            int n_zero) {
+  if (zero_ints != nullptr && blockIdx.x == 0 && (int)threadIdx.x < n_zero) zero_ints[threadIdx.x] = 0;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  for (int e = w; e < E; e += 16) {
-    const int32_t* src = cnt + (int64_t)e * U;
-    int32_t* dst = base + (int64_t)e * U;
-    int carry = 0;
-    for (int u0 = 0; u0 < U; u0 += 64 * VPL) {
-      int v[VPL];
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  const int32_t* src = cnt + (int64_t)e * U;
+  int32_t* dst = base + (int64_t)e * U;
+  int carry = 0;
+  for (int u0 = 0; u0 < U; u0 += 64 * VPL) {
+    int v[VPL];
 #pragma unroll
-      for (int i = 0; i < VPL; ++i) {
-        const int u = u0 + lane * VPL + i;
-        v[i] = (u < U) ? src[u] : 0;
-      }
-      int s = 0;
-#pragma unroll
-      for (int i = 0; i < VPL; ++i) s += v[i];
-      const int incl = wave_incl_scan(s, lane);
-      int run = carry + incl - s;
-#pragma unroll
-      for (int i = 0; i < VPL; ++i) {
-        const int u = u0 + lane * VPL + i;
-        if (u < U) dst[u] = run;
-        run += v[i];
-      }
-      carry += __shfl(incl, 63, 64);
+    for (int i = 0; i < VPL; ++i) {
+      const int u = u0 + lane * VPL + i;
+      v[i] = (u < U) ? src[u] : 0;
     }
-    if (lane == 0) tot[e] = carry;
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) sum += v[i];
+    const int incl = wave_incl_scan(sum, lane);
+    int run = carry + incl - sum;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int u = u0 + lane * VPL + i;
+      if (u < U) dst[u] = run;
+      run += v[i];
+    }
+    carry += __shfl(incl, 63, 64);
   }
-  __syncthreads();
-  // exclusive scan of tot over experts (E <= 512 <= 1024 threads)
-  const int i = threadIdx.x;
-  const int v = (i < E) ? tot[i] : 0;
-  const int incl = wave_incl_scan(v, lane);
-  if (lane == 63) wsum[w] = incl;
-  __syncthreads();
-  int b = 0;
-  for (int q = 0; q < w; ++q) b += wsum[q];
-  if (i < E) {
-    counts[i] = v;
-    offsets[i] = b + incl - v;
-  }
-  if (i == 0) offsets[E] = P;
+  if (lane == 0) counts[e] = carry;
 }
 
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ wts, int P, int k, int E, int U,
-    const int32_t* __restrict__ base, const int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv, int32_t* __restrict__ packed_ids, float* __restrict__ packed_w) {
+    const int32_t* __restrict__ base, const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ packed_ids,
+    float* __restrict__ packed_w) {
   __shared__ int pos0[4][kMaxE];  // offsets[e] + base[e][u], advanced as the wave places assignments
+  __shared__ int off[kMaxE];      // expert offsets: exclusive scan of counts
+  __shared__ int wsum[4];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int u = blockIdx.x * 4 + w;
-  if (u >= U) return;  // no workgroup barrier below: the waves are independent
   int id[kSeg / 64];
 #pragma unroll
   for (int r = 0; r < kSeg / 64; ++r) {
     const int a = u * kSeg + r * 64 + lane;
-    id[r] = (a < P) ? ids[a] : -1;
+    id[r] = (u < U && a < P) ? ids[a] : -1;
   }
-  for (int e = lane; e < E; e += 64) pos0[w][e] = offsets[e] + base[(int64_t)e * U + u];
+  // every workgroup scans the E <= 512 expert totals itself (two per thread)
+  {
+    const int e0 = 2 * threadIdx.x, e1 = e0 + 1;
+    const int c0 = (e0 < E) ? counts[e0] : 0;
+    const int c1 = (e1 < E) ? counts[e1] : 0;
+    const int incl = wave_incl_scan(c0 + c1, lane);
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    int b = 0;
+    for (int q = 0; q < w; ++q) b += wsum[q];
+    const int ex = b + incl - (c0 + c1);
+    if (e0 < E) off[e0] = ex;
+    if (e1 < E) off[e1] = ex + c0;
+    if (blockIdx.x == 0) {
+      if (e0 < E) offsets[e0] = ex;
+      if (e1 < E) offsets[e1] = ex + c0;
+      if (threadIdx.x == 0) offsets[E] = P;
+    }
+    __syncthreads();
+  }
+  if (u >= U) return;  // no workgroup barrier below: the waves are independent
+  for (int e = lane; e < E; e += 64) pos0[w][e] = off[e] + base[(int64_t)e * U + u];
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes land before its reads below
   __builtin_amdgcn_wave_barrier();
   const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
@@ -278,19 +285,18 @@ hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int
   hipLaunchKernelGGL(dispatch_hist_kernel, dim3(blocks), dim3(256), 0, s, ids, P, E, U, cnt);
   profile_end(s);
   profile_begin("dispatch_scan", s);
+  const dim3 sgrid((unsigned)((E + 3) / 4));
   if (U <= 64)
-    hipLaunchKernelGGL(dispatch_scan_kernel<1>, dim3(1), dim3(1024), 0, s, cnt, base, U, E, P, counts, offsets,
-                       zero_ints, n_zero);
+    hipLaunchKernelGGL(dispatch_scan_kernel<1>, sgrid, dim3(256), 0, s, cnt, base, U, E, counts, zero_ints, n_zero);
   else if (U <= 256)
-    hipLaunchKernelGGL(dispatch_scan_kernel<4>, dim3(1), dim3(1024), 0, s, cnt, base, U, E, P, counts, offsets,
-                       zero_ints, n_zero);
+    hipLaunchKernelGGL(dispatch_scan_kernel<4>, sgrid, dim3(256), 0, s, cnt, base, U, E, counts, zero_ints, n_zero);
   else
-    hipLaunchKernelGGL(dispatch_scan_kernel<16>, dim3(1), dim3(1024), 0, s, cnt, base, U, E, P, counts, offsets,
-                       zero_ints, n_zero);
+    hipLaunchKernelGGL(dispatch_scan_kernel<16>, sgrid, dim3(256), 0, s, cnt, base, U, E, counts, zero_ints,
+                       n_zero);
   profile_end(s);
   profile_begin("dispatch_scatter", s);
-  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(blocks), dim3(256), 0, s, ids, w, P, k, E, U, base, offsets,
-                     perm, inv, packed_ids, packed_w);
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(blocks), dim3(256), 0, s, ids, w, P, k, E, U, base, counts,
+                     offsets, perm, inv, packed_ids, packed_w);
   profile_end(s);
   return hipGetLastError();
 }
