@@ -348,14 +348,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
       const int q = qi * 4 + wave;
       const int r = q * 8 + (lane >> 3);  // B tile row
       const int c = (lane & 7) ^ (r & 7);
-      int wr;
-      if (EPI == EPI_SWIGLU) {
-        const int col = min(n0 + (r & 127), p.N - 1);
-        wr = (r < 128) ? col : p.up_row0 + col;
-      } else {
-        wr = min(n0 + r, p.N - 1);
-      }
-      d.b_off[qi] = (uint32_t)wr * row_bytes + (uint32_t)c * 16u;
+      // weight rows past N (a ragged last column block, or experts past E in
+      // the router) fetch through an offset past the buffer: zeros, no traffic
+      const int col = (EPI == EPI_SWIGLU) ? n0 + (r & 127) : n0 + r;
+      const int wr = (EPI == EPI_SWIGLU && r >= 128) ? p.up_row0 + col : col;
+      d.b_off[qi] = (col < p.N) ? (uint32_t)wr * row_bytes + (uint32_t)c * 16u : 0x80000000u;
     }
     const u32x4_t ra = make_rsrc(p.A, (uint32_t)p.a_rows * row_bytes);
     const int b_rows_total = (EPI == EPI_SWIGLU) ? 2 * p.up_row0 : p.N;

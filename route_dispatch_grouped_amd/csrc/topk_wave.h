@@ -1,0 +1,158 @@
+// Wave-level routing primitives shared by the router kernels: an
+// order-preserving float key, DPP wave reductions, and the top-k / softmax /
+// renormalisation of one token's logits by one wavefront.
+// [DWDP README "Router Module": routing probabilities, top-k expert indices,
+//  normalized routing weights; diffulex.moe "diffulex.moe.topk"]
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Order-preserving map float -> uint32 (larger float -> larger key), after
+// -0.0 has been folded onto +0.0.  NaN is not a supported input.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  if (f == 0.f) f = 0.f;
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float order_value(uint32_t o) {
+  const uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+
+// One step of a max-reduction through a DPP lane permutation (within 16-lane rows).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+  const int hi = (int)(v >> 32), lo = (int)(v & 0xFFFFFFFFu);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > v ? o : v;
+}
+
+// Wave-wide maximum of a 64-bit key, returned wave-uniform: DPP exchanges
+// (xor 1, xor 2, half-row mirror, row mirror) leave every lane of a 16-lane
+// row holding the row maximum; the four row maxima are then read out with
+// readlane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_step<0xB1>(v);   // quad_perm(1,0,3,2)
+  v = dpp_max_step<0x4E>(v);   // quad_perm(2,3,0,1)
+  v = dpp_max_step<0x141>(v);  // row_half_mirror
+  v = dpp_max_step<0x140>(v);  // row_mirror
+  uint64_t best = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), 16 * r);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(v & 0xFFFFFFFFu), 16 * r);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    best = o > best ? o : best;
+  }
+  return best;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add_step(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF,
+                                                         false));
+}
+
+// Wave-wide float sum, wave-uniform (same exchange pattern as wave_max_u64).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_add_step<0xB1>(v);
+  v = dpp_add_step<0x4E>(v);
+  v = dpp_add_step<0x141>(v);
+  v = dpp_add_step<0x140>(v);
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+  return s;
+}
+
+// One wavefront selects the top-k of one token's logits row[0..E) (global or
+// LDS memory) and writes ids[0..k), weights[0..k) and, when probs != NULL, the
+// full softmax probs[0..E).  Lane l holds experts l, l+64, ... (VPL >= E/64).
+// k rounds of a wave-wide max over the 64-bit key (order key << 32 | ~id): the
+// larger logit wins, and on equal logits the lower expert id has the larger
+// ~id and wins.  Winner j is kept by lane j % 64 in slot j / 64.  Weights:
+// exp(l_j - l_max) over the sum of the selected terms (renormalised) or over
+// all E terms (the plain softmax probability).
+template <int VPL>
+__device__ __forceinline__ void topk_row(const float* row, int E, int k, int renorm, int32_t* __restrict__ ids,
+                                         float* __restrict__ weights, float* __restrict__ probs, int lane) {
+  float v[VPL];
+  uint32_t key[VPL];
+  uint32_t avail = 0;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) {
+      v[i] = row[e];
+      key[i] = order_key(v[i]);
+      avail |= 1u << i;
+    } else {
+      v[i] = -INFINITY;
+      key[i] = 0;
+    }
+  }
+
+  int my_id[VPL];
+  float my_val[VPL];
+#pragma unroll
+  for (int c = 0; c < VPL; ++c) {
+    my_id[c] = 0;
+    my_val[c] = 0.f;
+    const int jn = min(64, k - 64 * c);
+    for (int jj = 0; jj < jn; ++jj) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        if ((avail >> i) & 1u) {
+          const uint64_t kk = ((uint64_t)key[i] << 32) | (uint32_t)(~(uint32_t)(lane + 64 * i));
+          best = kk > best ? kk : best;
+        }
+      }
+      best = wave_max_u64(best);
+      const int id = (int)(~(uint32_t)(best & 0xFFFFFFFFu));
+      if ((id & 63) == lane) avail &= ~(1u << (id >> 6));
+      if (jj == lane) {
+        my_id[c] = id;
+        my_val[c] = order_value((uint32_t)(best >> 32));
+      }
+    }
+  }
+
+  const float m = __shfl(my_val[0], 0, 64);  // largest logit
+  float s_sel = 0.f, s_all = 0.f;
+#pragma unroll
+  for (int c = 0; c < VPL; ++c)
+    if (64 * c + lane < k) s_sel += expf(my_val[c] - m);
+  s_sel = wave_sum(s_sel);
+  if (!renorm || probs != nullptr) {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (lane + 64 * i < E) s_all += expf(v[i] - m);
+    s_all = wave_sum(s_all);
+  }
+  const float denom = renorm ? s_sel : s_all;
+#pragma unroll
+  for (int c = 0; c < VPL; ++c) {
+    const int j = 64 * c + lane;
+    if (j < k) {
+      ids[j] = my_id[c];
+      weights[j] = expf(my_val[c] - m) / denom;
+    }
+  }
+  if (probs != nullptr) {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) probs[e] = expf(v[i] - m) / s_all;
+    }
+  }
+}
+
+}  // namespace moe

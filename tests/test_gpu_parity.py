@@ -237,9 +237,12 @@ def test_dispatch_edge_cases():
             assert torch.equal(g[key], g_again[key])
 
 
-def test_router_ties_and_special_logits():
-    # all-zero input -> all logits 0 -> experts 0..k-1, equal weights
-    cfg = workloads.config("qwen3_30b_a3b_prefill").scaled(num_tokens=40, hidden_size=64, num_experts=128, top_k=8)
+@pytest.mark.parametrize("T", [40, 100])
+def test_router_ties_and_special_logits(T):
+    # T = 40: small-batch router + top-k kernel; T = 100: router GEMM with the
+    # top-k in its epilogue.  All-zero input -> all logits 0 -> experts
+    # 0..k-1, equal weights
+    cfg = workloads.config("qwen3_30b_a3b_prefill").scaled(num_tokens=T, hidden_size=64, num_experts=128, top_k=8)
     inp = workloads.generate(cfg, seed=2)
     inp["x"][:] = 0
     inp["x"][5:10] = workloads.round_to_bf16_bits(-0.0 * np.ones((5, 64), np.float32))  # -0.0 inputs
@@ -258,7 +261,7 @@ def test_router_ties_and_special_logits():
     assert (Lg[:, 77] == Lg[:, 12]).all()
     ids = r["topk_ids"].cpu().numpy()
     assert (ids == oracle.select_topk(Lg.astype(np.float64), 8)).all()
-    for t in range(40):
+    for t in range(T):
         row = list(ids[t])
         if 77 in row:
             assert 12 in row and row.index(12) < row.index(77)
