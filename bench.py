@@ -248,6 +248,30 @@ def main():
         kernels = rdg.profile_collect()
         log("[bench] per-kernel: " + ", ".join(f"{n} {ms / c * 1e3:.1f}us" for n, (ms, c) in kernels.items()))
 
+    # expert-parallel routing table of this batch's routing, as rank 2 of 8
+    # (experts [E/4, 3E/8)): outside the layer step, timed on its own
+    ep = None
+    if not args.no_profile:
+        E = cfg.num_experts
+        lo, hi = E * 2 // 8, E * 3 // 8
+        ids_flat, w_flat = r["topk_ids"].reshape(-1), r["topk_weights"].reshape(-1)
+        for _ in range(3):
+            rdg.moe_ep_routing_table(ids_flat, w_flat, cfg.num_tokens, cfg.top_k, lo, hi, trim=False)
+        torch.cuda.synchronize()
+        rdg.profile_enable(True)
+        for _ in range(args.steps):
+            rdg.moe_ep_routing_table(ids_flat, w_flat, cfg.num_tokens, cfg.top_k, lo, hi, trim=False)
+        torch.cuda.synchronize()
+        rdg.profile_enable(False)
+        ms, c = rdg.profile_collect()["ep_routing_table"]
+        P = cfg.num_tokens * cfg.top_k
+        nbytes = P * 8 + P * 12 + 8  # ids + weights read; (token, expert, weight) written; counts
+        avg_s = ms / c / 1e3
+        ep = {"avg_us": round(avg_s * 1e6, 2), "local_range": [lo, hi], "algorithmic_bytes": nbytes,
+              "achieved": round(nbytes / avg_s / 1e9, 1), "unit": "GB/s",
+              "frac": round(nbytes / avg_s / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"[bench] ep routing table: {ep['avg_us']} us ({ep['achieved']} GB/s)")
+
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
         src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -309,6 +333,7 @@ def main():
         "roofline": roof,
         "grouped_ffn": ffn,
         "kernels": per_kernel,
+        "ep_routing_table": ep,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

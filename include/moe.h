@@ -140,6 +140,39 @@ moe_status moe_dispatch_plan(const int32_t* topk_ids, const float* topk_weights,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Expert-parallel routing table: the assignments split into this rank's
+ * experts and the rest.
+ * [metrale_model_layers ep_dispatch.rs: build_ep_routing_table,
+ *  EpRoutingTable; its tests print the expected tables]
+ *
+ * Assignment a = t*k + j of the row-major [T,k] gate arrays is local when
+ * local_expert_start <= gate_indices[a] < local_expert_end, the ids compared
+ * as unsigned 32-bit values (the page's expert ids are u32; a negative int32
+ * is a large id and therefore remote).  Each bucket lists its entries in
+ * assignment order; entry i is the triple
+ *   (*_token_indices[i] = a / k, *_expert_ids[i] = gate_indices[a] (global,
+ *    not rank-relative), *_weights[i] = gate_weights[a]).
+ * counts[0] = local entries, counts[1] = remote entries; their sum is T*k.
+ *
+ * gate_indices [gate_indices_len] int32, gate_weights [gate_weights_len] f32;
+ * each of the six outputs must hold T*k entries (device, caller-owned; only
+ * the first counts[0] / counts[1] are written); counts [2] int32 device.
+ * Errors: INVALID_ARG "gate_indices length mismatch" /
+ * "gate_weights length mismatch" when a length is not num_tokens * top_k
+ * (the page's function panics with these texts), NULL pointers, negative
+ * range bounds, top_k < 1; WORKSPACE.  num_tokens == 0 writes counts = {0, 0}.
+ * Deterministic (prefix sums, no atomics).
+ * workspace: moe_ep_routing_table_workspace_size(T, k) bytes of device memory.
+ */
+size_t moe_ep_routing_table_workspace_size(int64_t num_tokens, int64_t top_k);
+moe_status moe_ep_routing_table(const int32_t* gate_indices, int64_t gate_indices_len, const float* gate_weights,
+                                int64_t gate_weights_len, int64_t num_tokens, int64_t top_k,
+                                int64_t local_expert_start, int64_t local_expert_end,
+                                int32_t* local_token_indices, int32_t* local_expert_ids, float* local_weights,
+                                int32_t* remote_token_indices, int32_t* remote_expert_ids, float* remote_weights,
+                                int32_t* counts, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Grouped expert SwiGLU FFN over the expert-major layout.
  * [DWDP README "Executor Module": gather token activations per expert range,
  *  run the expert, write packed expert outputs; modelexpress refit test,

@@ -32,6 +32,7 @@ __all__ = [
     "library_loaded",
     "moe_router_topk",
     "moe_dispatch_plan",
+    "moe_ep_routing_table",
     "moe_grouped_ffn",
     "moe_combine",
     "moe_forward",
@@ -59,6 +60,10 @@ _SIGNATURES = {
     "moe_dispatch_workspace_size": (_size, [_i64, _i64, _i64]),
     "moe_dispatch_plan": (_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "moe_ep_routing_table_workspace_size": (_size, [_i64, _i64]),
+    "moe_ep_routing_table": (_int, [_c_void_p, _i64, _c_void_p, _i64, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p,
+                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size,
+                                    _c_void_p]),
     "moe_grouped_ffn_workspace_size": (_size, [_i64, _i64, _i64, _i64, _i64, _int]),
     "moe_grouped_ffn": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64,
                                _i64, _int, _c_void_p, _c_void_p, _size, _c_void_p]),
@@ -211,6 +216,46 @@ def moe_dispatch_plan(topk_ids: torch.Tensor, topk_weights: Optional[torch.Tenso
                                _ptr(out["offsets"]), _ptr(out["perm"]), _ptr(out["inv"]), _ptr(out["packed_ids"]),
                                _ptr(out.get("packed_w")), _ptr(ws), ws.numel(), _stream(stream))
     _check("moe_dispatch_plan", st)
+    return out
+
+
+def moe_ep_routing_table(gate_indices: torch.Tensor, gate_weights: torch.Tensor, num_tokens: int, top_k: int,
+                         local_expert_start: int, local_expert_end: int, trim: bool = True, stream=None):
+    """Local/remote split of the assignments (include/moe.h: moe_ep_routing_table).
+
+    ``gate_indices`` int32 and ``gate_weights`` f32 device tensors are read as
+    flat arrays; their lengths are passed through, so a length other than
+    ``num_tokens * top_k`` raises ``MoeError`` with the page's message.  Returns
+    a dict of the six buckets and ``counts [2]``; with ``trim`` the buckets are
+    cut to their counts (this reads the counts back to the host).
+    """
+    lib = load_library()
+    gi = gate_indices.reshape(-1)
+    gw = gate_weights.reshape(-1)
+    if gi.dtype != torch.int32 or gw.dtype != torch.float32 or not gi.is_cuda or not gw.is_cuda:
+        raise TypeError("gate_indices must be an int32 and gate_weights a float32 device tensor")
+    dev = gi.device
+    P = max(int(num_tokens) * int(top_k), 0)
+    out = {name: torch.empty((P,), dtype=torch.float32 if name.endswith("weights") else torch.int32, device=dev)
+           for name in ("local_token_indices", "local_expert_ids", "local_weights", "remote_token_indices",
+                        "remote_expert_ids", "remote_weights")}
+    out["counts"] = torch.empty((2,), dtype=torch.int32, device=dev)
+    ws_bytes = lib.moe_ep_routing_table_workspace_size(int(num_tokens), int(top_k))
+    ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
+    st = lib.moe_ep_routing_table(_ptr(gi), gi.numel(), _ptr(gw), gw.numel(), int(num_tokens), int(top_k),
+                                  int(local_expert_start), int(local_expert_end), _ptr(out["local_token_indices"]),
+                                  _ptr(out["local_expert_ids"]), _ptr(out["local_weights"]),
+                                  _ptr(out["remote_token_indices"]), _ptr(out["remote_expert_ids"]),
+                                  _ptr(out["remote_weights"]), _ptr(out["counts"]), _ptr(ws), ws.numel(),
+                                  _stream(stream))
+    _check("moe_ep_routing_table", st)
+    if trim:
+        nl, nr = (int(v) for v in out["counts"].cpu().tolist())
+        for name in list(out):
+            if name.startswith("local_"):
+                out[name] = out[name][:nl]
+            elif name.startswith("remote_"):
+                out[name] = out[name][:nr]
     return out
 
 

@@ -394,6 +394,46 @@ moe_status moe_dispatch_plan(const int32_t* topk_ids, const float* topk_weights,
                     "moe_dispatch_plan");
 }
 
+size_t moe_ep_routing_table_workspace_size(int64_t num_tokens, int64_t top_k) {
+  if (num_tokens < 0 || top_k < 1) return 0;
+  return align_up(moe::ep_split_scratch_bytes(num_tokens * top_k)) + kAlign;
+}
+
+moe_status moe_ep_routing_table(const int32_t* gate_indices, int64_t gate_indices_len, const float* gate_weights,
+                                int64_t gate_weights_len, int64_t num_tokens, int64_t top_k,
+                                int64_t local_expert_start, int64_t local_expert_end,
+                                int32_t* local_token_indices, int32_t* local_expert_ids, float* local_weights,
+                                int32_t* remote_token_indices, int32_t* remote_expert_ids, float* remote_weights,
+                                int32_t* counts, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "num_tokens is negative");
+  if (top_k < 1) return fail(MOE_ERR_INVALID_ARG, "top_k must be >= 1");
+  if (num_tokens * top_k >= (int64_t)1 << 31) return fail(MOE_ERR_UNSUPPORTED, "num_tokens * top_k must be < 2^31");
+  if (local_expert_start < 0 || local_expert_end < 0)
+    return fail(MOE_ERR_INVALID_ARG, "local expert range bounds must be >= 0");
+  const int64_t total = num_tokens * top_k;
+  if (gate_indices_len != total) return fail(MOE_ERR_INVALID_ARG, "gate_indices length mismatch");
+  if (gate_weights_len != total) return fail(MOE_ERR_INVALID_ARG, "gate_weights length mismatch");
+  REQUIRE_PTR(counts);
+  if (total > 0) {
+    REQUIRE_PTR(gate_indices);
+    REQUIRE_PTR(gate_weights);
+    REQUIRE_PTR(local_token_indices);
+    REQUIRE_PTR(local_expert_ids);
+    REQUIRE_PTR(local_weights);
+    REQUIRE_PTR(remote_token_indices);
+    REQUIRE_PTR(remote_expert_ids);
+    REQUIRE_PTR(remote_weights);
+  }
+  const size_t need = moe_ep_routing_table_workspace_size(num_tokens, top_k);
+  if (workspace == nullptr || workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(moe::launch_ep_split(gate_indices, gate_weights, (int)num_tokens, (int)top_k, local_expert_start,
+                                         local_expert_end, local_token_indices, local_expert_ids, local_weights,
+                                         remote_token_indices, remote_expert_ids, remote_weights, counts, workspace,
+                                         s),
+                    "moe_ep_routing_table");
+}
+
 // Split-K scratch of moe_grouped_ffn; with one expert the offsets may be
 // absent (one ungrouped block) or present, and the two can split differently.
 size_t grouped_ffn_partial_bytes(int64_t P, int64_t H, int64_t E, int64_t I, int dtype) {

@@ -25,7 +25,7 @@
 namespace moe {
 namespace {
 
-constexpr int kSeg = kDispatchSegment;  // 256 assignments per wave
+constexpr int kSeg = kDispatchSegment;  // assignments per wave
 constexpr int kMaxE = MOE_MAX_GROUPS_INTERNAL;
 
 __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __restrict__ ids, int P, int E, int U,

@@ -83,8 +83,14 @@ hipError_t launch_ffn_down_f32(const float* h, const int32_t* offsets, const flo
 hipError_t launch_topk(const float* logits, int T, int E, int k, int renormalize,
                        int32_t* ids, float* weights, float* probs, hipStream_t s);
 
+// ---------------------------------------------------------------- EP routing table
+size_t ep_split_scratch_bytes(int64_t P);
+hipError_t launch_ep_split(const int32_t* ids, const float* w, int T, int k, int64_t start, int64_t end,
+                           int32_t* l_tok, int32_t* l_eid, float* l_w, int32_t* r_tok, int32_t* r_eid, float* r_w,
+                           int32_t* counts, void* scratch, hipStream_t s);
+
 // ---------------------------------------------------------------- dispatch
-constexpr int kDispatchSegment = 256;  // assignments per wave-segment
+constexpr int kDispatchSegment = 128;  // assignments per wave-segment
 constexpr int kDispatchSmallP = 4096;  // up to this many assignments: one workgroup, all in LDS
 size_t dispatch_scratch_bytes(int64_t P, int64_t E);
 hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int E,

@@ -168,3 +168,20 @@ def test_forward_validation(lib):
 def test_profile_collect_empty(lib):
     lib.moe_profile_enable(0)
     assert rdg.profile_collect() == {}
+
+
+def ep(lib, gi_len=4, gw_len=4, T=2, k=2, start=0, end=256, out=P16, counts=P16, wsb=1 << 20):
+    return lib.moe_ep_routing_table(P16, gi_len, P16, gw_len, T, k, start, end, out, out, out, out, out, out, counts,
+                                    P16, wsb, NULL)
+
+
+def test_ep_routing_table_validation(lib):
+    # the page's panics, as INVALID_ARG with the same texts
+    assert ep(lib, gi_len=3) == INVALID and last(lib) == "gate_indices length mismatch"
+    assert ep(lib, gw_len=5) == INVALID and last(lib) == "gate_weights length mismatch"
+    assert ep(lib, k=0) == INVALID
+    assert ep(lib, start=-1) == INVALID
+    assert ep(lib, counts=NULL) == INVALID and "counts" in last(lib)
+    assert ep(lib, out=NULL) == INVALID
+    need = lib.moe_ep_routing_table_workspace_size(2, 2)
+    assert need > 0 and ep(lib, wsb=need - 1) == WS

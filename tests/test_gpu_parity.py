@@ -353,3 +353,53 @@ def test_combine_shapes(T, H, k):
                             shared_gate_logit=to_device(gl)).cpu().numpy().astype(np.float64)
     err_s, rms_s = rel_max_err(out_s, ref_s)
     assert err_s <= 1e-5 * rms_s + 1e-30
+
+
+def _ep_check(ids, w, T, k, start, end):
+    ref = oracle.ep_routing_table(ids, w, T, k, start, end)
+    g = rdg.moe_ep_routing_table(to_device(np.asarray(ids, dtype=np.int32).reshape(-1)),
+                                 to_device(np.asarray(w, dtype=np.float32).reshape(-1)), T, k, start, end)
+    nl, nr = (int(v) for v in g["counts"].cpu().tolist())
+    assert nl == len(ref["local_token_indices"]) and nr == len(ref["remote_token_indices"])
+    assert nl + nr == T * k
+    for key in ("local_token_indices", "local_expert_ids", "remote_token_indices", "remote_expert_ids"):
+        got = g[key].cpu().numpy().astype(np.int64) & 0xFFFFFFFF  # the page's ids are u32
+        assert (got == ref[key].astype(np.int64)).all(), key
+    for key in ("local_weights", "remote_weights"):
+        assert (g[key].cpu().numpy() == ref[key]).all(), key
+    return g
+
+
+def test_ep_routing_table():
+    """Local/remote split against the oracle (itself pinned by the printed
+    vectors of ep_dispatch.rs); bit-exact, including the page's own cases."""
+    import json
+    import os
+    vec = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "ep_dispatch_vectors.json")))
+    for case in vec["cases"]:
+        log(f"[parity] ep table {case['name']}")
+        _ep_check(case["indices"], case["weights"], case["num_tokens"], case["top_k"], case["start"], case["end"])
+    rng = np.random.default_rng(11)
+    # Qwen3-30B-A3B prefill routing, rank 2 of 8 (experts 32..47), plus ragged
+    # sizes around the 1024-assignment segments
+    for T, k, E, lo, hi in [(8192, 8, 128, 32, 48), (129, 8, 128, 0, 128), (129, 8, 128, 128, 256),
+                            (1000, 3, 64, 40, 40), (1, 1, 4, 0, 2), (513, 2, 512, 500, 1 << 40)]:
+        log(f"[parity] ep table T={T} k={k} E={E} range=[{lo},{hi})")
+        ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+        w = rng.random((T, k)).astype(np.float32)
+        g = _ep_check(ids, w, T, k, lo, hi)
+        g2 = rdg.moe_ep_routing_table(to_device(ids), to_device(w), T, k, lo, hi)
+        for key in g:
+            assert torch.equal(g[key], g2[key])
+    # negative int32 ids are large u32 ids: always remote for a range below 2^31
+    ids = np.array([[-1, 5], [7, -2]], dtype=np.int32)
+    _ep_check(ids.astype(np.int64) & 0xFFFFFFFF, np.ones((2, 2), np.float32), 2, 2, 0, 1 << 31)
+    # no tokens: counts {0, 0}
+    g = rdg.moe_ep_routing_table(torch.empty(0, dtype=torch.int32, device="cuda"),
+                                 torch.empty(0, dtype=torch.float32, device="cuda"), 0, 4, 0, 8)
+    assert g["counts"].cpu().tolist() == [0, 0]
+    # the page's length checks
+    with pytest.raises(rdg.MoeError, match="gate_indices length mismatch"):
+        rdg.moe_ep_routing_table(to_device(np.zeros(5, np.int32)), to_device(np.zeros(6, np.float32)), 3, 2, 0, 1)
+    with pytest.raises(rdg.MoeError, match="gate_weights length mismatch"):
+        rdg.moe_ep_routing_table(to_device(np.zeros(6, np.int32)), to_device(np.zeros(5, np.float32)), 3, 2, 0, 1)
