@@ -75,6 +75,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// silu(g) * u = g * u / (1 + e^-g), with the hardware reciprocal (about 1 ulp)
+// instead of an IEEE division: the result is rounded to bf16 right after.
+// e^-g overflowing to +inf gives exactly 0, the limit of silu at -inf.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
 // [6:4], lgkmcnt [11:8]); issued through the builtin so that the compiler's
 // own wait tracking sees them.
@@ -425,7 +432,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
               if (row < rows) {
                 const float gv = acc[i][jj][r];
                 const float uv = acc[i][jj + 2][r];
-                const float h = gv / (1.0f + __expf(-gv)) * uv;
+                const float h = silu_mul(gv, uv);
                 out[(int64_t)(m0 + row) * p.ldo + col] = f32_to_bf16_rne(h);
               }
             }
@@ -762,7 +769,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_big_kernel(GemmArg
             for (int c = 0; c < 4; ++c) {
               const float gv = acc[i][j][4 * gq + c];
               const float uv = acc[i][j + 2][4 * gq + c];
-              hb[c] = f32_to_bf16_rne(gv / (1.0f + __expf(-gv)) * uv);
+              hb[c] = f32_to_bf16_rne(silu_mul(gv, uv));
             }
             uint2 v;
             v.x = hb[0] | (hb[1] << 16);
@@ -1049,7 +1056,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
             for (int c = 0; c < 4; ++c) {
               const float gv = acc[i][j][4 * gq + c];
               const float uv = acc[i][j + 2][4 * gq + c];
-              hb[c] = f32_to_bf16_rne(gv / (1.0f + __expf(-gv)) * uv);
+              hb[c] = f32_to_bf16_rne(silu_mul(gv, uv));
             }
             typedef int i32x2_t __attribute__((ext_vector_type(2)));
             const i32x2_t v = {(int)(hb[0] | (hb[1] << 16)), (int)(hb[2] | (hb[3] << 16))};
@@ -1105,7 +1112,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     for (int s = 1; s < ksplit; ++s) u += *reinterpret_cast<const f32x4_t*>(src + N + s * plane);
     uint32_t hb[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) hb[c] = f32_to_bf16_rne(a[c] / (1.0f + __expf(-a[c])) * u[c]);
+    for (int c = 0; c < 4; ++c) hb[c] = f32_to_bf16_rne(silu_mul(a[c], u[c]));
     uint2 v;
     v.x = hb[0] | (hb[1] << 16);
     v.y = hb[2] | (hb[3] << 16);
