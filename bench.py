@@ -164,7 +164,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps; the clocks settle after about 15 forwards of this size")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(workloads.CONFIGS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
