@@ -55,18 +55,25 @@ constexpr int kMaxGroups = MOE_MAX_GROUPS_INTERNAL;
 constexpr int kXcds = 8;
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource, 32-bit data
 
-template <int BM>
+// BR weight rows per tile: 256 (EPI_SWIGLU: 128 gate + 128 up), or 128 for
+// narrow outputs (the router of up to 128 experts), which halves the stage
+// and leaves LDS for a deeper ring.
+template <int BM, int BR = kBRows>
 struct Tile {
   static constexpr int MSUB = BM / 16;
-  static constexpr int NS = (BM >= 64) ? 3 : 4;            // LDS ring depth
-  static constexpr int SLOTS = (BM + kBRows) * 8;          // 16-byte slots per stage
+  static constexpr int NJ = BR / 64;                       // 16-column weight sub-tiles per wave
+  static constexpr int STAGE_BYTES = (BM + BR) * BK * 2;
+  static constexpr int NS = (BR == kBRows) ? ((BM >= 64) ? 3 : 4)   // LDS ring depth
+                                           : ((144 * 1024 / STAGE_BYTES) < 8 ? (144 * 1024 / STAGE_BYTES) : 8);
+  static constexpr int SLOTS = (BM + BR) * 8;              // 16-byte slots per stage
   static constexpr int A_INSTR = BM / 8;                   // wave-instructions (64 slots each)
-  static constexpr int B_INSTR = kBRows / 8;               // 32
+  static constexpr int B_INSTR = BR / 8;
   static constexpr int A_MAX = (A_INSTR + 3) / 4;          // per wave
   static constexpr int A_MIN = A_INSTR / 4;
-  static constexpr int B_PER = B_INSTR / 4;                // 8 per wave
+  static constexpr int B_PER = B_INSTR / 4;                // per wave
   // outstanding DMA instructions allowed while waiting for the oldest stage
   static constexpr int VM_WAIT = (NS - 2) * (A_MIN + B_PER);
+  static_assert(NS >= 3 && VM_WAIT < 64, "ring depth");
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -100,10 +107,10 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Per-tile DMA addressing: byte offsets of every slot this lane fetches.
-template <int BM>
+template <int BM, int BR>
 struct DmaPlan {
-  uint32_t a_off[Tile<BM>::A_MAX];
-  uint32_t b_off[Tile<BM>::B_PER];
+  uint32_t a_off[Tile<BM, BR>::A_MAX];
+  uint32_t b_off[Tile<BM, BR>::B_PER];
 };
 
 // Raw buffer resource (gfx9 V#): 48-bit base, stride 0, size in bytes; loads
@@ -141,10 +148,10 @@ __device__ __forceinline__ void dma4(const int* lds_dst, u32x4_t rsrc, uint32_t 
       : "memory");
 }
 
-template <int BM>
-__device__ __forceinline__ void issue_stage(u32x4_t* buf, const DmaPlan<BM>& d, u32x4_t ra, u32x4_t rb, int wave,
-                                            int kbytes) {
-  using C = Tile<BM>;
+template <int BM, int BR>
+__device__ __forceinline__ void issue_stage(u32x4_t* buf, const DmaPlan<BM, BR>& d, u32x4_t ra, u32x4_t rb,
+                                            int wave, int kbytes) {
+  using C = Tile<BM, BR>;
 #pragma unroll
   for (int qi = 0; qi < C::A_MAX; ++qi) {
     const int q = qi * 4 + wave;
@@ -157,39 +164,38 @@ __device__ __forceinline__ void issue_stage(u32x4_t* buf, const DmaPlan<BM>& d, 
   }
 }
 
-// One K-step from one stage: LIVE row sub-tiles x 4 weight sub-tiles x 2 k32.
-template <int BM, int LIVE>
-__device__ __forceinline__ void mma_stage(f32x4_t (&acc)[BM / 16][4], const u32x4_t* __restrict__ buf,
-                                          const int (&brow)[4], int lane) {
+// One K-step from one stage: LIVE row sub-tiles x NJ weight sub-tiles x 2 k32.
+template <int BM, int NJ, int LIVE>
+__device__ __forceinline__ void mma_stage(f32x4_t (&acc)[BM / 16][NJ], const u32x4_t* __restrict__ buf,
+                                          const int (&brow)[NJ], int lane) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const int sw = (kk * 4 + (lane >> 4)) ^ (lane & 7);
-    bf16x8_t b[4];
+    bf16x8_t b[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = __builtin_bit_cast(bf16x8_t, buf[BM * 8 + (brow[j] + (lane & 15)) * 8 + sw]);
+    for (int j = 0; j < NJ; ++j) b[j] = __builtin_bit_cast(bf16x8_t, buf[BM * 8 + (brow[j] + (lane & 15)) * 8 + sw]);
 #pragma unroll
     for (int i = 0; i < LIVE; ++i) {
       const bf16x8_t a = __builtin_bit_cast(bf16x8_t, buf[(16 * i + (lane & 15)) * 8 + sw]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[i][j], 0, 0, 0);
     }
   }
 }
 
-// K loop over an NS-stage ring; the loop body is unrolled NS times so that
-// every stage buffer has a static role.
-template <int BM, int LIVE>
-__device__ __forceinline__ void kloop(f32x4_t (&acc)[BM / 16][4], u32x4_t* s0, u32x4_t* s1, u32x4_t* s2,
-                                      u32x4_t* s3, const DmaPlan<BM>& d, u32x4_t ra, u32x4_t rb, int wave,
-                                      int lane, int KT, int kbase, bool wave_live,
-                                      const int (&brow)[4]) {
-  using C = Tile<BM>;
+// K loop over an NS-stage ring (stage s at ring + s * SLOTS); the loop body is
+// unrolled NS times so that every stage buffer has a static role.
+template <int BM, int BR, int NJ, int LIVE>
+__device__ __forceinline__ void kloop(f32x4_t (&acc)[BM / 16][NJ], u32x4_t* ring, const DmaPlan<BM, BR>& d,
+                                      u32x4_t ra, u32x4_t rb, int wave, int lane, int KT, int kbase, bool wave_live,
+                                      const int (&brow)[NJ]) {
+  using C = Tile<BM, BR>;
+  static_assert(NJ == C::NJ, "weight sub-tiles per wave");
   constexpr int NS = C::NS;
   // prologue: stages 0 .. NS-2 in flight (kbase: byte offset of this tile's K range)
-  issue_stage<BM>(s0, d, ra, rb, wave, kbase);
-  if (KT > 1) issue_stage<BM>(s1, d, ra, rb, wave, kbase + BK * 2);
-  if (NS == 4 && KT > 2) issue_stage<BM>(s2, d, ra, rb, wave, kbase + 2 * BK * 2);
-  u32x4_t* bufs[4] = {s0, s1, s2, s3};
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < KT) issue_stage<BM, BR>(ring + st * C::SLOTS, d, ra, rb, wave, kbase + st * BK * 2);
   for (int kt0 = 0; kt0 < KT; kt0 += NS) {
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
@@ -200,8 +206,8 @@ __device__ __forceinline__ void kloop(f32x4_t (&acc)[BM / 16][4], u32x4_t* s0, u
       else wait_vmcnt<0>();
       lds_barrier();
       if (kt + NS - 1 < KT)
-        issue_stage<BM>(bufs[(u + NS - 1) % NS], d, ra, rb, wave, kbase + (kt + NS - 1) * BK * 2);
-      if (wave_live) mma_stage<BM, LIVE>(acc, bufs[u], brow, lane);
+        issue_stage<BM, BR>(ring + ((u + NS - 1) % NS) * C::SLOTS, d, ra, rb, wave, kbase + (kt + NS - 1) * BK * 2);
+      if (wave_live) mma_stage<BM, NJ, LIVE>(acc, ring + u * C::SLOTS, brow, lane);
     }
   }
 }
@@ -284,16 +290,15 @@ __device__ __forceinline__ TileCoord tile_coord(int t, int nblk, int G, const in
   return tc;
 }
 
-template <int BM, int EPI>
+template <int BM, int EPI, int BR>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p) {
-  using C = Tile<BM>;
+  using C = Tile<BM, BR>;
   constexpr int MSUB = C::MSUB;
-  constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;  // output columns per tile
+  constexpr int NJ = C::NJ;
+  static_assert(EPI != EPI_SWIGLU || BR == kBRows, "the SwiGLU tile pairs 128 gate with 128 up rows");
+  constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : BR;  // output columns per tile
 
-  __shared__ u32x4_t st0[C::SLOTS];
-  __shared__ u32x4_t st1[C::SLOTS];
-  __shared__ u32x4_t st2[C::SLOTS];
-  __shared__ u32x4_t st3[C::NS == 4 ? C::SLOTS : 1];
+  __shared__ u32x4_t ring[C::NS * C::SLOTS];
   __shared__ int s_off[kMaxGroups + 1];
   __shared__ int s_tb[kMaxGroups + 1];
   __shared__ int s_wsum[kThreads / 64];
@@ -322,12 +327,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
   const int KTc = (KT_all + ksplit - 1) / ksplit;
   const uint32_t row_bytes = (uint32_t)p.K * 2u;
 
-  // weight rows of this wave inside the 256-row B tile (sub-tile bases)
-  int brow[4];
+  // weight rows of this wave inside the BR-row B tile (sub-tile bases)
+  int brow[NJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < NJ; ++j)
     brow[j] = (EPI == EPI_SWIGLU) ? ((j < 2) ? 32 * wave + 16 * j : 128 + 32 * wave + 16 * (j - 2))
-                                  : 64 * wave + 16 * j;
+                                  : (BR / 4) * wave + 16 * j;
 
   for (int t = t_begin + slot; t < t_end; t += nslots) {
     const int kc = __builtin_amdgcn_readfirstlane(t / total_mn);
@@ -340,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
     const uint16_t* Bg = p.B + (int64_t)g * p.b_group_stride;
 
     // DMA plan of this lane: slot s = q*64 + lane holds row s/8, chunk (s%8)^(row%8)
-    DmaPlan<BM> d;
+    DmaPlan<BM, BR> d;
 #pragma unroll
     for (int qi = 0; qi < C::A_MAX; ++qi) {
       const int q = qi * 4 + wave;
@@ -365,21 +370,20 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
     const int b_rows_total = (EPI == EPI_SWIGLU) ? 2 * p.up_row0 : p.N;
     const u32x4_t rb = make_rsrc(Bg, (uint32_t)b_rows_total * row_bytes);
 
-    const int wave_col0 = (EPI == EPI_SWIGLU) ? n0 + 32 * wave : n0 + 64 * wave;
+    const int wave_col0 = (EPI == EPI_SWIGLU) ? n0 + 32 * wave : n0 + (BR / 4) * wave;
     const bool wave_live = wave_col0 < p.N;
 
-    f32x4_t acc[MSUB][4];
+    f32x4_t acc[MSUB][NJ];
 #pragma unroll
     for (int i = 0; i < MSUB; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     switch (msub_live) {
 #define MOE_LIVE_CASE(n)                                                                                      \
   case n:                                                                                                     \
     if (n <= MSUB)                                                                                            \
-      kloop<BM, (n <= MSUB ? n : MSUB)>(acc, st0, st1, st2, st3, d, ra, rb, wave, lane, KT, kbase, wave_live, \
-                                        brow);                                                              \
+      kloop<BM, BR, NJ, (n <= MSUB ? n : MSUB)>(acc, ring, d, ra, rb, wave, lane, KT, kbase, wave_live, brow); \
     break;
       MOE_LIVE_CASE(1) MOE_LIVE_CASE(2) MOE_LIVE_CASE(3) MOE_LIVE_CASE(4)
       MOE_LIVE_CASE(5) MOE_LIVE_CASE(6) MOE_LIVE_CASE(7) MOE_LIVE_CASE(8)
@@ -399,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
       for (int i = 0; i < MSUB; ++i) {
         if (i >= msub_live) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           int col;
           if (EPI == EPI_SWIGLU) {
             const int c0 = wave_col0 + 16 * (j & 1) + (lane & 15);
@@ -440,7 +444,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
         } else {
           float* out = reinterpret_cast<float*>(p.out);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+          for (int j = 0; j < NJ; ++j) {
             const int col = wave_col0 + 16 * j + (lane & 15);
             if (col >= p.N) continue;
 #pragma unroll
@@ -1147,14 +1151,14 @@ __global__ void zero_ints_kernel(int* p, int n) {
 
 // Resident workgroups per CU for one instantiation (the persistent grid must
 // fit in one wave of residency, or the static tile split would serialise).
-template <int BM, int EPI>
+template <int BM, int EPI, int BR>
 int resident_blocks_per_cu() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (cached[dev] == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grouped_gemm_bf16_kernel<BM, EPI>, kThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grouped_gemm_bf16_kernel<BM, EPI, BR>, kThreads, 0) !=
             hipSuccess || n < 1)
       n = 1;
     cached[dev] = n;
@@ -1199,21 +1203,21 @@ int ksplit_for(int64_t M, int64_t G, bool grouped, int64_t N, int64_t K, GemmEpi
   return (int)((KT + ktc - 1) / ktc);  // no empty chunk
 }
 
-template <int BM, int EPI>
+template <int BM, int EPI, int BR = kBRows>
 hipError_t launch_bm(const GemmArgs& a_in, hipStream_t s, const char* name) {
-  constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
+  constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : BR;
   GemmArgs a = a_in;
   a.ksplit = (a.partial != nullptr) ? ksplit_for(a.M, a.G, a.offsets != nullptr, a.N, a.K, (GemmEpilogue)EPI) : 1;
   const int64_t nblk = (a.N + BN_OUT - 1) / BN_OUT;
   int64_t ub_m = (a.M + BM - 1) / BM;
   if (a.offsets) ub_m += (a.G < a.M ? a.G : a.M);
   const int64_t ub = ub_m * nblk * a.ksplit;
-  int64_t grid = (int64_t)device_cu_count() * resident_blocks_per_cu<BM, EPI>();
+  int64_t grid = (int64_t)device_cu_count() * resident_blocks_per_cu<BM, EPI, BR>();
   if (ub < grid) grid = ub;
   grid = ((grid + kXcds - 1) / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
   profile_begin(name, s);
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, EPI>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, EPI, BR>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   if (EPI != EPI_ROUTER && a.ksplit > 1) {
     const int64_t n = (int64_t)a.M * (a.N / 4);
     hipLaunchKernelGGL((splitk_reduce_kernel<EPI>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.partial,
@@ -1317,7 +1321,8 @@ hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, GemmEpilogue epi, hipStre
     case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(a, s, name);
     case EPI_F32: return launch_epi<EPI_F32>(a, s, name);
     case EPI_ROUTER: {
-      hipError_t e = launch_bm<32, EPI_ROUTER>(a, s, name);
+      // up to 128 experts: 128-row weight tiles, half the stage, a deeper ring
+      hipError_t e = (a.N <= 128) ? launch_bm<32, EPI_ROUTER, 128>(a, s, name) : launch_bm<32, EPI_ROUTER>(a, s, name);
       if (e != hipSuccess || a.b_extra == nullptr) return e;
       profile_begin("router_gate_logit_bf16", s);
       hipLaunchKernelGGL(gate_logit_bf16_kernel, dim3((a.M + 3) / 4), dim3(256), 0, s, a.A, a.b_extra, a.M, a.K,
