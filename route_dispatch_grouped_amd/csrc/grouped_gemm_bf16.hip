@@ -536,17 +536,6 @@ __device__ __forceinline__ void big_read(BigFrags& f, const u32x4_t* __restrict_
   }
 }
 
-template <int LIVE>
-__device__ __forceinline__ void big_mma(f32x16_t (&acc)[4][4], const BigFrags& f) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int i = 0; i < LIVE; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[h][j], f.a[h][i], acc[i][j], 0, 0, 0);
-}
-
 // Waits until this wave's DMA of stage `st` has landed, given that stages up
 // to `issued - 1` have been issued (each later stage may stay in flight).
 __device__ __forceinline__ void big_wait(int st, int issued) {
@@ -556,39 +545,50 @@ __device__ __forceinline__ void big_wait(int st, int issued) {
   else wait_vmcnt<0>();
 }
 
-// One K-step for a wave with all four row sub-tiles live: the 32 MFMAs of
-// stage `cur` are issued in eight groups of four, and after each group one DMA
-// instruction of stage kt+4 and two fragment reads of stage kt+1.  Issue is in
-// order, so a long run of DMA or LDS instructions would hold the MFMA pipe
+// One K-step for a wave with LIVE >= 1 live row sub-tiles: the 8 * LIVE MFMAs
+// of stage `cur` are issued in 2 * LIVE groups of four (k16 half h, row
+// sub-tile i); after each group come that group's share of the 8 DMA
+// instructions of stage kt+4 and of the next stage's fragment reads.  Issue is
+// in order, so a long run of DMA or LDS instructions would hold the MFMA pipe
 // idle while the texture and LDS queues drain; spreading them keeps the pipe
-// fed.  Scheduling barriers pin this order.
-template <int EPI>
-__device__ __forceinline__ void big_step_full(f32x16_t (&acc)[4][4], const BigFrags& cur, BigFrags& nxt,
-                                              u32x4_t* refill, const u32x4_t* __restrict__ next_buf, bool dma,
-                                              int kbytes, const BigPlan& d, u32x4_t ra, u32x4_t rb, int wave,
-                                              const int (&a_slot)[2], const int (&b_slot)[2]) {
+// fed.  The reads (weight fragments of h = 0 and 1, then row fragments of
+// h = 0 and 1) all go out in the first half of the step, so that they have
+// landed by the next barrier.  Scheduling barriers pin this order.
+template <int EPI, int LIVE>
+__device__ __forceinline__ void big_step(f32x16_t (&acc)[4][4], const BigFrags& cur, BigFrags& nxt,
+                                         u32x4_t* refill, const u32x4_t* __restrict__ next_buf, bool dma, int kbytes,
+                                         const BigPlan& d, u32x4_t ra, u32x4_t rb, int wave,
+                                         const int (&a_slot)[2], const int (&b_slot)[2]) {
+  static_assert(LIVE >= 1 && LIVE <= 4, "live row sub-tiles");
+  constexpr int NG = 2 * LIVE;
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    const int h = g >> 2, i = g & 3;
+  for (int g = 0; g < NG; ++g) {
+    const int h = g / LIVE, i = g % LIVE;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[h][j], cur.a[h][i], acc[i][j], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
     if (dma) {
-      if (g < 4) dma16(refill + (g * 4 + wave) * 64, ra, d.a_off[g], kbytes);
-      else dma16(refill + Big::A_SLOTS + ((g - 4) * 4 + wave) * 64, rb, d.b_off[g - 4], kbytes);
+#pragma unroll
+      for (int q = (g * 8) / NG; q < ((g + 1) * 8) / NG; ++q) {
+        if (q < 4) dma16(refill + (q * 4 + wave) * 64, ra, d.a_off[q], kbytes);
+        else dma16(refill + Big::A_SLOTS + ((q - 4) * 4 + wave) * 64, rb, d.b_off[q - 4], kbytes);
+      }
     }
-    // fragment reads of the next stage, all in the first half of the step so
-    // that they have landed by the time the step ends at the next barrier:
-    // g = 0, 1 weight sub-tiles (h = g), g = 2, 3 row sub-tiles (h = g - 2)
-    if (g < 2) {
+    // read chunk c (0, 1: weight fragments of h = c; 2, 3: row fragments of
+    // h = c - 2) goes out with group (c * NG) / 8
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        nxt.b[g][jj] = __builtin_bit_cast(bf16x8_t, next_buf[b_slot[g] + big_b_off<EPI>(jj)]);
-    } else if (g < 4) {
+    for (int c = 0; c < 4; ++c) {
+      if ((c * NG) / 8 != g) continue;
+      if (c < 2) {
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        nxt.a[g - 2][ii] = __builtin_bit_cast(bf16x8_t, next_buf[a_slot[g - 2] + 256 * ii]);
+        for (int jj = 0; jj < 4; ++jj)
+          nxt.b[c][jj] = __builtin_bit_cast(bf16x8_t, next_buf[b_slot[c] + big_b_off<EPI>(jj)]);
+      } else {
+#pragma unroll
+        for (int ii = 0; ii < LIVE; ++ii)
+          nxt.a[c - 2][ii] = __builtin_bit_cast(bf16x8_t, next_buf[a_slot[c - 2] + 256 * ii]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -631,13 +631,11 @@ __device__ __forceinline__ void big_kloop(f32x16_t (&acc)[4][4], u32x4_t* s0, u3
       big_wait(kt + 1, issued);
       lds_barrier();
       const bool dma = kt + 4 < KT;
-      if (LIVE == 4) {
-        big_step_full<EPI>(acc, cur, nxt, bufs[u], bufs[(u + 1) & 3], dma, (kt + 4) * Big::KB * 2, d, ra, rb,
-                           wave, a_slot, b_slot);
+      if constexpr (LIVE >= 1) {
+        big_step<EPI, LIVE>(acc, cur, nxt, bufs[u], bufs[(u + 1) & 3], dma, (kt + 4) * Big::KB * 2, d, ra, rb,
+                            wave, a_slot, b_slot);
       } else {
         if (dma) big_issue(bufs[u], d, ra, rb, wave, (kt + 4) * Big::KB * 2);
-        big_read<EPI, LIVE>(nxt, bufs[(u + 1) & 3], a_slot, b_slot);
-        big_mma<LIVE>(acc, cur);
       }
       if (dma) ++issued;
     }
@@ -916,13 +914,11 @@ __device__ __forceinline__ void pipe_kloop(f32x16_t (&acc)[4][4], u32x4_t* s0, u
       }
       const BigPlan& dd = last ? dn : d;
       const u32x4_t rbs = last ? rbn : rb;
-      if (LIVE == 4) {
-        big_step_full<EPI>(acc, cur, nxt, bufs[u], bufs[(u + 1) & 3], dma, kbytes, dd, ra, rbs, wave, a_slot,
-                           b_slot);
+      if constexpr (LIVE >= 1) {
+        big_step<EPI, LIVE>(acc, cur, nxt, bufs[u], bufs[(u + 1) & 3], dma, kbytes, dd, ra, rbs, wave, a_slot,
+                            b_slot);
       } else {
         if (dma) big_issue(bufs[u], dd, ra, rbs, wave, kbytes);
-        big_read<EPI, LIVE>(nxt, bufs[(u + 1) & 3], a_slot, b_slot);
-        big_mma<LIVE>(acc, cur);
       }
     }
   }
