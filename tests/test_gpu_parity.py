@@ -403,3 +403,48 @@ def test_ep_routing_table():
         rdg.moe_ep_routing_table(to_device(np.zeros(5, np.int32)), to_device(np.zeros(6, np.float32)), 3, 2, 0, 1)
     with pytest.raises(rdg.MoeError, match="gate_weights length mismatch"):
         rdg.moe_ep_routing_table(to_device(np.zeros(6, np.int32)), to_device(np.zeros(5, np.float32)), 3, 2, 0, 1)
+
+
+@pytest.mark.parametrize("name", ["bf16_decode_shared", "bf16_pipe_tiles"])
+def test_forward_graph_capture(name):
+    """The whole forward captured into a HIP graph (through torch's graph API)
+    and replayed several times, with eager work and synchronisation between
+    the replays: every replay equals the eager forward bit for bit.  Covers the
+    shared expert's fork onto the second stream and the split-K scratch
+    (decode), and the pipelined 256-row GEMMs (large batch)."""
+    cfg = SMALL[name]
+    log(f"[parity] graph capture {name}")
+    inp = workloads.generate(cfg, seed=6)
+    dev = device_inputs(inp)
+    layer = rdg.MoeLayer(dev["router_weight"], dev["w13"], dev["w2"], cfg.top_k, router_bias=dev.get("router_bias"),
+                         shared_w13=dev.get("shared_w13"), shared_w2=dev.get("shared_w2"),
+                         shared_gate=dev.get("shared_gate"), renormalize=cfg.renormalize)
+    x = dev["x"].clone()
+    ref = layer(x).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            layer(x)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = layer(x)
+    for rep in range(4):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep}"
+        # eager work in between, on the same buffers
+        eager = layer(x)
+        torch.cuda.synchronize()
+        assert torch.equal(eager, ref)
+    # a new input copied into the captured input buffer changes the replay
+    x.copy_(dev["x"].flip(0))
+    graph.replay()
+    torch.cuda.synchronize()
+    expect = rdg.moe_forward(dev["x"].flip(0).contiguous(), dev["router_weight"], dev["w13"], dev["w2"], cfg.top_k,
+                             router_bias=dev.get("router_bias"), shared_w13=dev.get("shared_w13"),
+                             shared_w2=dev.get("shared_w2"), shared_gate=dev.get("shared_gate"),
+                             renormalize=cfg.renormalize)
+    assert torch.equal(out, expect)
