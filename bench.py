@@ -49,7 +49,7 @@ def kernel_work(name, cfg, touched, touched_shared=True):
     T, H, E, k, I = cfg.num_tokens, cfg.hidden_size, cfg.num_experts, cfg.top_k, cfg.intermediate_size
     Is = cfg.shared_intermediate_size
     P = T * k
-    es = 2 if cfg.dtype == "bf16" else 4
+    es = 2 if cfg.dtype == "bf16" else 4  # activations, weights and h; y is fp32
     if name in ("ffn_gate_up_bf16", "ffn_gate_up_f32"):
         # weights of touched experts, every token row once, h written once
         return 4.0 * P * H * I, touched * 2 * I * H * es + T * H * es + P * I * es
@@ -71,6 +71,7 @@ def kernel_work(name, cfg, touched, touched_shared=True):
     if name == "dispatch_scatter":
         return 0.0, P * 4 + 3 * P * 4
     if name == "combine":
+        # y and the shared output (fp32) read once, fp32 output written once
         return 0.0, P * H * 4 + P * 8 + T * H * 4 + (T * H * 4 if Is else 0)
     return 0.0, 0.0
 

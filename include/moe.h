@@ -16,9 +16,10 @@
  *    a pointer after the call returns.  Pointers to activations, weights and
  *    outputs must be 16-byte aligned.
  *  - `dtype` (moe_dtype) is the storage type of the hidden states and of every
- *    weight.  Logits, routing weights, router bias, shared-gate logits and the
- *    packed expert outputs are always float32; expert ids and every dispatch
- *    array are int32.
+ *    weight.  Logits, routing weights, router bias and shared-gate logits are
+ *    always float32; the packed expert outputs are float32 or, for bf16
+ *    layers, bf16 (an explicit argument says which); expert ids and every
+ *    dispatch array are int32.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
  *    call only enqueues work on that stream: it does not synchronise and does
  *    not copy anything to the host.
@@ -48,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 #define MOE_MAX_EXPERTS 512
 
 typedef enum moe_status {
@@ -183,7 +184,7 @@ moe_status moe_ep_routing_table(const int32_t* gate_indices, int64_t gate_indice
  * with x = hidden_states[packed_token_indices[p]]:
  *   g = w13[e, 0:I, :] . x,  u = w13[e, I:2I, :] . x
  *   h = silu(g) * u,  silu(z) = z / (1 + exp(-z))
- *   packed_expert_outputs[p] = w2[e] . h                                     [P,H] f32
+ *   packed_expert_outputs[p] = w2[e] . h                          [P,H] expert_out_dtype
  * Routing weights are NOT applied here (moe_combine applies them).
  *
  * hidden_states [T,H] dtype; packed_token_indices [P] int32, or NULL meaning
@@ -191,7 +192,10 @@ moe_status moe_ep_routing_table(const int32_t* gate_indices, int64_t gate_indice
  * NULL meaning a single expert (E must be 1) owning all P rows; w13 [E,2I,H]
  * dtype; w2 [E,H,I] dtype.  P = num_tokens * top_k.
  * Numerics (bf16): fp32 accumulation, h rounded once to bf16 (it is the
- * operand of the second bf16 GEMM), outputs fp32.  f32: fp32 throughout.
+ * operand of the second bf16 GEMM), outputs fp32 or rounded once to bf16
+ * (expert_out_dtype MOE_DTYPE_F32 or MOE_DTYPE_BF16; bf16 halves the bytes
+ * the down projection writes and the combine reads).  f32 layers: fp32
+ * throughout, expert_out_dtype must be MOE_DTYPE_F32.
  * Experts with no rows are skipped and their weights are not read.
  * workspace: moe_grouped_ffn_workspace_size(...) bytes (tile counters, h,
  * and for few rows per expert the fp32 partial sums of a split K loop).
@@ -202,7 +206,7 @@ moe_status moe_grouped_ffn(const void* hidden_states, const int32_t* packed_toke
                            const int32_t* expert_offsets, const void* w13, const void* w2,
                            int64_t num_tokens, int64_t hidden_size, int64_t num_experts,
                            int64_t top_k, int64_t intermediate_size, int dtype,
-                           float* packed_expert_outputs,
+                           int expert_out_dtype, void* packed_expert_outputs,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -214,16 +218,18 @@ moe_status moe_grouped_ffn(const void* hidden_states, const int32_t* packed_toke
  *               (+ sigmoid(shared_gate_logit[t]) * shared_output[t])
  * summed in ascending j in fp32, the shared term added last.
  *
- * packed_expert_outputs [P,H] f32; inverse_permutation [P] int32; topk_weights
- * [T,k] f32; shared_output [T,H] f32 or NULL; shared_gate_logit [T] f32 or NULL
- * (NULL with a shared_output means a gate of 1); out_dtype MOE_DTYPE_F32 or
- * MOE_DTYPE_BF16 (round to nearest even); output [T,H] out_dtype.
+ * packed_expert_outputs [P,H] and shared_output [T,H] (or NULL) are
+ * expert_dtype (MOE_DTYPE_F32 or MOE_DTYPE_BF16; bf16 values are widened
+ * exactly); inverse_permutation [P] int32; topk_weights [T,k] f32;
+ * shared_gate_logit [T] f32 or NULL (NULL with a shared_output means a gate
+ * of 1); out_dtype MOE_DTYPE_F32 or MOE_DTYPE_BF16 (round to nearest even);
+ * output [T,H] out_dtype.
  */
-moe_status moe_combine(const float* packed_expert_outputs, const int32_t* inverse_permutation,
-                       const float* topk_weights, const float* shared_output,
+moe_status moe_combine(const void* packed_expert_outputs, const int32_t* inverse_permutation,
+                       const float* topk_weights, const void* shared_output,
                        const float* shared_gate_logit,
                        int64_t num_tokens, int64_t hidden_size, int64_t top_k,
-                       int out_dtype, void* output, void* stream);
+                       int expert_dtype, int out_dtype, void* output, void* stream);
 
 /*
  * Whole layer forward: router -> dispatch plan -> grouped FFN -> combine,
@@ -241,7 +247,8 @@ moe_status moe_combine(const float* packed_expert_outputs, const int32_t* invers
  * Optional outputs (NULL to skip): topk_ids_out [T,k] int32, topk_weights_out
  * [T,k] f32, router_logits_out [T,E] f32.
  * workspace: moe_forward_workspace_size(...) bytes; it holds the routing, the
- * plan, h and the packed expert outputs.
+ * plan, h and the packed expert outputs (fp32: bf16 storage would about
+ * double the output error of a bf16 layer).
  */
 size_t moe_forward_workspace_size(int64_t num_tokens, int64_t hidden_size, int64_t num_experts,
                                   int64_t top_k, int64_t intermediate_size,

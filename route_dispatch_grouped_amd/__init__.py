@@ -66,8 +66,8 @@ _SIGNATURES = {
                                     _c_void_p]),
     "moe_grouped_ffn_workspace_size": (_size, [_i64, _i64, _i64, _i64, _i64, _int]),
     "moe_grouped_ffn": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64,
-                               _i64, _int, _c_void_p, _c_void_p, _size, _c_void_p]),
-    "moe_combine": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _int,
+                               _i64, _int, _int, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "moe_combine": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _int, _int,
                            _c_void_p, _c_void_p]),
     "moe_forward_workspace_size": (_size, [_i64, _i64, _i64, _i64, _i64, _i64, _int]),
     "moe_forward": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -261,10 +261,11 @@ def moe_ep_routing_table(gate_indices: torch.Tensor, gate_weights: torch.Tensor,
 
 def moe_grouped_ffn(hidden_states: torch.Tensor, packed_token_indices: Optional[torch.Tensor],
                     expert_offsets: Optional[torch.Tensor], w13: torch.Tensor, w2: torch.Tensor, top_k: int,
-                    stream=None) -> torch.Tensor:
+                    out_dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
     """Grouped SwiGLU experts over the expert-major layout (include/moe.h: moe_grouped_ffn).
 
-    Returns the packed expert outputs ``[T*top_k, H]`` float32 (routing weights not applied).
+    Returns the packed expert outputs ``[T*top_k, H]`` in ``out_dtype`` (float32,
+    or bfloat16 for a bf16 layer; routing weights not applied).
     """
     lib = load_library()
     T, H = hidden_states.shape
@@ -280,12 +281,12 @@ def moe_grouped_ffn(hidden_states: torch.Tensor, packed_token_indices: Optional[
     if expert_offsets is not None:
         _need(expert_offsets, "expert_offsets", (E + 1,), torch.int32)
     dev = hidden_states.device
-    y = torch.empty((P, H), dtype=torch.float32, device=dev)
+    y = torch.empty((P, H), dtype=out_dtype, device=dev)
     ws_bytes = lib.moe_grouped_ffn_workspace_size(T, H, top_k, E, I, _dtype_code(dt))
     ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
     st = lib.moe_grouped_ffn(_ptr(hidden_states), _ptr(packed_token_indices), _ptr(expert_offsets), _ptr(w13),
-                             _ptr(w2), T, H, E, int(top_k), I, _dtype_code(dt), _ptr(y), _ptr(ws), ws.numel(),
-                             _stream(stream))
+                             _ptr(w2), T, H, E, int(top_k), I, _dtype_code(dt), _dtype_code(out_dtype), _ptr(y),
+                             _ptr(ws), ws.numel(), _stream(stream))
     _check("moe_grouped_ffn", st)
     return y
 
@@ -293,21 +294,25 @@ def moe_grouped_ffn(hidden_states: torch.Tensor, packed_token_indices: Optional[
 def moe_combine(packed_expert_outputs: torch.Tensor, inverse_permutation: torch.Tensor, topk_weights: torch.Tensor,
                 shared_output: Optional[torch.Tensor] = None, shared_gate_logit: Optional[torch.Tensor] = None,
                 out_dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
-    """Weighted combine to token order (include/moe.h: moe_combine)."""
+    """Weighted combine to token order (include/moe.h: moe_combine).
+
+    ``packed_expert_outputs`` (and ``shared_output``) are float32 or bfloat16.
+    """
     lib = load_library()
     T, k = topk_weights.shape
     H = packed_expert_outputs.shape[1]
-    _need(packed_expert_outputs, "packed_expert_outputs", (T * k, H), torch.float32)
+    ydt = packed_expert_outputs.dtype
+    _need(packed_expert_outputs, "packed_expert_outputs", (T * k, H), ydt)
     _need(inverse_permutation, "inverse_permutation", (T * k,), torch.int32)
     _need(topk_weights, "topk_weights", (T, k), torch.float32)
     if shared_output is not None:
-        _need(shared_output, "shared_output", (T, H), torch.float32)
+        _need(shared_output, "shared_output", (T, H), ydt)
     if shared_gate_logit is not None:
         _need(shared_gate_logit, "shared_gate_logit", (T,), torch.float32)
     out = torch.empty((T, H), dtype=out_dtype, device=packed_expert_outputs.device)
     st = lib.moe_combine(_ptr(packed_expert_outputs), _ptr(inverse_permutation), _ptr(topk_weights),
-                         _ptr(shared_output), _ptr(shared_gate_logit), T, H, k, _dtype_code(out_dtype), _ptr(out),
-                         _stream(stream))
+                         _ptr(shared_output), _ptr(shared_gate_logit), T, H, k, _dtype_code(ydt),
+                         _dtype_code(out_dtype), _ptr(out), _stream(stream))
     _check("moe_combine", st)
     return out
 

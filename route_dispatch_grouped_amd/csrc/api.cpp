@@ -62,11 +62,12 @@ moe_status check_sizes(int64_t T, int64_t H, int64_t E, int64_t k, int dtype, bo
 
 // The bf16 kernels address every operand with 32-bit byte offsets from a
 // buffer base (one expert's weights, the activations, h).
-moe_status check_buffer_bytes(int64_t T, int64_t H, int64_t k, int64_t I, int dtype) {
+// y_elt: bytes per element of the packed expert outputs [T*k, H] (0: none)
+moe_status check_buffer_bytes(int64_t T, int64_t H, int64_t k, int64_t I, int dtype, int64_t y_elt = 0) {
   if (dtype != MOE_DTYPE_BF16) return MOE_OK;
   const int64_t lim = ((int64_t)1 << 31) - 1;
-  if (T * H * 2 > lim || T * k * I * 2 > lim || 2 * I * H * 2 > lim)
-    return fail(MOE_ERR_UNSUPPORTED, "a bf16 operand exceeds 2 GiB (32-bit buffer offsets)");
+  if (T * H * 2 > lim || T * k * I * 2 > lim || 2 * I * H * 2 > lim || T * k * H * y_elt > lim)
+    return fail(MOE_ERR_UNSUPPORTED, "a bf16-layer operand exceeds 2 GiB (32-bit buffer offsets)");
   return MOE_OK;
 }
 
@@ -117,7 +118,7 @@ struct ForwardLayout {
   int32_t* packed_ids;
   void* dispatch_scratch;
   void* h;
-  float* y;
+  float* y;  // packed expert outputs (fp32: bf16 would double the layer's output error)
   void* hs;
   float* ys;
   int* counters;  // tile counters of the four grouped GEMMs (routed, shared)
@@ -197,9 +198,10 @@ hipError_t run_router(const void* x, const void* wr, const float* bias, const vo
   return moe::launch_topk(logits, T, E, k, renorm, ids, weights, probs, s);
 }
 
-// counters: 2 * kTileCounterInts zeroed ints (gate/up, down) or NULL.
+// counters: 2 * kTileCounterInts zeroed ints (gate/up, down) or NULL.  y is
+// bf16 when y_dtype is MOE_DTYPE_BF16 (bf16 layers only), else fp32.
 hipError_t run_ffn(const void* x, const int32_t* gather, const int32_t* offsets, const void* w13, const void* w2,
-                   int T_rows, int P, int H, int E, int I, int dtype, void* h, float* y, hipStream_t s,
+                   int T_rows, int P, int H, int E, int I, int dtype, void* h, void* y, int y_dtype, hipStream_t s,
                    bool shared, int* counters, float* partial) {
   hipError_t e;
   if (dtype == MOE_DTYPE_BF16) {
@@ -236,13 +238,14 @@ hipError_t run_ffn(const void* x, const int32_t* gather, const int32_t* offsets,
     b.ldo = H;
     b.tile_counter = counters ? counters + moe::kTileCounterInts : nullptr;
     b.partial = partial;
-    return moe::launch_grouped_gemm_bf16(b, moe::EPI_F32, s, shared ? "shared_down_bf16" : "ffn_down_bf16");
+    return moe::launch_grouped_gemm_bf16(b, y_dtype == MOE_DTYPE_BF16 ? moe::EPI_BF16 : moe::EPI_F32, s,
+                                         shared ? "shared_down_bf16" : "ffn_down_bf16");
   }
   e = moe::launch_ffn_gate_up_f32(static_cast<const float*>(x), gather, offsets, static_cast<const float*>(w13), P,
                                   H, E, I, static_cast<float*>(h), s);
   if (e != hipSuccess) return e;
   return moe::launch_ffn_down_f32(static_cast<const float*>(h), offsets, static_cast<const float*>(w2), P, H, E, I,
-                                  y, s);
+                                  static_cast<float*>(y), s);
 }
 
 // -------------------------------------------------------------- profiling
@@ -454,11 +457,16 @@ size_t moe_grouped_ffn_workspace_size(int64_t num_tokens, int64_t hidden_size, i
 moe_status moe_grouped_ffn(const void* hidden_states, const int32_t* packed_token_indices,
                            const int32_t* expert_offsets, const void* w13, const void* w2, int64_t num_tokens,
                            int64_t hidden_size, int64_t num_experts, int64_t top_k, int64_t intermediate_size,
-                           int dtype, float* packed_expert_outputs, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+                           int dtype, int expert_out_dtype, void* packed_expert_outputs, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   RETURN_IF_ERR(check_sizes(num_tokens, hidden_size, num_experts, top_k, dtype, true));
   RETURN_IF_ERR(check_inter(intermediate_size, dtype, "intermediate_size"));
-  RETURN_IF_ERR(check_buffer_bytes(num_tokens, hidden_size, top_k, intermediate_size, dtype));
+  if (expert_out_dtype != MOE_DTYPE_F32 && expert_out_dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "expert_out_dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
+  if (expert_out_dtype == MOE_DTYPE_BF16 && dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "bf16 expert outputs need a bf16 layer");
+  RETURN_IF_ERR(check_buffer_bytes(num_tokens, hidden_size, top_k, intermediate_size, dtype,
+                                   dtype_size(expert_out_dtype)));
   if (num_tokens == 0) return succeed();
   REQUIRE_PTR(hidden_states);
   REQUIRE_PTR(w13);
@@ -490,19 +498,22 @@ moe_status moe_grouped_ffn(const void* hidden_states, const int32_t* packed_toke
   }
   return hip_status(run_ffn(hidden_states, packed_token_indices, expert_offsets, w13, w2, (int)num_tokens, P,
                             (int)hidden_size, (int)num_experts, (int)intermediate_size, dtype, h,
-                            packed_expert_outputs, s, false, dtype == MOE_DTYPE_BF16 ? counters : nullptr,
+                            packed_expert_outputs, expert_out_dtype, s, false,
+                            dtype == MOE_DTYPE_BF16 ? counters : nullptr,
                             partial),
                     "moe_grouped_ffn");
 }
 
-moe_status moe_combine(const float* packed_expert_outputs, const int32_t* inverse_permutation,
-                       const float* topk_weights, const float* shared_output, const float* shared_gate_logit,
-                       int64_t num_tokens, int64_t hidden_size, int64_t top_k, int out_dtype, void* output,
-                       void* stream) {
+moe_status moe_combine(const void* packed_expert_outputs, const int32_t* inverse_permutation,
+                       const float* topk_weights, const void* shared_output, const float* shared_gate_logit,
+                       int64_t num_tokens, int64_t hidden_size, int64_t top_k, int expert_dtype, int out_dtype,
+                       void* output, void* stream) {
   if (num_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "num_tokens is negative");
   if (top_k < 1) return fail(MOE_ERR_INVALID_ARG, "top_k must be >= 1");
   if (hidden_size < 1) return fail(MOE_ERR_INVALID_ARG, "hidden_size must be >= 1");
   if (hidden_size % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "hidden_size % 8 != 0");
+  if (expert_dtype != MOE_DTYPE_F32 && expert_dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "expert_dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
   if (out_dtype != MOE_DTYPE_F32 && out_dtype != MOE_DTYPE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "out_dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
   if (num_tokens * top_k >= (int64_t)1 << 31) return fail(MOE_ERR_UNSUPPORTED, "num_tokens * top_k must be < 2^31");
@@ -517,9 +528,9 @@ moe_status moe_combine(const float* packed_expert_outputs, const int32_t* invers
   REQUIRE_ALIGNED(shared_output);
   REQUIRE_ALIGNED(output);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(moe::launch_combine(packed_expert_outputs, inverse_permutation, topk_weights, shared_output,
-                                        shared_gate_logit, (int)num_tokens, (int)hidden_size, (int)top_k,
-                                        out_dtype == MOE_DTYPE_BF16, output, s),
+  return hip_status(moe::launch_combine(packed_expert_outputs, expert_dtype == MOE_DTYPE_BF16, inverse_permutation,
+                                        topk_weights, shared_output, shared_gate_logit, (int)num_tokens,
+                                        (int)hidden_size, (int)top_k, out_dtype == MOE_DTYPE_BF16, output, s),
                     "moe_combine");
 }
 
@@ -546,8 +557,8 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
     return fail(MOE_ERR_INVALID_ARG, "shared_w13, shared_w2 and shared_gate must be given together");
   const int64_t Is = nshared ? shared_intermediate_size : 0;
   if (nshared) RETURN_IF_ERR(check_inter(Is, dtype, "shared_intermediate_size"));
-  RETURN_IF_ERR(check_buffer_bytes(num_tokens, hidden_size, top_k, intermediate_size, dtype));
-  if (nshared) RETURN_IF_ERR(check_buffer_bytes(num_tokens, hidden_size, 1, Is, dtype));
+  RETURN_IF_ERR(check_buffer_bytes(num_tokens, hidden_size, top_k, intermediate_size, dtype, 4));
+  if (nshared) RETURN_IF_ERR(check_buffer_bytes(num_tokens, hidden_size, 1, Is, dtype, 4));
   if (out_dtype != MOE_DTYPE_F32 && out_dtype != MOE_DTYPE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "out_dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
   if (num_tokens == 0) return succeed();
@@ -578,16 +589,11 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
   float* weights = topk_weights_out ? topk_weights_out : L.weights;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  hipError_t e = run_router(hidden_states, router_weight, router_bias, Is ? shared_gate : nullptr, T, H, E, k,
-                            renormalize ? 1 : 0, dtype, logits, nullptr, ids, weights, Is ? L.gate_logit : nullptr, s);
-  if (e != hipSuccess) return hip_status(e, "moe_forward(router)");
-  // the dispatch scan also zeroes the tile counters of the grouped GEMMs below
-  e = moe::launch_dispatch(ids, nullptr, T, k, E, L.counts, L.offsets, L.perm, L.inv, L.packed_ids, nullptr,
-                           L.dispatch_scratch, s, L.counters, 4 * moe::kTileCounterInts);
-  if (e != hipSuccess) return hip_status(e, "moe_forward(dispatch)");
-  // shared expert on the aux stream (forked after the dispatch, which zeroes
-  // its tile counters), routed experts on the caller's stream, join before
-  // the combine
+  hipError_t e = hipSuccess;
+  // The shared expert depends only on the input: it starts first, on the aux
+  // stream, so that its weight streaming overlaps the router, top-k and
+  // dispatch (small launches that leave most of the chip idle) and then the
+  // routed experts; the join comes before the combine.
   std::unique_lock<std::mutex> aux_lock(g_aux_mu, std::defer_lock);
   AuxStream* aux = nullptr;
   if (Is) {
@@ -600,23 +606,40 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
       if (e != hipSuccess) return hip_status(e, "moe_forward(fork)");
       ss = aux->stream;
     }
-    e = run_ffn(hidden_states, nullptr, nullptr, shared_w13, shared_w2, T, T, H, 1, (int)Is, dtype, L.hs, L.ys, ss,
-                true, L.counters + 2 * moe::kTileCounterInts, L.partial_shared);
+    int* shared_counters = L.counters + 2 * moe::kTileCounterInts;
+    if (dtype == MOE_DTYPE_BF16) {
+      moe::GemmArgs probe = gemm_args();
+      probe.M = T;
+      probe.G = 1;
+      if (moe::grouped_gemm_uses_counter(probe)) {
+        e = moe::launch_zero_ints(shared_counters, 2 * moe::kTileCounterInts, ss);
+        if (e != hipSuccess) return hip_status(e, "moe_forward(shared expert)");
+      }
+    }
+    e = run_ffn(hidden_states, nullptr, nullptr, shared_w13, shared_w2, T, T, H, 1, (int)Is, dtype, L.hs, L.ys,
+                MOE_DTYPE_F32, ss, true, shared_counters, L.partial_shared);
     if (e != hipSuccess) return hip_status(e, "moe_forward(shared expert)");
     if (aux != nullptr) {
       e = hipEventRecord(aux->join, aux->stream);
       if (e != hipSuccess) return hip_status(e, "moe_forward(join)");
     }
   }
-  e = run_ffn(hidden_states, L.packed_ids, L.offsets, w13, w2, T, P, H, E, I, dtype, L.h, L.y, s, false,
-              L.counters, L.partial);
+  e = run_router(hidden_states, router_weight, router_bias, Is ? shared_gate : nullptr, T, H, E, k,
+                 renormalize ? 1 : 0, dtype, logits, nullptr, ids, weights, Is ? L.gate_logit : nullptr, s);
+  if (e != hipSuccess) return hip_status(e, "moe_forward(router)");
+  // the dispatch scan also zeroes the tile counters of the routed GEMMs
+  e = moe::launch_dispatch(ids, nullptr, T, k, E, L.counts, L.offsets, L.perm, L.inv, L.packed_ids, nullptr,
+                           L.dispatch_scratch, s, L.counters, 2 * moe::kTileCounterInts);
+  if (e != hipSuccess) return hip_status(e, "moe_forward(dispatch)");
+  e = run_ffn(hidden_states, L.packed_ids, L.offsets, w13, w2, T, P, H, E, I, dtype, L.h, L.y, MOE_DTYPE_F32, s,
+              false, L.counters, L.partial);
   if (e != hipSuccess) return hip_status(e, "moe_forward(experts)");
   if (aux != nullptr) {
     e = hipStreamWaitEvent(s, aux->join, 0);
     if (e != hipSuccess) return hip_status(e, "moe_forward(join)");
   }
   if (aux_lock.owns_lock()) aux_lock.unlock();
-  e = moe::launch_combine(L.y, L.inv, weights, Is ? L.ys : nullptr, Is ? L.gate_logit : nullptr, T, H, k,
+  e = moe::launch_combine(L.y, 0, L.inv, weights, Is ? L.ys : nullptr, Is ? L.gate_logit : nullptr, T, H, k,
                           out_dtype == MOE_DTYPE_BF16, output, s);
   return hip_status(e, "moe_forward(combine)");
 }

@@ -6,6 +6,7 @@
 //               the modelexpress refit test lays them out) and writes
 //               h = silu(g) * u as bf16.               [DWDP README "Executor Module"]
 //   EPI_F32     down projection y = W2[e] h, fp32 out.  [DWDP README "Executor Module"]
+//   EPI_BF16    the same, y rounded once to bf16 (RNE).
 //   EPI_ROUTER  router logits x Wr^T (+ bias).          [DWDP README "Router Module"]
 //
 // Scheduling: the packed rows of each group (expert) form expert-major execution
@@ -80,6 +81,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return static_cast<uint16_t>(u >> 16);
+}
+
+// two values rounded to bf16, the first in the low half (the lower address)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
 }
 
 // silu(g) * u = g * u / (1 + e^-g), with the hardware reciprocal (about 1 ulp)
@@ -441,6 +447,18 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
               }
             }
           }
+        } else if (EPI == EPI_BF16) {
+          uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const int col = wave_col0 + 16 * j + (lane & 15);
+            if (col >= p.N) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int row = 16 * i + 4 * (lane >> 4) + r;
+              if (row < rows) out[(int64_t)(m0 + row) * p.ldo + col] = f32_to_bf16_rne(acc[i][j][r]);
+            }
+          }
         } else {
           float* out = reinterpret_cast<float*>(p.out);
 #pragma unroll
@@ -779,6 +797,20 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_big_kernel(GemmArg
             *reinterpret_cast<uint2*>(out + col) = v;
           }
         }
+      } else if (EPI == EPI_BF16) {
+        uint16_t* out = reinterpret_cast<uint16_t*>(p.out) + (int64_t)(m0 + row) * p.ldo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int col = n0 + 128 * wn + 32 * j + 8 * gq + 4 * (lane >> 5);
+            if (col >= p.N) continue;
+            uint2 v;
+            v.x = pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]);
+            v.y = pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
+            *reinterpret_cast<uint2*>(out + col) = v;
+          }
+        }
       } else {
         float* out = reinterpret_cast<float*>(p.out) + (int64_t)(m0 + row) * p.ldo;
 #pragma unroll
@@ -970,7 +1002,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
   const u32x4_t ra = make_rsrc(p.A, (uint32_t)p.a_rows * row_bytes);
   const int b_rows_total = (EPI == EPI_SWIGLU) ? 2 * p.up_row0 : p.N;
   const uint32_t b_bytes = (uint32_t)b_rows_total * row_bytes;
-  const size_t out_elt = (EPI == EPI_SWIGLU) ? 2 : 4;
+  const size_t out_elt = (EPI == EPI_F32) ? 4 : 2;
   const __amdgpu_buffer_rsrc_t ro =
       __builtin_amdgcn_make_buffer_rsrc(p.out, (short)0, (int)((size_t)p.M * p.ldo * out_elt), kBufferWord3);
 
@@ -1065,6 +1097,20 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
             __builtin_amdgcn_raw_buffer_store_b64(v, ro, (int)off, 0, 0);
           }
         }
+      } else if (EPI == EPI_BF16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int col = n0 + 128 * wn + 32 * j + 8 * gq + 4 * (lane >> 5);
+            typedef int i32x2_t __attribute__((ext_vector_type(2)));
+            const i32x2_t v = {(int)pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]),
+                               (int)pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3])};
+            const uint32_t off = (row_ok && col < p.N) ? (uint32_t)(((int64_t)(m0 + row) * p.ldo + col) * 2)
+                                                       : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b64(v, ro, (int)off, 0, 0);
+          }
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -1093,7 +1139,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
 
 // Split-K reduction: the chunks' fp32 partial sums added in chunk order (so
 // the result does not depend on timing), then the epilogue of the unsplit
-// kernel: SwiGLU to bf16 h, or fp32 y.  One thread per 4 columns of a row.
+// kernel: SwiGLU to bf16 h, or y in fp32 or bf16.  One thread per 4 columns
+// of a row.
 template <int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int ksplit, int M,
                                                             int N, void* __restrict__ out, int64_t ldo) {
@@ -1116,6 +1163,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     uint2 v;
     v.x = hb[0] | (hb[1] << 16);
     v.y = hb[2] | (hb[3] << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + row * ldo + col) = v;
+  } else if (EPI == EPI_BF16) {
+    uint2 v;
+    v.x = pack_bf16x2(a[0], a[1]);
+    v.y = pack_bf16x2(a[2], a[3]);
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + row * ldo + col) = v;
   } else {
     *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + row * ldo + col) = a;
@@ -1316,6 +1368,7 @@ hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, GemmEpilogue epi, hipStre
   switch (epi) {
     case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(a, s, name);
     case EPI_F32: return launch_epi<EPI_F32>(a, s, name);
+    case EPI_BF16: return launch_epi<EPI_BF16>(a, s, name);
     case EPI_ROUTER: {
       // up to 128 experts: 128-row weight tiles, half the stage, a deeper ring
       hipError_t e = (a.N <= 128) ? launch_bm<32, EPI_ROUTER, 128>(a, s, name) : launch_bm<32, EPI_ROUTER>(a, s, name);

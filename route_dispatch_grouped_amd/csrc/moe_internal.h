@@ -23,6 +23,7 @@ enum GemmEpilogue {
   EPI_SWIGLU = 0,  // paired gate/up rows -> h = silu(g) * u, stored bf16
   EPI_F32 = 1,     // plain fp32 store
   EPI_ROUTER = 2,  // fp32 logits (+ bias), extra column -> gate logit
+  EPI_BF16 = 3,    // plain store rounded once to bf16 (RNE)
 };
 
 struct GemmArgs {
@@ -38,7 +39,7 @@ struct GemmArgs {
   int K;                    // reduction length, multiple of 64
   int N;                    // output columns (EPI_SWIGLU: I, the h width)
   int up_row0;              // EPI_SWIGLU: first up row inside a group (= I)
-  void* out;                // EPI_SWIGLU: bf16 h; EPI_F32: f32; EPI_ROUTER: f32 logits
+  void* out;                // EPI_SWIGLU: bf16 h; EPI_F32: f32; EPI_BF16: bf16; EPI_ROUTER: f32 logits
   int64_t ldo;              // output row stride in elements
   const float* bias;        // EPI_ROUTER: per-column bias or NULL
   float* extra_out;         // EPI_ROUTER: x . b_extra per row, when b_extra != NULL
@@ -99,8 +100,9 @@ hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int
                            int* zero_ints = nullptr, int n_zero = 0);
 
 // ---------------------------------------------------------------- combine
-hipError_t launch_combine(const float* y, const int32_t* inv, const float* w,
-                          const float* shared, const float* shared_gate_logit,
+// y [P,H] and shared [T,H] (or NULL) are bf16 when y_bf16, else fp32.
+hipError_t launch_combine(const void* y, int y_bf16, const int32_t* inv, const float* w,
+                          const void* shared, const float* shared_gate_logit,
                           int T, int H, int k, int out_bf16, void* out, hipStream_t s);
 
 }  // namespace moe

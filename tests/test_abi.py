@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     for code, text in [(0, b"MOE_OK"), (1, b"MOE_ERR_INVALID_ARG"), (2, b"MOE_ERR_UNSUPPORTED"),
                        (3, b"MOE_ERR_WORKSPACE"), (4, b"MOE_ERR_HIP")]:
         assert lib.moe_status_string(code) == text
@@ -91,12 +91,18 @@ def test_dispatch_validation(lib):
     assert dispatch(lib, T=0) == OK
 
 
-def ffn(lib, T=4, H=64, E=8, k=2, I=64, dtype=BF16, gather=P16, off=P16, ws=P16, wsb=1 << 24):
-    return lib.moe_grouped_ffn(P16, gather, off, P16, P16, T, H, E, k, I, dtype, P16, ws, wsb, NULL)
+def ffn(lib, T=4, H=64, E=8, k=2, I=64, dtype=BF16, ydt=F32, gather=P16, off=P16, ws=P16, wsb=1 << 24):
+    return lib.moe_grouped_ffn(P16, gather, off, P16, P16, T, H, E, k, I, dtype, ydt, P16, ws, wsb, NULL)
 
 
 def test_grouped_ffn_validation(lib):
     assert ffn(lib, I=96) == UNSUP
+    assert ffn(lib, ydt=3) == INVALID and "expert_out_dtype" in last(lib)
+    assert ffn(lib, dtype=F32, ydt=BF16) == UNSUP and "bf16 layer" in last(lib)
+    # fp32 expert outputs past 2 GiB would overflow the 32-bit store offsets;
+    # the same rows in bf16 fit
+    assert ffn(lib, T=65536, H=4096, k=2, ydt=F32, wsb=1) == UNSUP and "2 GiB" in last(lib)
+    assert ffn(lib, T=65536, H=4096, k=2, ydt=BF16, wsb=1) == WS
     assert ffn(lib, off=NULL) == INVALID and "expert_offsets" in last(lib)
     assert ffn(lib, gather=NULL) == INVALID and "packed_token_indices" in last(lib)
     need = lib.moe_grouped_ffn_workspace_size(4, 64, 2, 8, 64, BF16)
@@ -133,13 +139,14 @@ def test_grouped_ffn_valid_f32_shape_is_not_rejected_for_size(lib):
     assert ffn(lib, I=48, dtype=F32, wsb=1) == WS
 
 
-def combine(lib, T=4, H=64, k=2, out_dtype=F32, shared=NULL, gl=NULL, out=P16):
-    return lib.moe_combine(P16, P16, P16, shared, gl, T, H, k, out_dtype, out, NULL)
+def combine(lib, T=4, H=64, k=2, ydt=F32, out_dtype=F32, shared=NULL, gl=NULL, out=P16):
+    return lib.moe_combine(P16, P16, P16, shared, gl, T, H, k, ydt, out_dtype, out, NULL)
 
 
 def test_combine_validation(lib):
     assert combine(lib, H=60) == UNSUP
     assert combine(lib, out_dtype=3) == INVALID
+    assert combine(lib, ydt=3) == INVALID and "expert_dtype" in last(lib)
     assert combine(lib, gl=P16) == INVALID
     assert combine(lib, out=NULL) == INVALID and last(lib) == "output is NULL"
     assert combine(lib, out=BAD) == UNSUP

@@ -143,6 +143,23 @@ def test_small_staged_and_end_to_end(name):
     err_c, rms_c = rel_max_err(out_c.cpu().numpy().astype(np.float64), ref_c)
     assert err_c <= 1e-5 * rms_c + 1e-30
 
+    if cfg.dtype == "bf16":
+        # bf16 expert outputs: the same fp32 sums (same tiles, same K order),
+        # each rounded once to nearest even
+        yb = rdg.moe_grouped_ffn(dev["x"], g["packed_ids"], g["offsets"], dev["w13"], dev["w2"], cfg.top_k,
+                                 out_dtype=torch.bfloat16)
+        assert yb.dtype == torch.bfloat16
+        assert torch.equal(yb.view(torch.int16), y.to(torch.bfloat16).view(torch.int16))
+        # against the oracle: the fp32 result's error plus at most half a bf16
+        # ulp (2^-8 relative) per element
+        y32 = y.cpu().numpy().astype(np.float64)
+        yb64 = yb.float().cpu().numpy().astype(np.float64)
+        assert (np.abs(yb64 - y_ref) <= np.abs(y32 - y_ref) + 2.0 ** -8 * np.abs(y32) + 1e-30).all()
+        out_b = rdg.moe_combine(yb, g["inv"], to_device(w_o))
+        ref_b = oracle.combine(yb.float().cpu().numpy().astype(np.float64), plan_o["inv"], w_o.astype(np.float64))
+        err_b, rms_b = rel_max_err(out_b.cpu().numpy().astype(np.float64), ref_b)
+        assert err_b <= 1e-5 * rms_b + 1e-30
+
     # end to end
     f = gpu_forward(cfg, dev)
     ids_f = f["topk_ids"].cpu().numpy()
@@ -328,28 +345,39 @@ def test_no_renormalize():
     assert err <= 2e-2 * rms
 
 
-@pytest.mark.parametrize("T,H,k", [(5, 4160, 2), (9, 24, 10), (3, 8, 1), (17, 1032, 9)])
-def test_combine_shapes(T, H, k):
+@pytest.mark.parametrize("ydt", ["f32", "bf16"])
+@pytest.mark.parametrize("T,H,k", [(5, 4160, 2), (9, 24, 10), (3, 8, 1), (17, 1032, 9), (4, 4096, 3)])
+def test_combine_shapes(T, H, k, ydt):
     """Combine over row widths that need several column passes (H = 4160),
     partial column groups (H = 24, 8, 1032) and more slots than one gather pass
-    holds (k = 9, 10), with and without the gated shared term."""
-    log(f"[parity] combine T={T} H={H} k={k}")
+    holds (k = 9, 10), with and without the gated shared term; expert outputs
+    in fp32 or bf16 (bf16 values enter the fp32 sums exactly)."""
+    log(f"[parity] combine T={T} H={H} k={k} y={ydt}")
     rng = np.random.default_rng(T * 1000 + H + k)
     P = T * k
     y = rng.standard_normal((P, H)).astype(np.float32)
+    shared = rng.standard_normal((T, H)).astype(np.float32)
+    if ydt == "bf16":
+        # values exactly representable in bf16, so the oracle sees what the GPU reads
+        y = torch.from_numpy(y).to(torch.bfloat16).float().numpy()
+        shared = torch.from_numpy(shared).to(torch.bfloat16).float().numpy()
+    tdt = torch.bfloat16 if ydt == "bf16" else torch.float32
+
+    def dev_y(a):
+        return torch.from_numpy(a).to(tdt).cuda()
+
     perm = rng.permutation(P).astype(np.int32)
     inv = np.empty(P, dtype=np.int32)
     inv[perm] = np.arange(P, dtype=np.int32)
     w = rng.random((T, k)).astype(np.float32)
-    shared = rng.standard_normal((T, H)).astype(np.float32)
     gl = rng.standard_normal(T).astype(np.float32)
     ref = oracle.combine(y.astype(np.float64), inv, w.astype(np.float64))
-    out = rdg.moe_combine(to_device(y), to_device(inv), to_device(w)).cpu().numpy().astype(np.float64)
+    out = rdg.moe_combine(dev_y(y), to_device(inv), to_device(w)).cpu().numpy().astype(np.float64)
     err, rms = rel_max_err(out, ref)
     assert err <= 1e-5 * rms + 1e-30
     sig = 1.0 / (1.0 + np.exp(-gl.astype(np.float64)))
     ref_s = ref + sig[:, None] * shared.astype(np.float64)
-    out_s = rdg.moe_combine(to_device(y), to_device(inv), to_device(w), shared_output=to_device(shared),
+    out_s = rdg.moe_combine(dev_y(y), to_device(inv), to_device(w), shared_output=dev_y(shared),
                             shared_gate_logit=to_device(gl)).cpu().numpy().astype(np.float64)
     err_s, rms_s = rel_max_err(out_s, ref_s)
     assert err_s <= 1e-5 * rms_s + 1e-30
