@@ -167,9 +167,10 @@ moe::GemmArgs gemm_args() {
   return a;
 }
 
+// Router logits, then (with_topk) the top-k ids and weights.
 hipError_t run_router(const void* x, const void* wr, const float* bias, const void* gate, int T, int H, int E, int k,
                       int renorm, int dtype, float* logits, float* probs, int32_t* ids, float* weights,
-                      float* gate_logit, hipStream_t s) {
+                      float* gate_logit, hipStream_t s, bool with_topk = true) {
   hipError_t e;
   if (dtype == MOE_DTYPE_BF16 && T <= moe::kRouterSmallT) {
     e = moe::launch_router_small_t_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr), bias,
@@ -194,7 +195,7 @@ hipError_t run_router(const void* x, const void* wr, const float* bias, const vo
     e = moe::launch_router_logits_f32(static_cast<const float*>(x), static_cast<const float*>(wr), bias,
                                       static_cast<const float*>(gate), T, H, E, logits, gate_logit, s);
   }
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !with_topk) return e;
   return moe::launch_topk(logits, T, E, k, renorm, ids, weights, probs, s);
 }
 
@@ -276,9 +277,13 @@ AuxStream* aux_stream() {
   AuxStream& a = g_aux[dev];
   if (!a.tried) {
     a.tried = true;
+    // The join only orders device work after device work (the shared
+    // expert's kernels before the combine), so it needs no system-scope
+    // fence; the fork keeps it, because the aux stream's first reads may
+    // follow a host-to-device copy on the caller's stream.
     a.ok = hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking) == hipSuccess &&
            hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) == hipSuccess &&
-           hipEventCreateWithFlags(&a.join, hipEventDisableTiming) == hipSuccess;
+           hipEventCreateWithFlags(&a.join, hipEventDisableTiming | hipEventDisableSystemFence) == hipSuccess;
   }
   return a.ok ? &a : nullptr;
 }
@@ -590,22 +595,38 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipError_t e = hipSuccess;
-  // The shared expert depends only on the input: it starts first, on the aux
-  // stream, so that its weight streaming overlaps the router, top-k and
+  // The shared expert depends only on the input: the aux stream forks before
+  // the router, so that its weight streaming overlaps the router, top-k and
   // dispatch (small launches that leave most of the chip idle) and then the
-  // routed experts; the join comes before the combine.
+  // routed experts; the join comes before the combine.  The routing launches
+  // are enqueued first, so that the host's launch latency delays the shared
+  // expert rather than the critical path.
   std::unique_lock<std::mutex> aux_lock(g_aux_mu, std::defer_lock);
   AuxStream* aux = nullptr;
   if (Is) {
     aux_lock.lock();
     aux = aux_stream();
-    hipStream_t ss = s;
     if (aux != nullptr) {
       e = hipEventRecord(aux->fork, s);
       if (e == hipSuccess) e = hipStreamWaitEvent(aux->stream, aux->fork, 0);
       if (e != hipSuccess) return hip_status(e, "moe_forward(fork)");
-      ss = aux->stream;
     }
+  }
+  // decode batches: top-k and the plan in one single-workgroup launch
+  const bool small = T <= moe::kTopkDispatchSmallT && P <= moe::kDispatchSmallP;
+  e = run_router(hidden_states, router_weight, router_bias, Is ? shared_gate : nullptr, T, H, E, k,
+                 renormalize ? 1 : 0, dtype, logits, nullptr, ids, weights, Is ? L.gate_logit : nullptr, s, !small);
+  if (e != hipSuccess) return hip_status(e, "moe_forward(router)");
+  // the dispatch also zeroes the tile counters of the routed GEMMs
+  if (small)
+    e = moe::launch_topk_dispatch_small(logits, T, E, k, renormalize ? 1 : 0, ids, weights, L.counts, L.offsets,
+                                        L.perm, L.inv, L.packed_ids, s, L.counters, 2 * moe::kTileCounterInts);
+  else
+    e = moe::launch_dispatch(ids, nullptr, T, k, E, L.counts, L.offsets, L.perm, L.inv, L.packed_ids, nullptr,
+                             L.dispatch_scratch, s, L.counters, 2 * moe::kTileCounterInts);
+  if (e != hipSuccess) return hip_status(e, "moe_forward(dispatch)");
+  if (Is) {
+    hipStream_t ss = aux != nullptr ? aux->stream : s;
     int* shared_counters = L.counters + 2 * moe::kTileCounterInts;
     if (dtype == MOE_DTYPE_BF16) {
       moe::GemmArgs probe = gemm_args();
@@ -624,13 +645,6 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
       if (e != hipSuccess) return hip_status(e, "moe_forward(join)");
     }
   }
-  e = run_router(hidden_states, router_weight, router_bias, Is ? shared_gate : nullptr, T, H, E, k,
-                 renormalize ? 1 : 0, dtype, logits, nullptr, ids, weights, Is ? L.gate_logit : nullptr, s);
-  if (e != hipSuccess) return hip_status(e, "moe_forward(router)");
-  // the dispatch scan also zeroes the tile counters of the routed GEMMs
-  e = moe::launch_dispatch(ids, nullptr, T, k, E, L.counts, L.offsets, L.perm, L.inv, L.packed_ids, nullptr,
-                           L.dispatch_scratch, s, L.counters, 2 * moe::kTileCounterInts);
-  if (e != hipSuccess) return hip_status(e, "moe_forward(dispatch)");
   e = run_ffn(hidden_states, L.packed_ids, L.offsets, w13, w2, T, P, H, E, I, dtype, L.h, L.y, MOE_DTYPE_F32, s,
               false, L.counters, L.partial);
   if (e != hipSuccess) return hip_status(e, "moe_forward(experts)");

@@ -21,6 +21,7 @@
 //              position p.  Equal ids therefore keep index order (stability),
 //              and no position depends on the timing of atomics.
 #include "moe_internal.h"
+#include "topk_wave.h"
 
 namespace moe {
 namespace {
@@ -178,14 +179,11 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 // the assignments, C = ceil(P / 16).
 constexpr int kSmallWaves = 16;
 
-__global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __restrict__ ids,
-                                                              const float* __restrict__ wts, int P, int k, int E,
-                                                              int32_t* __restrict__ counts,
-                                                              int32_t* __restrict__ offsets,
-                                                              int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-                                                              int32_t* __restrict__ packed_ids,
-                                                              float* __restrict__ packed_w, int* zero_ints,
-                                                              int n_zero) {
+__device__ __forceinline__ void dispatch_small_body(const int32_t* __restrict__ ids, const float* __restrict__ wts,
+                                                    int P, int k, int E, int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                                    int32_t* __restrict__ inv, int32_t* __restrict__ packed_ids,
+                                                    float* __restrict__ packed_w, int* zero_ints, int n_zero) {
   __shared__ int cnt[kSmallWaves][kMaxE];  // per-wave counts, then per-wave running positions
   __shared__ int wsum[kSmallWaves];
   const int tid = threadIdx.x;
@@ -258,7 +256,68 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
   }
 }
 
+
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __restrict__ ids,
+                                                              const float* __restrict__ wts, int P, int k, int E,
+                                                              int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                                              int32_t* __restrict__ packed_ids,
+                                                              float* __restrict__ packed_w, int* zero_ints,
+                                                              int n_zero) {
+  dispatch_small_body(ids, wts, P, k, E, counts, offsets, perm, inv, packed_ids, packed_w, zero_ints, n_zero);
+}
+
+// Decode batches: top-k of every token (one wave per token, the same
+// wave-level selection and weights as the router's top-k kernel, so the ids
+// and weights are identical bit for bit), then, after a workgroup barrier,
+// the whole plan as in dispatch_small_kernel, reading the ids from LDS.
+// One launch instead of two on the latency-bound path from the logits to the
+// expert GEMMs.
+template <int VPL>
+__global__ __launch_bounds__(1024) void topk_dispatch_small_kernel(const float* __restrict__ logits, int T, int E,
+                                                                   int k, int renorm, int32_t* __restrict__ ids,
+                                                                   float* __restrict__ weights,
+                                                                   int32_t* __restrict__ counts,
+                                                                   int32_t* __restrict__ offsets,
+                                                                   int32_t* __restrict__ perm,
+                                                                   int32_t* __restrict__ inv,
+                                                                   int32_t* __restrict__ packed_ids, int* zero_ints,
+                                                                   int n_zero) {
+  // the ids also go to LDS, where the plan reads them (no global round trip)
+  __shared__ int32_t s_ids[kDispatchSmallP];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  for (int t = w; t < T; t += kSmallWaves)
+    topk_row<VPL>(logits + (int64_t)t * E, E, k, renorm, ids + (int64_t)t * k, weights + (int64_t)t * k, nullptr,
+                  lane, s_ids + t * k);
+  __syncthreads();
+  dispatch_small_body(s_ids, nullptr, T * k, k, E, counts, offsets, perm, inv, packed_ids, nullptr, zero_ints,
+                      n_zero);
+}
+
 }  // namespace
+
+hipError_t launch_topk_dispatch_small(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
+                                      float* weights, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                      int32_t* packed_ids, hipStream_t s, int* zero_ints, int n_zero) {
+  if (T == 0) return hipSuccess;
+  profile_begin("topk_dispatch_small", s);
+  if (E <= 64)
+    hipLaunchKernelGGL(topk_dispatch_small_kernel<1>, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, ids,
+                       weights, counts, offsets, perm, inv, packed_ids, zero_ints, n_zero);
+  else if (E <= 128)
+    hipLaunchKernelGGL(topk_dispatch_small_kernel<2>, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, ids,
+                       weights, counts, offsets, perm, inv, packed_ids, zero_ints, n_zero);
+  else if (E <= 256)
+    hipLaunchKernelGGL(topk_dispatch_small_kernel<4>, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, ids,
+                       weights, counts, offsets, perm, inv, packed_ids, zero_ints, n_zero);
+  else
+    hipLaunchKernelGGL(topk_dispatch_small_kernel<8>, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, ids,
+                       weights, counts, offsets, perm, inv, packed_ids, zero_ints, n_zero);
+  profile_end(s);
+  return hipGetLastError();
+}
 
 size_t dispatch_scratch_bytes(int64_t P, int64_t E) {
   const int64_t U = (P + kSeg - 1) / kSeg;

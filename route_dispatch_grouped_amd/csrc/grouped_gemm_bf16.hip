@@ -482,6 +482,310 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
 }
 
 // ---------------------------------------------------------------------------
+// Streaming variant for groups of at most 16 rows on average (decode
+// batches).  There the GEMM is a pure weight stream, so the tile is shaped for
+// HBM rather than for operand reuse:
+//   * a tile is BM rows x 64 weight rows (EPI_SWIGLU: 32 gate rows and the
+//     matching 32 up rows, 32 h columns; otherwise 64 output columns), and a
+//     stage covers 256 k, i.e. 512 contiguous bytes of every row.  A read-only
+//     probe of the two orders on MI355X: 128-byte pieces of 256 rows per stage
+//     (the large-tile kernels' K walk) stream HBM at about 4.1 TB/s with one
+//     workgroup per CU, 512-byte pieces of 64 rows at about 6.1 TB/s, the rate
+//     of a contiguous read.
+//   * wave w owns weight rows 16w..16w+15 of the tile.  With EPI_SWIGLU those
+//     are 8 gate rows and the same 8 up rows, so a 16x16 accumulator holds
+//     gate in its columns 0-7 and up in columns 8-15; one lane exchange pairs
+//     them for the SwiGLU epilogue.
+//   * each workgroup runs through its units (tile, K chunk) as one software
+//     pipeline over a 3-stage ring: the DMA of sequence stage g + 2 is issued
+//     while stage g is computed, across unit boundaries, so the stream never
+//     drains between tiles.
+//   * vmcnt: every stage is exactly SD DMA instructions per wave and every
+//     epilogue exactly SS stores per wave (masked lanes store through an
+//     offset past the buffer, which the hardware drops), so each wait is an
+//     exact count of what was issued after the stage it needs.
+//   * LDS: row r of a stage holds 32 chunks of 16 bytes, chunk c at position
+//     c ^ (r & 15); the fragment reads (16 rows, one chunk column) then touch
+//     16 distinct 4-bank groups.
+//   * K need not be a multiple of 256: chunks past the end of a row are
+//     fetched through an offset past the buffer (zeros).
+//   * the gathered row indices are staged in LDS up front, so that building
+//     the DMA plan of the next unit issues no vector load (which would make
+//     the compiler wait for every DMA in flight).
+constexpr int kStreamBR = 64;          // weight rows per tile
+constexpr int kStreamCH = 32;          // 16-byte chunks per row per stage (256 k)
+constexpr int kStreamNS = 3;           // ring depth
+
+template <int BM>
+struct StreamTile {
+  static constexpr int MSUB = BM / 16;
+  static constexpr int SLOTS = (BM + kStreamBR) * kStreamCH;  // 16-byte slots per stage
+  static constexpr int A_PER = BM * kStreamCH / 64 / 4;       // DMA instructions per wave (A rows)
+  static constexpr int B_PER = kStreamBR * kStreamCH / 64 / 4;
+  static constexpr int SD = A_PER + B_PER;                    // per wave per stage
+  static constexpr int SS = 4 * MSUB;                         // epilogue stores per wave
+  // packed rows whose gathered indices fit in LDS next to the ring
+  static constexpr int MAX_ROWS = (BM == 16) ? 8192 : 2048;
+  static_assert(SD + 2 * SS < 64, "vmcnt");
+};
+
+struct StreamUnit {
+  int g, m0, rows, n0, kc, KT;
+};
+
+template <int BM>
+struct StreamPlan {
+  uint32_t a_off[StreamTile<BM>::A_PER];
+  uint32_t b_off[StreamTile<BM>::B_PER];
+  uint32_t a_cb[StreamTile<BM>::A_PER];  // byte offset of the lane's chunk inside a stage row
+  uint32_t b_cb[StreamTile<BM>::B_PER];
+  u32x4_t rb;
+};
+
+template <int BM, int EPI>
+__device__ __forceinline__ StreamUnit stream_unit(int t, int total_mn, int nblk, int G, const int* s_tb,
+                                                  const int* s_off, int KTc, int KT_all) {
+  constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? kStreamBR / 2 : kStreamBR;
+  StreamUnit u;
+  u.kc = __builtin_amdgcn_readfirstlane(t / total_mn);
+  const TileCoord tc = tile_coord<BM>(t - u.kc * total_mn, nblk, G, s_tb, s_off);
+  u.g = tc.g;
+  u.m0 = tc.m0;
+  u.rows = tc.rows;
+  u.n0 = tc.nb * BN_OUT;
+  u.KT = __builtin_amdgcn_readfirstlane(min(KTc, KT_all - u.kc * KTc));
+  return u;
+}
+
+template <int BM, int EPI>
+__device__ __forceinline__ void stream_plan(StreamPlan<BM>& d, const GemmArgs& p, const int* s_gidx,
+                                            const StreamUnit& u, int wave, int lane, uint32_t row_bytes) {
+  using C = StreamTile<BM>;
+#pragma unroll
+  for (int qi = 0; qi < C::A_PER; ++qi) {
+    const int r = 2 * (qi * 4 + wave) + (lane >> 5);  // A row of the tile
+    const int c = (lane & 31) ^ (r & 15);
+    d.a_cb[qi] = (uint32_t)c * 16u;
+    if (r < u.rows) {
+      const int grow = p.gather ? s_gidx[u.m0 + r] : (u.m0 + r);
+      d.a_off[qi] = (uint32_t)grow * row_bytes + (uint32_t)c * 16u;
+    } else {
+      d.a_off[qi] = 0x80000000u;
+    }
+  }
+#pragma unroll
+  for (int qi = 0; qi < C::B_PER; ++qi) {
+    const int rb = 2 * (qi * 4 + wave) + (lane >> 5);  // weight row of the tile
+    const int c = (lane & 31) ^ (rb & 15);
+    d.b_cb[qi] = (uint32_t)c * 16u;
+    int col, wr;
+    if (EPI == EPI_SWIGLU) {
+      col = u.n0 + 8 * (rb >> 4) + (rb & 7);
+      wr = (rb & 8) ? p.up_row0 + col : col;
+    } else {
+      col = u.n0 + rb;
+      wr = col;
+    }
+    d.b_off[qi] = (col < p.N) ? (uint32_t)wr * row_bytes + (uint32_t)c * 16u : 0x80000000u;
+  }
+  const int b_rows_total = (EPI == EPI_SWIGLU) ? 2 * p.up_row0 : p.N;
+  d.rb = make_rsrc(p.B + (int64_t)u.g * p.b_group_stride, (uint32_t)b_rows_total * row_bytes);
+}
+
+template <int BM>
+__device__ __forceinline__ void stream_issue(u32x4_t* buf, const StreamPlan<BM>& d, u32x4_t ra, int wave, int kbytes,
+                                             uint32_t row_bytes, bool ktail) {
+  using C = StreamTile<BM>;
+#pragma unroll
+  for (int qi = 0; qi < C::A_PER; ++qi) {
+    uint32_t v = d.a_off[qi];
+    if (ktail && d.a_cb[qi] + (uint32_t)kbytes >= row_bytes) v = 0x80000000u;
+    dma16(buf + (qi * 4 + wave) * 64, ra, v, kbytes);
+  }
+#pragma unroll
+  for (int qi = 0; qi < C::B_PER; ++qi) {
+    uint32_t v = d.b_off[qi];
+    if (ktail && d.b_cb[qi] + (uint32_t)kbytes >= row_bytes) v = 0x80000000u;
+    dma16(buf + BM * kStreamCH + (qi * 4 + wave) * 64, d.rb, v, kbytes);
+  }
+}
+
+template <int BM, int LIVE>
+__device__ __forceinline__ void stream_mma(f32x4_t (&acc)[BM / 16], const u32x4_t* __restrict__ buf, int wave,
+                                           int lane) {
+#pragma unroll
+  for (int kk = 0; kk < kStreamCH / 4; ++kk) {
+    const int pos = (kk * 4 + (lane >> 4)) ^ (lane & 15);
+    const bf16x8_t b =
+        __builtin_bit_cast(bf16x8_t, buf[(BM + 16 * wave + (lane & 15)) * kStreamCH + pos]);
+#pragma unroll
+    for (int i = 0; i < LIVE; ++i) {
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, buf[(16 * i + (lane & 15)) * kStreamCH + pos]);
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
+    }
+  }
+}
+
+template <int BM, int EPI>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_stream_kernel(GemmArgs p) {
+  using C = StreamTile<BM>;
+  constexpr int MSUB = C::MSUB;
+  constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? kStreamBR / 2 : kStreamBR;
+  static_assert(EPI != EPI_ROUTER, "the router has its own kernels");
+
+  __shared__ u32x4_t ring[kStreamNS * C::SLOTS];
+  __shared__ int s_off[kMaxGroups + 1];
+  __shared__ int s_tb[kMaxGroups + 1];
+  __shared__ int s_wsum[kThreads / 64];
+  __shared__ int s_gidx[C::MAX_ROWS];  // the host keeps M <= MAX_ROWS
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = p.G;
+  if (p.gather)
+    for (int i = tid; i < p.M; i += kThreads) s_gidx[i] = p.gather[i];
+  build_schedule<BM>(p, s_off, s_tb, s_wsum, tid, lane, wave);  // ends with a barrier
+
+  const int nblk = (p.N + BN_OUT - 1) / BN_OUT;
+  const int ksplit = (p.partial != nullptr && p.ksplit > 1) ? p.ksplit : 1;
+  const int total_mn = s_tb[G] * nblk;
+  const int total = total_mn * ksplit;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int nslots = gridDim.x / kXcds;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int t_end = min(total, xcd * per + per);
+  const uint32_t row_bytes = (uint32_t)p.K * 2u;
+  const int KT_all = (p.K + 8 * kStreamCH - 1) / (8 * kStreamCH);
+  const int KTc = (KT_all + ksplit - 1) / ksplit;
+  const bool ktail = (p.K % (8 * kStreamCH)) != 0;
+  constexpr int kStageBytes = kStreamCH * 16;
+
+  int t_dma = xcd * per + slot;
+  if (t_dma >= t_end) return;
+  int t_cmp = t_dma;
+
+  const u32x4_t ra = make_rsrc(p.A, (uint32_t)p.a_rows * row_bytes);
+  // output: the fp32 partial planes of a split K, else y / h
+  const int ldp = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;
+  const size_t out_bytes = (ksplit > 1) ? (size_t)ksplit * p.M * ldp * 4
+                                        : (size_t)p.M * p.ldo * ((EPI == EPI_F32) ? 4 : 2);
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+      (ksplit > 1) ? static_cast<void*>(p.partial) : p.out, (short)0, (int)out_bytes, kBufferWord3);
+
+  // DMA side: unit t_dma, its next stage kt_dma, its plan
+  StreamUnit ud = stream_unit<BM, EPI>(t_dma, total_mn, nblk, G, s_tb, s_off, KTc, KT_all);
+  StreamPlan<BM> dp;
+  stream_plan<BM, EPI>(dp, p, s_gidx, ud, wave, lane, row_bytes);
+  int kt_dma = 0;
+  bool dma_live = true;
+  int dma_slot = 0;
+  int issued = 0;  // stages issued so far (sequence numbers 0 .. issued-1)
+
+  auto issue_next = [&]() {
+    stream_issue<BM>(ring + dma_slot * C::SLOTS, dp, ra, wave, (ud.kc * KTc + kt_dma) * kStageBytes, row_bytes,
+                     ktail);
+    ++issued;
+    dma_slot = (dma_slot + 1 == kStreamNS) ? 0 : dma_slot + 1;
+    if (++kt_dma == ud.KT) {
+      kt_dma = 0;
+      t_dma += nslots;
+      dma_live = t_dma < t_end;
+      if (dma_live) {
+        ud = stream_unit<BM, EPI>(t_dma, total_mn, nblk, G, s_tb, s_off, KTc, KT_all);
+        stream_plan<BM, EPI>(dp, p, s_gidx, ud, wave, lane, row_bytes);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < kStreamNS - 1; ++s)
+    if (dma_live) issue_next();
+
+  StreamUnit uc = stream_unit<BM, EPI>(t_cmp, total_mn, nblk, G, s_tb, s_off, KTc, KT_all);
+  int kt_cmp = 0;
+  int cmp_slot = 0;
+  int seq = 0;
+  int ends = 0;  // epilogues of the last two iterations (issued after the stage being waited for)
+  f32x4_t acc[MSUB];
+#pragma unroll
+  for (int i = 0; i < MSUB; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  while (true) {
+    // wait for the DMA of stage `seq`: later stages and later epilogue stores may stay in flight
+    const int n_dma = issued - (seq + 1);  // 0 or 1
+    const int n_epi = (ends & 1) + (ends >> 1);
+    switch (n_dma * 3 + n_epi) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<C::SS>(); break;
+      case 2: wait_vmcnt<2 * C::SS>(); break;
+      case 3: wait_vmcnt<C::SD>(); break;
+      case 4: wait_vmcnt<C::SD + C::SS>(); break;
+      default: wait_vmcnt<C::SD + 2 * C::SS>(); break;
+    }
+    lds_barrier();  // the stage is complete for every wave; the slot the next DMA overwrites is free
+    if (dma_live) issue_next();
+    const u32x4_t* buf = ring + cmp_slot * C::SLOTS;
+    const int live = (uc.rows + 15) >> 4;
+    if (MSUB == 1 || live >= MSUB) stream_mma<BM, MSUB>(acc, buf, wave, lane);
+    else stream_mma<BM, 1>(acc, buf, wave, lane);
+    cmp_slot = (cmp_slot + 1 == kStreamNS) ? 0 : cmp_slot + 1;
+    ++seq;
+    const bool end = ++kt_cmp == uc.KT;
+    if (end) {
+      // ---- epilogue: exactly SS stores per wave.  Lane: column (lane & 15)
+      // of the wave's 16 weight rows, rows 4 * (lane >> 4) + r of each sub-tile.
+      const int cl = lane & 15;
+#pragma unroll
+      for (int i = 0; i < MSUB; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * i + 4 * (lane >> 4) + r;
+          const bool row_ok = row < uc.rows;
+          const float v = acc[i][r];
+          if (EPI == EPI_SWIGLU) {
+            const float other = __shfl_xor(v, 8, 64);  // up for gate lanes, gate for up lanes
+            const int col = uc.n0 + 8 * wave + (cl & 7);
+            const bool ok = row_ok && col < p.N;
+            if (ksplit > 1) {
+              const int pc = (cl < 8) ? col : p.N + col;
+              const uint32_t off =
+                  ok ? (uint32_t)((((int64_t)uc.kc * p.M + uc.m0 + row) * ldp + pc) * 4) : 0x80000000u;
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ro, (int)off, 0, 0);
+            } else {
+              const uint32_t off =
+                  (ok && cl < 8) ? (uint32_t)(((int64_t)(uc.m0 + row) * p.ldo + col) * 2) : 0x80000000u;
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(silu_mul(v, other)), ro, (int)off, 0, 0);
+            }
+          } else {
+            const int col = uc.n0 + 16 * wave + cl;
+            const bool ok = row_ok && col < p.N;
+            if (ksplit > 1) {
+              const uint32_t off =
+                  ok ? (uint32_t)((((int64_t)uc.kc * p.M + uc.m0 + row) * ldp + col) * 4) : 0x80000000u;
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ro, (int)off, 0, 0);
+            } else if (EPI == EPI_BF16) {
+              const uint32_t off = ok ? (uint32_t)(((int64_t)(uc.m0 + row) * p.ldo + col) * 2) : 0x80000000u;
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), ro, (int)off, 0, 0);
+            } else {
+              const uint32_t off = ok ? (uint32_t)(((int64_t)(uc.m0 + row) * p.ldo + col) * 4) : 0x80000000u;
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ro, (int)off, 0, 0);
+            }
+          }
+        }
+        acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      t_cmp += nslots;
+      if (t_cmp >= t_end) break;
+      uc = stream_unit<BM, EPI>(t_cmp, total_mn, nblk, G, s_tb, s_off, KTc, KT_all);
+      kt_cmp = 0;
+    }
+    ends = ((ends << 1) | (end ? 1 : 0)) & 3;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Large-group variant (groups of hundreds of rows, e.g. prefill): 256 x 256
 // tiles, BK = 32 per stage, a 4-stage ring (32 KB per stage), 2 x 2 waves of
 // 128 x 128 computed with v_mfma_f32_32x32x16_bf16 (4 x 4 sub-tiles of 32 x 32;
@@ -1236,11 +1540,32 @@ int pick_bm(int64_t M, int64_t groups) {
 constexpr int64_t kSplitTarget = 256;
 constexpr int64_t kSplitMinStages = 8;
 
+// The streaming kernel (16-row groups, up to StreamTile<16>::MAX_ROWS packed
+// rows) pipelines its units, so it only needs about two units per CU, each
+// at least kStreamMinStages stages of 256 k.
+constexpr int64_t kStreamSplitTarget = 512;
+constexpr int64_t kStreamMinStages = 2;
+
+bool uses_stream(int64_t M, int64_t groups) { return pick_bm(M, groups) == 16 && M <= StreamTile<16>::MAX_ROWS; }
+
 int ksplit_for(int64_t M, int64_t G, bool grouped, int64_t N, int64_t K, GemmEpilogue epi) {
   if (epi == EPI_ROUTER || M <= 0) return 1;
   const int64_t groups = grouped ? (G < M ? G : M) : 1;
   const int bm = pick_bm(M, groups);
   if (bm == 0) return 1;
+  if (uses_stream(M, groups)) {
+    const int64_t bn = (epi == EPI_SWIGLU) ? kStreamBR / 2 : kStreamBR;
+    const int64_t tiles = ((M + 15) / 16 + (grouped ? groups : 0)) * ((N + bn - 1) / bn);
+    const int64_t KT = (K + 8 * kStreamCH - 1) / (8 * kStreamCH);
+    int64_t ks = (kStreamSplitTarget + tiles - 1) / tiles;
+    if (ks > KT / kStreamMinStages) ks = KT / kStreamMinStages;
+    if (ks <= 1) return 1;
+    const int64_t ktc = (KT + ks - 1) / ks;
+    ks = (KT + ktc - 1) / ktc;
+    const int64_t ldp = (epi == EPI_SWIGLU) ? 2 * N : N;
+    if (ks * M * ldp * 4 > ((int64_t)1 << 31) - 1) return 1;  // 32-bit store offsets
+    return (int)ks;
+  }
   const int64_t bn = (epi == EPI_SWIGLU) ? 128 : 256;
   const int64_t tiles = ((M + bm - 1) / bm + (grouped ? groups : 0)) * ((N + bn - 1) / bn);
   const int64_t KT = K / BK;
@@ -1267,6 +1592,45 @@ hipError_t launch_bm(const GemmArgs& a_in, hipStream_t s, const char* name) {
   profile_begin(name, s);
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, EPI, BR>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   if (EPI != EPI_ROUTER && a.ksplit > 1) {
+    const int64_t n = (int64_t)a.M * (a.N / 4);
+    hipLaunchKernelGGL((splitk_reduce_kernel<EPI>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.partial,
+                       a.ksplit, a.M, a.N, a.out, a.ldo);
+  }
+  profile_end(s);
+  return hipGetLastError();
+}
+
+template <int BM, int EPI>
+int resident_stream_per_cu() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grouped_gemm_bf16_stream_kernel<BM, EPI>, kThreads, 0) !=
+            hipSuccess || n < 1)
+      n = 1;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int BM, int EPI>
+hipError_t launch_stream(const GemmArgs& a_in, hipStream_t s, const char* name) {
+  constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? kStreamBR / 2 : kStreamBR;
+  GemmArgs a = a_in;
+  a.ksplit = (a.partial != nullptr) ? ksplit_for(a.M, a.G, a.offsets != nullptr, a.N, a.K, (GemmEpilogue)EPI) : 1;
+  const int64_t nblk = (a.N + BN_OUT - 1) / BN_OUT;
+  int64_t ub_m = (a.M + BM - 1) / BM;
+  if (a.offsets) ub_m += (a.G < a.M ? a.G : a.M);
+  const int64_t ub = ub_m * nblk * a.ksplit;
+  int64_t grid = (int64_t)device_cu_count() * resident_stream_per_cu<BM, EPI>();
+  if (ub < grid) grid = ub;
+  grid = ((grid + kXcds - 1) / kXcds) * kXcds;
+  if (grid < kXcds) grid = kXcds;
+  profile_begin(name, s);
+  hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<BM, EPI>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  if (a.ksplit > 1) {
     const int64_t n = (int64_t)a.M * (a.N / 4);
     hipLaunchKernelGGL((splitk_reduce_kernel<EPI>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.partial,
                        a.ksplit, a.M, a.N, a.out, a.ldo);
@@ -1328,6 +1692,7 @@ template <int EPI>
 hipError_t launch_epi(const GemmArgs& a, hipStream_t s, const char* name) {
   // rows per group on average decides the m-tile height
   const int64_t groups = a.offsets ? (a.G < a.M ? a.G : a.M) : 1;
+  if (uses_stream(a.M, groups)) return launch_stream<16, EPI>(a, s, name);
   switch (pick_bm(a.M, groups)) {
     case 16: return launch_bm<16, EPI>(a, s, name);
     case 32: return launch_bm<32, EPI>(a, s, name);

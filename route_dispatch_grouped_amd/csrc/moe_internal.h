@@ -99,6 +99,14 @@ hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int
                            int32_t* packed_ids, float* packed_w, void* scratch, hipStream_t s,
                            int* zero_ints = nullptr, int n_zero = 0);
 
+// Top-k of T <= kTopkDispatchSmallT tokens fused with the one-workgroup plan
+// (T*k <= kDispatchSmallP): the same ids, weights and plan as launch_topk
+// followed by launch_dispatch.
+constexpr int kTopkDispatchSmallT = 64;
+hipError_t launch_topk_dispatch_small(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
+                                      float* weights, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                      int32_t* packed_ids, hipStream_t s, int* zero_ints, int n_zero);
+
 // ---------------------------------------------------------------- combine
 // y [P,H] and shared [T,H] (or NULL) are bf16 when y_bf16, else fp32.
 hipError_t launch_combine(const void* y, int y_bf16, const int32_t* inv, const float* w,

@@ -72,16 +72,20 @@ __global__ __launch_bounds__(256) void router_small_t_bf16_kernel(const uint16_t
 #pragma unroll
   for (int tt = 0; tt < kSmallT; ++tt) acc[tt] = 0.f;
   for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
+    // every load of the pass is issued before the first FMA (rows past the
+    // batch re-read its last row and are never stored)
+    uint4 xv[kSmallT];
+#pragma unroll
+    for (int tt = 0; tt < kSmallT; ++tt)
+      xv[tt] = *reinterpret_cast<const uint4*>(x + (int64_t)(t0 + min(tt, nt - 1)) * H + h);
     float wf[8];
     bf16x8_to_f32(*reinterpret_cast<const uint4*>(w + h), wf);
 #pragma unroll
     for (int tt = 0; tt < kSmallT; ++tt) {
-      if (tt < nt) {
-        float xf[8];
-        bf16x8_to_f32(*reinterpret_cast<const uint4*>(x + (int64_t)(t0 + tt) * H + h), xf);
+      float xf[8];
+      bf16x8_to_f32(xv[tt], xf);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[tt] = fmaf(xf[c], wf[c], acc[tt]);
-      }
+      for (int c = 0; c < 8; ++c) acc[tt] = fmaf(xf[c], wf[c], acc[tt]);
     }
   }
   __shared__ float red[4][kSmallT];

@@ -82,7 +82,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 // all E terms (the plain softmax probability).
 template <int VPL>
 __device__ __forceinline__ void topk_row(const float* row, int E, int k, int renorm, int32_t* __restrict__ ids,
-                                         float* __restrict__ weights, float* __restrict__ probs, int lane) {
+                                         float* __restrict__ weights, float* __restrict__ probs, int lane,
+                                         int32_t* ids_copy = nullptr) {
   float v[VPL];
   uint32_t key[VPL];
   uint32_t avail = 0;
@@ -143,6 +144,7 @@ __device__ __forceinline__ void topk_row(const float* row, int E, int k, int ren
     const int j = 64 * c + lane;
     if (j < k) {
       ids[j] = my_id[c];
+      if (ids_copy != nullptr) ids_copy[j] = my_id[c];
       weights[j] = expf(my_val[c] - m) / denom;
     }
   }

@@ -114,18 +114,20 @@ def test_grouped_ffn_validation(lib):
 
 
 def test_grouped_ffn_workspace_with_split_k(lib):
-    # Qwen1.5-MoE decode shape: 64 rows over 60 experts.  Tile upper bounds:
-    # gate/up (4 + 60) * 11 = 704 and down (4 + 60) * 8 = 512 tiles, both at
-    # least the split target of 256: no split, no partial sums.
+    # Qwen1.5-MoE decode shape: 64 rows over 60 experts, so the streaming
+    # kernel (16-row groups; 32 h columns or 64 output columns per tile,
+    # 256 k per stage).  Tile upper bounds: gate/up (4 + 60) * 44 = 2816 and
+    # down (4 + 60) * 32 = 2048, both at least the split target of 512: no
+    # split, no partial sums.
     h = 64 * 1408 * 2
     assert lib.moe_grouped_ffn_workspace_size(16, 2048, 4, 60, 1408, BF16) == 256 + h
     # its shared expert (one ungrouped block of 16 rows, I = 5632): gate/up
-    # 1 * 44 tiles, K = 2048 (32 stages) -> ceil(256 / 44) = 6, at most 32 / 8 = 4
-    # chunks of 8 stages; down 1 * 8 tiles, K = 5632 (88 stages) -> 32, at most
-    # 11 chunks of 8 stages.  Partial sums: max(4 * 16 * 2 * 5632, 11 * 16 * 2048).
+    # 1 * 176 tiles, K = 2048 (8 stages) -> ceil(512 / 176) = 3 chunks (at
+    # most 8 / 2 = 4); down 1 * 32 tiles, K = 5632 (22 stages) -> 16, at most
+    # 11 chunks of 2 stages.  Partial sums: max(3 * 16 * 2 * 5632, 11 * 16 * 2048).
     need = lib.moe_grouped_ffn_workspace_size(16, 2048, 1, 1, 5632, BF16)
     hs = 16 * 5632 * 2
-    assert need == 256 + hs + max(4 * 16 * 2 * 5632, 11 * 16 * 2048) * 4
+    assert need == 256 + hs + max(3 * 16 * 2 * 5632, 11 * 16 * 2048) * 4
     # the f32 path never splits
     assert lib.moe_grouped_ffn_workspace_size(16, 2048, 4, 60, 1408, F32) == 256 + 64 * 1408 * 4
     # forward workspace grows by the larger of the routed and shared split scratch

@@ -165,6 +165,10 @@ def test_small_staged_and_end_to_end(name):
     ids_f = f["topk_ids"].cpu().numpy()
     w_f = f["topk_weights"].cpu().numpy().astype(np.float64)
     assert (f["logits"].cpu().numpy() == r["logits"].cpu().numpy()).all()
+    # the forward's top-k (fused with the plan for small batches) is the
+    # router's top-k bit for bit
+    assert (ids_f == r["topk_ids"].cpu().numpy()).all()
+    assert (f["topk_weights"].cpu().numpy().view(np.int32) == r["topk_weights"].cpu().numpy().view(np.int32)).all()
     tie = near_tie_tokens(L, max(eps, 1e-30), cfg.top_k)
     outside = np.setdiff1d(np.arange(cfg.num_tokens), tie)
     assert (ids_f[outside] == ids_o[outside]).all()
