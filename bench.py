@@ -40,6 +40,20 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def y_bytes_per_value(cfg):
+    """Bytes per packed expert output value as the layer forward stores them:
+    bf16 layers whose down projection runs on the pipelined 256-row kernel (at
+    least 96 rows per expert on average, I/32 a multiple of 4 and at least 8)
+    keep fp16 values plus one int32 exponent per 64 columns; otherwise fp32."""
+    P = cfg.num_tokens * cfg.top_k
+    groups = min(cfg.num_experts, P)
+    avg = (P + groups - 1) // groups
+    kt = cfg.intermediate_size // 32
+    if cfg.dtype == "bf16" and avg >= 96 and kt >= 8 and kt % 4 == 0:
+        return 2.0 + 4.0 / 64
+    return 4.0
+
+
 def kernel_work(name, cfg, touched, touched_shared=True):
     """Algorithmic FLOPs and HBM bytes of ONE launch of a library kernel.
 
@@ -49,12 +63,13 @@ def kernel_work(name, cfg, touched, touched_shared=True):
     T, H, E, k, I = cfg.num_tokens, cfg.hidden_size, cfg.num_experts, cfg.top_k, cfg.intermediate_size
     Is = cfg.shared_intermediate_size
     P = T * k
-    es = 2 if cfg.dtype == "bf16" else 4  # activations, weights and h; y is fp32
+    es = 2 if cfg.dtype == "bf16" else 4  # activations, weights and h
+    ys = y_bytes_per_value(cfg)  # routed y; the shared expert's output is fp32
     if name in ("ffn_gate_up_bf16", "ffn_gate_up_f32"):
         # weights of touched experts, every token row once, h written once
         return 4.0 * P * H * I, touched * 2 * I * H * es + T * H * es + P * I * es
     if name in ("ffn_down_bf16", "ffn_down_f32"):
-        return 2.0 * P * H * I, touched * H * I * es + P * I * es + P * H * 4
+        return 2.0 * P * H * I, touched * H * I * es + P * I * es + P * H * ys
     if name == "shared_gate_up_bf16":
         return 4.0 * T * H * Is, 2 * Is * H * es + T * H * es + T * Is * es
     if name == "shared_down_bf16":
@@ -74,7 +89,7 @@ def kernel_work(name, cfg, touched, touched_shared=True):
         return 0.0, P * 4 + 3 * P * 4
     if name == "combine":
         # y and the shared output (fp32) read once, fp32 output written once
-        return 0.0, P * H * 4 + P * 8 + T * H * 4 + (T * H * 4 if Is else 0)
+        return 0.0, P * H * ys + P * 8 + T * H * 4 + (T * H * 4 if Is else 0)
     return 0.0, 0.0
 
 

@@ -198,8 +198,11 @@ def w13_up(w13: np.ndarray, e: int) -> np.ndarray:
 
 def silu(z: np.ndarray) -> np.ndarray:
     """``silu(z) = z * sigmoid(z) = z / (1 + exp(-z))`` (standard SwiGLU
-    activation; the pages name SwiGLU experts but print no formula)."""
-    return z / (1.0 + np.exp(-z))
+    activation; the pages name SwiGLU experts but print no formula).  For
+    z below about -709, exp(-z) overflows to inf and the quotient is the
+    exact limit 0; the overflow is expected, not reported."""
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
 
 
 def swiglu_expert(X: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:

@@ -201,9 +201,11 @@ hipError_t run_router(const void* x, const void* wr, const float* bias, const vo
 
 // counters: 2 * kTileCounterInts zeroed ints (gate/up, down) or NULL.  y is
 // bf16 when y_dtype is MOE_DTYPE_BF16 (bf16 layers only), else fp32.
+// y_format (moe::YFormat, bf16 layers only for Y_BF16 and Y_F16S): fp32 y,
+// bf16 y, or fp16 y with the exponents y_scale [P, H/64].
 hipError_t run_ffn(const void* x, const int32_t* gather, const int32_t* offsets, const void* w13, const void* w2,
-                   int T_rows, int P, int H, int E, int I, int dtype, void* h, void* y, int y_dtype, hipStream_t s,
-                   bool shared, int* counters, float* partial) {
+                   int T_rows, int P, int H, int E, int I, int dtype, void* h, void* y, int y_format,
+                   int32_t* y_scale, hipStream_t s, bool shared, int* counters, float* partial) {
   hipError_t e;
   if (dtype == MOE_DTYPE_BF16) {
     moe::GemmArgs a = gemm_args();
@@ -239,8 +241,11 @@ hipError_t run_ffn(const void* x, const int32_t* gather, const int32_t* offsets,
     b.ldo = H;
     b.tile_counter = counters ? counters + moe::kTileCounterInts : nullptr;
     b.partial = partial;
-    return moe::launch_grouped_gemm_bf16(b, y_dtype == MOE_DTYPE_BF16 ? moe::EPI_BF16 : moe::EPI_F32, s,
-                                         shared ? "shared_down_bf16" : "ffn_down_bf16");
+    b.scale_out = y_scale;
+    const moe::GemmEpilogue epi = (y_format == moe::Y_BF16)   ? moe::EPI_BF16
+                                  : (y_format == moe::Y_F16S) ? moe::EPI_F16S
+                                                              : moe::EPI_F32;
+    return moe::launch_grouped_gemm_bf16(b, epi, s, shared ? "shared_down_bf16" : "ffn_down_bf16");
   }
   e = moe::launch_ffn_gate_up_f32(static_cast<const float*>(x), gather, offsets, static_cast<const float*>(w13), P,
                                   H, E, I, static_cast<float*>(h), s);
@@ -503,7 +508,8 @@ moe_status moe_grouped_ffn(const void* hidden_states, const int32_t* packed_toke
   }
   return hip_status(run_ffn(hidden_states, packed_token_indices, expert_offsets, w13, w2, (int)num_tokens, P,
                             (int)hidden_size, (int)num_experts, (int)intermediate_size, dtype, h,
-                            packed_expert_outputs, expert_out_dtype, s, false,
+                            packed_expert_outputs, expert_out_dtype == MOE_DTYPE_BF16 ? moe::Y_BF16 : moe::Y_F32,
+                            nullptr, s, false,
                             dtype == MOE_DTYPE_BF16 ? counters : nullptr,
                             partial),
                     "moe_grouped_ffn");
@@ -533,7 +539,9 @@ moe_status moe_combine(const void* packed_expert_outputs, const int32_t* inverse
   REQUIRE_ALIGNED(shared_output);
   REQUIRE_ALIGNED(output);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(moe::launch_combine(packed_expert_outputs, expert_dtype == MOE_DTYPE_BF16, inverse_permutation,
+  return hip_status(moe::launch_combine(packed_expert_outputs,
+                                        expert_dtype == MOE_DTYPE_BF16 ? moe::Y_BF16 : moe::Y_F32, nullptr,
+                                        inverse_permutation,
                                         topk_weights, shared_output, shared_gate_logit, (int)num_tokens,
                                         (int)hidden_size, (int)top_k, out_dtype == MOE_DTYPE_BF16, output, s),
                     "moe_combine");
@@ -638,14 +646,33 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
       }
     }
     e = run_ffn(hidden_states, nullptr, nullptr, shared_w13, shared_w2, T, T, H, 1, (int)Is, dtype, L.hs, L.ys,
-                MOE_DTYPE_F32, ss, true, shared_counters, L.partial_shared);
+                moe::Y_F32, nullptr, ss, true, shared_counters, L.partial_shared);
     if (e != hipSuccess) return hip_status(e, "moe_forward(shared expert)");
     if (aux != nullptr) {
       e = hipEventRecord(aux->join, aux->stream);
       if (e != hipSuccess) return hip_status(e, "moe_forward(join)");
     }
   }
-  e = run_ffn(hidden_states, L.packed_ids, L.offsets, w13, w2, T, P, H, E, I, dtype, L.h, L.y, MOE_DTYPE_F32, s,
+  // Large batches (the pipelined 256-row down kernel): the packed expert
+  // outputs go out as fp16 with a power-of-two scale per (row, 64 columns),
+  // half the bytes of fp32 for the down projection to write and the combine
+  // to read, with 11 significant bits (bf16 storage would keep 8 and about
+  // double the layer's output error).  The exponents follow the values in
+  // y's fp32-sized slot.
+  int y_format = moe::Y_F32;
+  int32_t* y_scale = nullptr;
+  if (dtype == MOE_DTYPE_BF16) {
+    moe::GemmArgs probe = gemm_args();
+    probe.M = P;
+    probe.G = E;
+    probe.offsets = L.offsets;
+    probe.K = I;
+    if (moe::grouped_gemm_uses_pipe(probe) && H % moe::kF16SegCols == 0) {
+      y_format = moe::Y_F16S;
+      y_scale = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(L.y) + align_up((size_t)P * H * 2));
+    }
+  }
+  e = run_ffn(hidden_states, L.packed_ids, L.offsets, w13, w2, T, P, H, E, I, dtype, L.h, L.y, y_format, y_scale, s,
               false, L.counters, L.partial);
   if (e != hipSuccess) return hip_status(e, "moe_forward(experts)");
   if (aux != nullptr) {
@@ -653,8 +680,8 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
     if (e != hipSuccess) return hip_status(e, "moe_forward(join)");
   }
   if (aux_lock.owns_lock()) aux_lock.unlock();
-  e = moe::launch_combine(L.y, 0, L.inv, weights, Is ? L.ys : nullptr, Is ? L.gate_logit : nullptr, T, H, k,
-                          out_dtype == MOE_DTYPE_BF16, output, s);
+  e = moe::launch_combine(L.y, y_format, y_scale, L.inv, weights, Is ? L.ys : nullptr, Is ? L.gate_logit : nullptr,
+                          T, H, k, out_dtype == MOE_DTYPE_BF16, output, s);
   return hip_status(e, "moe_forward(combine)");
 }
 

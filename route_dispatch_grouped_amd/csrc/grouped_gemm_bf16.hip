@@ -7,6 +7,8 @@
 //               h = silu(g) * u as bf16.               [DWDP README "Executor Module"]
 //   EPI_F32     down projection y = W2[e] h, fp32 out.  [DWDP README "Executor Module"]
 //   EPI_BF16    the same, y rounded once to bf16 (RNE).
+//   EPI_F16S    the same, y as fp16 with a power-of-two scale per (row, 64
+//               columns) (pipelined 256-row kernel only).
 //   EPI_ROUTER  router logits x Wr^T (+ bias).          [DWDP README "Router Module"]
 //
 // Scheduling: the packed rows of each group (expert) form expert-major execution
@@ -1157,8 +1159,28 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_big_kernel(GemmArg
 //    more than 63 operations follow a stage, that stage has retired.
 template <int EPI>
 struct PipeEpi {
-  static constexpr int kStores = (EPI == EPI_SWIGLU) ? 32 : 64;
+  // EPI_F16S: per row sub-tile and 64-column segment, one exponent and 8 values
+  static constexpr int kStores = (EPI == EPI_SWIGLU) ? 32 : (EPI == EPI_F16S) ? 72 : 64;
 };
+
+// Exponent k that brings a segment whose largest magnitude is m into
+// [2^14, 2^15) (0 for an all-zero segment; below the normal range the
+// smallest normal's k is used, and Inf/NaN keep their value).
+__device__ __forceinline__ int f16s_exponent(float m) {
+  const uint32_t eb = (__float_as_uint(m) >> 23) & 0xFFu;
+  if (m == 0.f) return 0;
+  const int e = (eb == 0) ? -126 : (int)eb - 127;
+  return 14 - e;
+}
+
+// two values rounded to fp16 (nearest even; one v_cvt_pk_f16_f32), the first
+// in the low half
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_clamped() {
@@ -1399,6 +1421,42 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
             const uint32_t off = (row_ok && col < p.N) ? (uint32_t)(((int64_t)(m0 + row) * p.ldo + col) * 2)
                                                        : 0x80000000u;
             __builtin_amdgcn_raw_buffer_store_b64(v, ro, (int)off, 0, 0);
+          }
+        }
+      } else if (EPI == EPI_F16S) {
+        // two 64-column segments per wave row: j = 2s, 2s + 1 (this lane's 32
+        // values and the 32 of lane ^ 32, which holds the same row)
+        const int nseg = (int)(p.ldo / kF16SegCols);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            p.scale_out, (short)0, (int)((size_t)p.M * nseg * 4), kBufferWord3);
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) {
+          float m = 0.f;
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(acc[i][2 * sg + jj][e]));
+          m = fmaxf(m, __shfl_xor(m, 32, 64));
+          const int kx = f16s_exponent(m);
+          const int seg_col = n0 + 128 * wn + 64 * sg;
+          const uint32_t soff = (row_ok && seg_col < p.N && lane < 32)
+                                    ? (uint32_t)(((int64_t)(m0 + row) * nseg + seg_col / kF16SegCols) * 4)
+                                    : 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b32((uint32_t)kx, rs, (int)soff, 0, 0);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * sg + jj;
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int col = n0 + 128 * wn + 32 * j + 8 * gq + 4 * (lane >> 5);
+              typedef int i32x2_t __attribute__((ext_vector_type(2)));
+              const i32x2_t v = {(int)pack_f16x2(ldexpf(acc[i][j][4 * gq], kx), ldexpf(acc[i][j][4 * gq + 1], kx)),
+                                 (int)pack_f16x2(ldexpf(acc[i][j][4 * gq + 2], kx),
+                                                 ldexpf(acc[i][j][4 * gq + 3], kx))};
+              const uint32_t off = (row_ok && col < p.N) ? (uint32_t)(((int64_t)(m0 + row) * p.ldo + col) * 2)
+                                                         : 0x80000000u;
+              __builtin_amdgcn_raw_buffer_store_b64(v, ro, (int)off, 0, 0);
+            }
           }
         }
       } else if (EPI == EPI_BF16) {
@@ -1728,8 +1786,19 @@ size_t grouped_gemm_partial_bytes(int64_t M, int64_t G, bool grouped, int64_t N,
   return (size_t)ks * (size_t)M * (size_t)ldp * sizeof(float);
 }
 
+bool grouped_gemm_uses_pipe(const GemmArgs& a) {
+  const int64_t groups = a.offsets ? (a.G < a.M ? a.G : a.M) : 1;
+  const int64_t KT = a.K / Big::KB;
+  return a.M > 0 && pick_bm(a.M, groups) == 0 && KT >= 8 && KT % 4 == 0;
+}
+
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, GemmEpilogue epi, hipStream_t s, const char* name) {
   if (a.M <= 0) return hipSuccess;
+  if (epi == EPI_F16S) {
+    if (!grouped_gemm_uses_pipe(a) || a.scale_out == nullptr || a.N % kF16SegCols != 0 || a.ldo % kF16SegCols != 0)
+      return hipErrorInvalidValue;
+    return launch_pipe<EPI_F16S>(a, s, name);
+  }
   switch (epi) {
     case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(a, s, name);
     case EPI_F32: return launch_epi<EPI_F32>(a, s, name);

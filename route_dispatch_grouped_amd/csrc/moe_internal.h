@@ -24,7 +24,14 @@ enum GemmEpilogue {
   EPI_F32 = 1,     // plain fp32 store
   EPI_ROUTER = 2,  // fp32 logits (+ bias), extra column -> gate logit
   EPI_BF16 = 3,    // plain store rounded once to bf16 (RNE)
+  EPI_F16S = 4,    // fp16 scaled by a power of two per (row, 64 columns); 256-row pipelined kernel only
 };
+
+// EPI_F16S layout: value (r, c) is stored as fp16(y * 2^k) with k =
+// scale_out[r * (ldo / 64) + c / 64], chosen from the segment's largest |y|
+// so that it lands in [2^14, 2^15): fp16 keeps 11 significant bits (about 8x
+// finer than bf16) with no overflow, and takes half the bytes of fp32.
+constexpr int kF16SegCols = 64;
 
 struct GemmArgs {
   const uint16_t* A;        // bf16 activations, rows of length K
@@ -43,6 +50,7 @@ struct GemmArgs {
   int64_t ldo;              // output row stride in elements
   const float* bias;        // EPI_ROUTER: per-column bias or NULL
   float* extra_out;         // EPI_ROUTER: x . b_extra per row, when b_extra != NULL
+  int32_t* scale_out;       // EPI_F16S: per (row, 64-column segment) exponents, [M, ldo / 64]
   int* tile_counter;        // large-group kernel: 8 zeroed ints (per-XCD tile grabs) or NULL
   float* partial;           // split-K scratch of grouped_gemm_partial_bytes() bytes, or NULL (no split)
   int ksplit;               // set by launch_grouped_gemm_bf16 (callers leave it 0)
@@ -52,6 +60,9 @@ constexpr int kTileCounterInts = 8;
 // True when the grouped GEMM for `a` runs the large-group kernel (which uses
 // a.tile_counter when given).
 bool grouped_gemm_uses_counter(const GemmArgs& a);
+// True when `a` runs on the pipelined 256-row kernel (the only one with the
+// EPI_F16S epilogue).
+bool grouped_gemm_uses_pipe(const GemmArgs& a);
 hipError_t launch_zero_ints(int* p, int n, hipStream_t s);
 
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, GemmEpilogue epi, hipStream_t s, const char* name);
@@ -108,8 +119,11 @@ hipError_t launch_topk_dispatch_small(const float* logits, int T, int E, int k, 
                                       int32_t* packed_ids, hipStream_t s, int* zero_ints, int n_zero);
 
 // ---------------------------------------------------------------- combine
-// y [P,H] and shared [T,H] (or NULL) are bf16 when y_bf16, else fp32.
-hipError_t launch_combine(const void* y, int y_bf16, const int32_t* inv, const float* w,
+// y [P,H]: fp32 (y_format 0), bf16 (1), or fp16 with the EPI_F16S
+// exponents y_scale [P, H/64] (2).  shared [T,H] (or NULL): fp32, or bf16
+// when y_format is 1.
+enum YFormat { Y_F32 = 0, Y_BF16 = 1, Y_F16S = 2 };
+hipError_t launch_combine(const void* y, int y_format, const int32_t* y_scale, const int32_t* inv, const float* w,
                           const void* shared, const float* shared_gate_logit,
                           int T, int H, int k, int out_bf16, void* out, hipStream_t s);
 

@@ -333,6 +333,34 @@ def test_forward_bf16_output_and_determinism():
     assert torch.equal(c["out"], a["out"].to(torch.bfloat16))
 
 
+def _scale_bf16_bits(bits: np.ndarray, s: float) -> np.ndarray:
+    """bf16 bit patterns times a power of two (exact inside the bf16 range)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(s)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("scale", [2.0 ** 12, 2.0 ** -20])
+def test_forward_large_batch_output_range(scale):
+    """Large batches keep the packed expert outputs as fp16 with a power-of-two
+    scale per 64 columns.  Activations scaled by 2^12 (outputs near 1e5, past
+    fp16's 65504) and by 2^-20 (outputs near 1e-14, below fp16's normal range)
+    must still match the oracle within the bf16 bound."""
+    cfg = SMALL["bf16_pipe_tiles"]
+    log(f"[parity] output range, x scaled by {scale:g}")
+    inp = dict(workloads.generate(cfg, seed=2))
+    inp["x"] = _scale_bf16_bits(inp["x"], scale)
+    dev = device_inputs(inp)
+    f = gpu_forward(cfg, dev)
+    ids = f["topk_ids"].cpu().numpy()
+    w = f["topk_weights"].cpu().numpy().astype(np.float64)
+    tokens = np.unique(np.concatenate([np.arange(8), np.random.default_rng(5).choice(cfg.num_tokens, 56, False)]))
+    ref = oracle.token_outputs(inp, tokens, ids, w)
+    err, rms = rel_max_err(f["out"].cpu().numpy().astype(np.float64)[tokens], ref)
+    log(f"[parity] output range {scale:g}: rms {rms:.3e} max|err|/rms = {err / rms:.3e}")
+    assert np.isfinite(f["out"].cpu().numpy()).all()
+    assert err <= tol_for(cfg) * rms
+
+
 def test_no_renormalize():
     cfg = SMALL["bf16_mid_rows"].scaled(renormalize=False)
     inp = workloads.generate(cfg, seed=4)
