@@ -176,28 +176,31 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 // Whole plan in one workgroup for P <= kDispatchSmallP (decode batches):
 // the same three steps as above with the 16 waves as the segments and every
 // intermediate in LDS.  Wave w owns the contiguous chunk [w*C, (w+1)*C) of
-// the assignments, C = ceil(P / 16).
+// the assignments, C = ceil(P / 16).  The per-wave counters take 16 * E ints
+// of dynamic LDS (only what E needs, so that these launches fit next to a
+// streaming GEMM's workgroup on a CU).
 constexpr int kSmallWaves = 16;
 
 __device__ __forceinline__ void dispatch_small_body(const int32_t* __restrict__ ids, const float* __restrict__ wts,
                                                     int P, int k, int E, int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                                     int32_t* __restrict__ inv, int32_t* __restrict__ packed_ids,
-                                                    float* __restrict__ packed_w, int* zero_ints, int n_zero) {
-  __shared__ int cnt[kSmallWaves][kMaxE];  // per-wave counts, then per-wave running positions
+                                                    float* __restrict__ packed_w, int* zero_ints, int n_zero,
+                                                    int* cnt) {
+  // cnt[q * E + e]: per-wave counts, then per-wave running positions
   __shared__ int wsum[kSmallWaves];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   if (zero_ints != nullptr && tid < n_zero) zero_ints[tid] = 0;
-  for (int i = tid; i < kSmallWaves * kMaxE; i += 1024) (&cnt[0][0])[i] = 0;
+  for (int i = tid; i < kSmallWaves * E; i += 1024) cnt[i] = 0;
   __syncthreads();
   const int C = (P + kSmallWaves - 1) / kSmallWaves;
   const int a0 = w * C;
   const int a1 = min(P, a0 + C);
   for (int a = a0 + lane; a < a1; a += 64) {
     const int e = ids[a];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[w][e], 1);  // ids outside [0, E) are a caller error
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[w * E + e], 1);  // ids outside [0, E) are a caller error
   }
   __syncthreads();
   // per expert: running sum over the waves (cnt[w][e] <- count of waves < w)
@@ -206,8 +209,8 @@ __device__ __forceinline__ void dispatch_small_body(const int32_t* __restrict__ 
   if (tid < E) {
 #pragma unroll
     for (int q = 0; q < kSmallWaves; ++q) {
-      const int c = cnt[q][tid];
-      cnt[q][tid] = tot;
+      const int c = cnt[q * E + tid];
+      cnt[q * E + tid] = tot;
       tot += c;
     }
   }
@@ -221,7 +224,7 @@ __device__ __forceinline__ void dispatch_small_body(const int32_t* __restrict__ 
     counts[tid] = tot;
     offsets[tid] = off;
 #pragma unroll
-    for (int q = 0; q < kSmallWaves; ++q) cnt[q][tid] += off;
+    for (int q = 0; q < kSmallWaves; ++q) cnt[q * E + tid] += off;
   }
   if (tid == 0) offsets[E] = P;
   __syncthreads();
@@ -241,10 +244,10 @@ __device__ __forceinline__ void dispatch_small_body(const int32_t* __restrict__ 
       todo &= ~m;
     }
     int pos = 0;
-    if (valid) pos = cnt[w][my] + __popcll(peers & lt_mask);
+    if (valid) pos = cnt[w * E + my] + __popcll(peers & lt_mask);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
-    if (valid && lane == __builtin_ctzll(peers)) cnt[w][my] += __popcll(peers);
+    if (valid && lane == __builtin_ctzll(peers)) cnt[w * E + my] += __popcll(peers);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
     if (valid) {
@@ -265,7 +268,9 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
                                                               int32_t* __restrict__ packed_ids,
                                                               float* __restrict__ packed_w, int* zero_ints,
                                                               int n_zero) {
-  dispatch_small_body(ids, wts, P, k, E, counts, offsets, perm, inv, packed_ids, packed_w, zero_ints, n_zero);
+  extern __shared__ int dyn_lds[];  // [16 * E]
+  dispatch_small_body(ids, wts, P, k, E, counts, offsets, perm, inv, packed_ids, packed_w, zero_ints, n_zero,
+                      dyn_lds);
 }
 
 // Decode batches: top-k of every token (one wave per token, the same
@@ -285,7 +290,8 @@ __global__ __launch_bounds__(1024) void topk_dispatch_small_kernel(const float* 
                                                                    int32_t* __restrict__ packed_ids, int* zero_ints,
                                                                    int n_zero) {
   // the ids also go to LDS, where the plan reads them (no global round trip)
-  __shared__ int32_t s_ids[kDispatchSmallP];
+  extern __shared__ int dyn_lds[];  // [16 * E] counters, then [T * k] ids
+  int32_t* s_ids = dyn_lds + kSmallWaves * E;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   for (int t = w; t < T; t += kSmallWaves)
@@ -293,7 +299,7 @@ __global__ __launch_bounds__(1024) void topk_dispatch_small_kernel(const float* 
                   lane, s_ids + t * k);
   __syncthreads();
   dispatch_small_body(s_ids, nullptr, T * k, k, E, counts, offsets, perm, inv, packed_ids, nullptr, zero_ints,
-                      n_zero);
+                      n_zero, dyn_lds);
 }
 
 }  // namespace
@@ -302,18 +308,19 @@ hipError_t launch_topk_dispatch_small(const float* logits, int T, int E, int k, 
                                       float* weights, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                                       int32_t* packed_ids, hipStream_t s, int* zero_ints, int n_zero) {
   if (T == 0) return hipSuccess;
+  const size_t lds = (size_t)(kSmallWaves * E + T * k) * sizeof(int);
   profile_begin("topk_dispatch_small", s);
   if (E <= 64)
-    hipLaunchKernelGGL(topk_dispatch_small_kernel<1>, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, ids,
+    hipLaunchKernelGGL(topk_dispatch_small_kernel<1>, dim3(1), dim3(1024), lds, s, logits, T, E, k, renorm, ids,
                        weights, counts, offsets, perm, inv, packed_ids, zero_ints, n_zero);
   else if (E <= 128)
-    hipLaunchKernelGGL(topk_dispatch_small_kernel<2>, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, ids,
+    hipLaunchKernelGGL(topk_dispatch_small_kernel<2>, dim3(1), dim3(1024), lds, s, logits, T, E, k, renorm, ids,
                        weights, counts, offsets, perm, inv, packed_ids, zero_ints, n_zero);
   else if (E <= 256)
-    hipLaunchKernelGGL(topk_dispatch_small_kernel<4>, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, ids,
+    hipLaunchKernelGGL(topk_dispatch_small_kernel<4>, dim3(1), dim3(1024), lds, s, logits, T, E, k, renorm, ids,
                        weights, counts, offsets, perm, inv, packed_ids, zero_ints, n_zero);
   else
-    hipLaunchKernelGGL(topk_dispatch_small_kernel<8>, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, ids,
+    hipLaunchKernelGGL(topk_dispatch_small_kernel<8>, dim3(1), dim3(1024), lds, s, logits, T, E, k, renorm, ids,
                        weights, counts, offsets, perm, inv, packed_ids, zero_ints, n_zero);
   profile_end(s);
   return hipGetLastError();
@@ -331,8 +338,8 @@ hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int
   if (P == 0) return hipSuccess;
   if (P <= kDispatchSmallP) {
     profile_begin("dispatch_small", s);
-    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, s, ids, w, P, k, E, counts, offsets, perm, inv,
-                       packed_ids, packed_w, zero_ints, n_zero);
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), (size_t)kSmallWaves * E * sizeof(int), s, ids, w,
+                       P, k, E, counts, offsets, perm, inv, packed_ids, packed_w, zero_ints, n_zero);
     profile_end(s);
     return hipGetLastError();
   }

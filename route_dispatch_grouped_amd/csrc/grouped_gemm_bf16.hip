@@ -511,9 +511,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
 //     16 distinct 4-bank groups.
 //   * K need not be a multiple of 256: chunks past the end of a row are
 //     fetched through an offset past the buffer (zeros).
-//   * the gathered row indices are staged in LDS up front, so that building
-//     the DMA plan of the next unit issues no vector load (which would make
-//     the compiler wait for every DMA in flight).
+//   * the gathered row indices are staged in LDS up front (dynamic LDS of M
+//     ints, none without a gather), so that building the DMA plan of the next
+//     unit issues no vector load (which would make the compiler wait for
+//     every DMA in flight).
 constexpr int kStreamBR = 64;          // weight rows per tile
 constexpr int kStreamCH = 32;          // 16-byte chunks per row per stage (256 k)
 constexpr int kStreamNS = 3;           // ring depth
@@ -639,7 +640,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_stream_kernel(Gemm
   __shared__ int s_off[kMaxGroups + 1];
   __shared__ int s_tb[kMaxGroups + 1];
   __shared__ int s_wsum[kThreads / 64];
-  __shared__ int s_gidx[C::MAX_ROWS];  // the host keeps M <= MAX_ROWS
+  extern __shared__ int s_gidx[];  // [M] with a gather; the host keeps M <= MAX_ROWS
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1687,7 +1688,8 @@ hipError_t launch_stream(const GemmArgs& a_in, hipStream_t s, const char* name) 
   grid = ((grid + kXcds - 1) / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
   profile_begin(name, s);
-  hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<BM, EPI>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  const size_t lds = a.gather ? (size_t)a.M * sizeof(int) : 0;
+  hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<BM, EPI>), dim3((unsigned)grid), dim3(kThreads), lds, s, a);
   if (a.ksplit > 1) {
     const int64_t n = (int64_t)a.M * (a.N / 4);
     hipLaunchKernelGGL((splitk_reduce_kernel<EPI>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.partial,
