@@ -178,6 +178,48 @@ def cpu_baseline(cfg, inp, sample_tokens, target_s):
             "seconds": round(dt, 3)}
 
 
+SECONDARY_WORKLOAD = "qwen15_moe_decode"
+
+
+def decode_measure(rdg, torch, seed, steps=400, warmup=50):
+    """The memory-bound decode shape beside the headline: one forward per
+    step, reported as tokens/s and as weight bytes streamed per second against
+    the HBM peak.  Bytes per step: the touched experts' w13 and w2, the shared
+    expert's weights, the router and gate rows (activations are negligible)."""
+    cfg = workloads.config(SECONDARY_WORKLOAD)
+    inp = workloads.generate(cfg, seed=seed)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    d = {kk: dev(v) for kk, v in inp.items()}
+    layer = rdg.MoeLayer(d["router_weight"], d["w13"], d["w2"], cfg.top_k, router_bias=d.get("router_bias"),
+                         shared_w13=d.get("shared_w13"), shared_w2=d.get("shared_w2"),
+                         shared_gate=d.get("shared_gate"), renormalize=cfg.renormalize)
+    x = d["x"]
+    layer.reserve(cfg.num_tokens, x.device)
+    for _ in range(warmup):
+        layer(x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer(x)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    r = rdg.moe_router_topk(x, d["router_weight"], cfg.top_k, renormalize=cfg.renormalize)
+    counts = rdg.moe_dispatch_plan(r["topk_ids"], None, cfg.num_experts)["counts"].cpu().numpy()
+    touched = int((counts > 0).sum())
+    H, I, Is, E = cfg.hidden_size, cfg.intermediate_size, cfg.shared_intermediate_size, cfg.num_experts
+    nbytes = touched * 3 * I * H * 2 + 3 * Is * H * 2 + (E + 1) * H * 2
+    gbs = nbytes / dt / 1e9
+    return {"workload": cfg.name, "steps": steps, "warmup": warmup, "ms_per_step": round(dt * 1e3, 4),
+            "value": round(cfg.num_tokens / dt, 1), "unit": "tokens/s", "experts_touched": touched,
+            "weight_bytes_per_step": nbytes, "achieved": round(gbs, 1), "achieved_unit": "GB/s",
+            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +232,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--cpu-target-seconds", type=float, default=15.0)
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event region")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help=f"skip the {SECONDARY_WORKLOAD} measurement reported beside the headline workload")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the steps, run one plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -325,6 +369,13 @@ def main():
         ffn = {"tflops": round(fl / t_ffn / 1e12, 2), "frac_bf16_peak": round(fl / t_ffn / 1e12 / PEAK_BF16_TFLOPS, 4),
                "us": round(t_ffn * 1e6, 2)}
 
+    secondary = None
+    if not args.no_secondary and cfg.name == DEFAULT_WORKLOAD:
+        log(f"[bench] secondary: {SECONDARY_WORKLOAD}")
+        secondary = decode_measure(rdg, torch, args.seed)
+        log(f"[bench] {SECONDARY_WORKLOAD}: {secondary['ms_per_step']} ms/step, {secondary['achieved']} GB/s "
+            f"({100 * secondary['frac_hbm_peak']:.1f} % of HBM peak)")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
@@ -353,6 +404,7 @@ def main():
         "grouped_ffn": ffn,
         "kernels": per_kernel,
         "ep_routing_table": ep,
+        "decode": secondary,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
