@@ -24,7 +24,13 @@ design notes of the repository):
   ``inv[a] = p``; offsets have E+1 entries;
 * an expert computes ``h = silu(gate) * up`` with ``silu(z) = z / (1 + e^-z)``,
   then ``y = W2 h``; routing weights are applied in the combine;
-* the shared expert output is scaled by sigmoid(x . g) for a gate vector g [H].
+* the shared expert output is scaled by sigmoid(x . g) for a gate vector g [H];
+* group-limited selection (diffulex "diffulex.moe.topk" names a router with
+  group-limited expert selection and nothing more): the experts form n_group
+  contiguous groups of E / n_group; a group's score is its largest logit; the
+  topk_group best groups are kept (equal scores: the lower group), and the
+  top-k is taken among their experts by the plain rule.  Weights follow the
+  plain router's rule (softmax over all experts, renormalised over the k).
 
 Everything is float64; bf16 inputs are widened exactly and nothing is rounded
 on the way.  This module imports NumPy only.
@@ -40,6 +46,7 @@ __all__ = [
     "router_logits",
     "shared_gate_logit",
     "select_topk",
+    "select_topk_grouped",
     "routing_probs",
     "routing_weights",
     "dispatch_plan",
@@ -112,6 +119,34 @@ def select_topk(logits: np.ndarray, top_k: int) -> np.ndarray:
     if not (1 <= top_k <= E):
         raise ValueError("top_k out of range")
     order = np.argsort(-L, axis=1, kind="stable")
+    return order[:, :top_k].astype(np.int32)
+
+
+def select_topk_grouped(logits: np.ndarray, top_k: int, n_group: int, topk_group: int) -> np.ndarray:
+    """Group-limited top-k expert ids per token, ``[T, k]`` int32.
+
+    [diffulex] "diffulex.moe.topk" (a router with group-limited expert
+    selection; the steps are the reading stated in the module docstring):
+    group g holds experts [g*E/n_group, (g+1)*E/n_group); its score is the
+    largest logit it holds; the topk_group highest-scoring groups are kept,
+    equal scores going to the lower group; then the plain selection of
+    ``select_topk`` runs over the kept groups' experts only.
+    """
+    L = np.asarray(logits, dtype=np.float64)
+    T, E = L.shape
+    if n_group < 1 or E % n_group != 0:
+        raise ValueError("n_group must divide the number of experts")
+    gs = E // n_group
+    if not (1 <= topk_group <= n_group):
+        raise ValueError("topk_group out of range")
+    if not (1 <= top_k <= topk_group * gs):
+        raise ValueError("top_k exceeds the experts of the kept groups")
+    score = L.reshape(T, n_group, gs).max(axis=2)
+    kept = np.argsort(-score, axis=1, kind="stable")[:, :topk_group]
+    allowed = np.zeros((T, n_group), dtype=bool)
+    np.put_along_axis(allowed, kept, True, axis=1)
+    masked = np.where(np.repeat(allowed, gs, axis=1), L, -np.inf)
+    order = np.argsort(-masked, axis=1, kind="stable")
     return order[:, :top_k].astype(np.int32)
 
 

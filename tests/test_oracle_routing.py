@@ -162,3 +162,81 @@ def test_widen_bf16_exact():
     assert vals[4] == 3.140625  # 0x4049 = 1.5703125 * 2
     assert vals[5] == 2.0 ** -7
     assert vals[6] == (2 - 2.0 ** -7) * 2.0 ** 127
+
+
+# ---------------------------------------------------------------- group-limited
+def _brute_topk_grouped(row, k, n_group, topk_group):
+    """Subset formulation: the kept groups are the topk_group-subset whose
+    (-score, group) pairs, sorted, are lexicographically smallest (largest
+    scores first, lower groups on ties); the experts are the k-subset of the
+    kept groups' experts chosen the same way on (-logit, id)."""
+    E = len(row)
+    gs = E // n_group
+    score = [max(float(row[e]) for e in range(g * gs, (g + 1) * gs)) for g in range(n_group)]
+    best_s = min(itertools.combinations(range(n_group), topk_group),
+                 key=lambda S: sorted((-score[g], g) for g in S))
+    allowed = [e for e in range(E) if e // gs in best_s]
+    best_e = min(itertools.combinations(allowed, k), key=lambda C: sorted((-float(row[e]), e) for e in C))
+    return [e for _, e in sorted((-float(row[e]), e) for e in best_e)]
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_topk_grouped_matches_bruteforce(seed):
+    rng = np.random.default_rng(100 + seed)
+    n_group = int(rng.choice([2, 3, 4]))
+    gs = int(rng.integers(1, 4))
+    E = n_group * gs
+    tg = int(rng.integers(1, n_group + 1))
+    k = int(rng.integers(1, tg * gs + 1))
+    L = rng.integers(-3, 4, size=(5, E)).astype(np.float64) / 4.0  # many exact ties
+    ids = oracle.select_topk_grouped(L, k, n_group, tg)
+    for t in range(L.shape[0]):
+        assert list(ids[t]) == _brute_topk_grouped(L[t], k, n_group, tg)
+
+
+def test_topk_grouped_reduces_to_plain():
+    rng = np.random.default_rng(7)
+    L = rng.standard_normal((40, 32))
+    for k in (1, 4, 8):
+        plain = oracle.select_topk(L, k)
+        assert (oracle.select_topk_grouped(L, k, 1, 1) == plain).all()
+        assert (oracle.select_topk_grouped(L, k, 8, 8) == plain).all()
+        assert (oracle.select_topk_grouped(L, k, 4, 4) == plain).all()
+
+
+def test_topk_grouped_hand_cases():
+    # groups of 2: maxima 9, 2, 8.5, 8.4 -> keep groups 0 and 2 -> experts 0, 1, 4, 5;
+    # the plain top-4 would take expert 6 (8.4) instead of expert 5 (0)
+    L = np.array([[9, 8.9, 1, 2, 8.5, 0, 8.4, 0]], dtype=np.float64)
+    assert list(oracle.select_topk_grouped(L, 4, 4, 2)[0]) == [0, 1, 4, 5]
+    assert list(oracle.select_topk(L, 4)[0]) == [0, 1, 4, 6]
+    # equal group scores (5 and 5): the lower group is kept
+    L = np.array([[5, 0, 0, 5, 1, 1, 2, 2]], dtype=np.float64)
+    assert list(oracle.select_topk_grouped(L, 2, 4, 1)[0]) == [0, 1]
+
+
+def test_topk_grouped_invariants():
+    rng = np.random.default_rng(11)
+    T, E, ng, tg, k = 200, 128, 8, 4, 8
+    L = rng.standard_normal((T, E))
+    ids = oracle.select_topk_grouped(L, k, ng, tg)
+    gs = E // ng
+    score = L.reshape(T, ng, gs).max(axis=2)
+    for t in range(T):
+        groups = set(int(e) // gs for e in ids[t])
+        top_groups = set(np.argsort(-score[t], kind="stable")[:tg].tolist())
+        assert groups <= top_groups and len(set(ids[t].tolist())) == k
+        allowed = [e for e in range(E) if e // gs in top_groups]
+        rest = [e for e in allowed if e not in set(ids[t].tolist())]
+        assert L[t, ids[t]].min() >= L[t, rest].max()
+        assert (np.diff(L[t, ids[t]]) <= 0).all()
+
+
+def test_topk_grouped_rejects_bad_shapes():
+    L = np.zeros((2, 12))
+    with pytest.raises(ValueError):
+        oracle.select_topk_grouped(L, 2, 5, 2)   # 5 does not divide 12
+    with pytest.raises(ValueError):
+        oracle.select_topk_grouped(L, 7, 4, 2)   # only 2 * 3 experts kept
+    with pytest.raises(ValueError):
+        oracle.select_topk_grouped(L, 2, 4, 5)   # more kept groups than groups
