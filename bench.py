@@ -335,6 +335,30 @@ def main():
               "frac": round(nbytes / avg_s / 1e9 / PEAK_HBM_GBS, 4)}
         log(f"[bench] ep routing table: {ep['avg_us']} us ({ep['achieved']} GB/s)")
 
+    # group-limited top-k on this batch (experts in 8 groups, 4 kept): the
+    # selection kernel alone, timed like the plain one (outside the layer step)
+    grouped = None
+    if not args.no_profile and cfg.num_experts % 8 == 0 and cfg.top_k <= 4 * (cfg.num_experts // 8):
+        ng, tg = 8, 4
+        for _ in range(3):
+            rdg.moe_router_topk_grouped(x, d["router_weight"], cfg.top_k, ng, tg, router_bias=d.get("router_bias"),
+                                        renormalize=cfg.renormalize)
+        torch.cuda.synchronize()
+        rdg.profile_enable(True)
+        for _ in range(args.steps):
+            rdg.moe_router_topk_grouped(x, d["router_weight"], cfg.top_k, ng, tg, router_bias=d.get("router_bias"),
+                                        renormalize=cfg.renormalize)
+        torch.cuda.synchronize()
+        rdg.profile_enable(False)
+        prof = rdg.profile_collect()
+        ms, c = prof["router_topk_grouped"]
+        avg_s = ms / c / 1e3
+        nbytes = cfg.num_tokens * cfg.num_experts * 4 + 2 * cfg.num_tokens * cfg.top_k * 4
+        grouped = {"avg_us": round(avg_s * 1e6, 2), "n_group": ng, "topk_group": tg, "algorithmic_bytes": nbytes,
+                   "achieved": round(nbytes / avg_s / 1e9, 1), "unit": "GB/s",
+                   "frac": round(nbytes / avg_s / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"[bench] grouped top-k ({ng} groups, {tg} kept): {grouped['avg_us']} us")
+
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
         src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -404,6 +428,7 @@ def main():
         "grouped_ffn": ffn,
         "kernels": per_kernel,
         "ep_routing_table": ep,
+        "router_topk_grouped": grouped,
         "decode": secondary,
         "cpu_baseline": cpu,
     }

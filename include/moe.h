@@ -111,6 +111,30 @@ moe_status moe_router_topk(const void* hidden_states, const void* router_weight,
                            float* shared_gate_logit, void* stream);
 
 /*
+ * Router with group-limited expert selection.
+ * [diffulex.moe "diffulex.moe.topk": GroupLimitedTopKRouter, a router with
+ *  group-limited expert selection; the steps below are this library's
+ *  reading, the page gives none]
+ *
+ * As moe_router_topk (no shared gate), except for the choice of experts:
+ *   group g holds experts [g*E/n_group, (g+1)*E/n_group); its score is its
+ *   largest logit; the topk_group highest-scoring groups are kept (equal
+ *   scores: the lower group first); topk_ids[t,:] are the k largest logits
+ *   among the kept groups' experts, with the ordering and tie rule of
+ *   moe_router_topk.  Weights and routing_probs are defined as there (the
+ *   softmax runs over all E experts).  n_group == 1 is moe_router_topk.
+ * Errors: as moe_router_topk, plus INVALID_ARG unless 1 <= n_group <= 64,
+ * n_group divides E, 1 <= topk_group <= n_group and
+ * k <= topk_group * E / n_group.
+ */
+moe_status moe_router_topk_grouped(const void* hidden_states, const void* router_weight,
+                                   const float* router_bias, int64_t num_tokens, int64_t hidden_size,
+                                   int64_t num_experts, int64_t top_k, int64_t n_group,
+                                   int64_t topk_group, int renormalize, int dtype,
+                                   float* router_logits, float* routing_probs,
+                                   int32_t* topk_ids, float* topk_weights, void* stream);
+
+/*
  * Dispatch plan: token-major assignments -> expert-major layout.
  * [DWDP README "Dispatcher Module": expert-major grouping, per-expert counts,
  *  expert offsets, token permutation, inverse permutation, packed token

@@ -31,6 +31,7 @@ __all__ = [
     "load_library",
     "library_loaded",
     "moe_router_topk",
+    "moe_router_topk_grouped",
     "moe_dispatch_plan",
     "moe_ep_routing_table",
     "moe_grouped_ffn",
@@ -57,6 +58,8 @@ _SIGNATURES = {
     "moe_last_error_message": (ctypes.c_char_p, []),
     "moe_router_topk": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _int, _int,
                                _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "moe_router_topk_grouped": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _i64, _i64, _int,
+                                       _int, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "moe_dispatch_workspace_size": (_size, [_i64, _i64, _i64]),
     "moe_dispatch_plan": (_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
@@ -184,6 +187,38 @@ def moe_router_topk(hidden_states: torch.Tensor, router_weight: torch.Tensor, to
                              _ptr(out["logits"]), _ptr(out.get("probs")), _ptr(out["topk_ids"]),
                              _ptr(out["topk_weights"]), _ptr(out.get("shared_gate_logit")), _stream(stream))
     _check("moe_router_topk", st)
+    return out
+
+
+def moe_router_topk_grouped(hidden_states: torch.Tensor, router_weight: torch.Tensor, top_k: int, n_group: int,
+                            topk_group: int, router_bias: Optional[torch.Tensor] = None, renormalize: bool = True,
+                            return_probs: bool = False, stream=None) -> Dict[str, torch.Tensor]:
+    """Router with group-limited expert selection (include/moe.h: moe_router_topk_grouped).
+
+    Returns ``logits [T,E] f32``, ``topk_ids [T,k] int32``, ``topk_weights [T,k] f32`` and
+    optionally ``probs [T,E]``.
+    """
+    lib = load_library()
+    T, H = hidden_states.shape
+    E = router_weight.shape[0]
+    dt = hidden_states.dtype
+    _need(hidden_states, "hidden_states", (T, H), dt)
+    _need(router_weight, "router_weight", (E, H), dt)
+    if router_bias is not None:
+        _need(router_bias, "router_bias", (E,), torch.float32)
+    dev = hidden_states.device
+    out = {
+        "logits": torch.empty((T, E), dtype=torch.float32, device=dev),
+        "topk_ids": torch.empty((T, top_k), dtype=torch.int32, device=dev),
+        "topk_weights": torch.empty((T, top_k), dtype=torch.float32, device=dev),
+    }
+    if return_probs:
+        out["probs"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+    st = lib.moe_router_topk_grouped(_ptr(hidden_states), _ptr(router_weight), _ptr(router_bias), T, H, E,
+                                     int(top_k), int(n_group), int(topk_group), int(bool(renormalize)),
+                                     _dtype_code(dt), _ptr(out["logits"]), _ptr(out.get("probs")),
+                                     _ptr(out["topk_ids"]), _ptr(out["topk_weights"]), _stream(stream))
+    _check("moe_router_topk_grouped", st)
     return out
 
 

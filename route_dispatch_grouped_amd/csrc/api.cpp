@@ -384,6 +384,36 @@ size_t moe_dispatch_workspace_size(int64_t num_tokens, int64_t top_k, int64_t nu
   return align_up(moe::dispatch_scratch_bytes(num_tokens * top_k, num_experts));
 }
 
+moe_status moe_router_topk_grouped(const void* hidden_states, const void* router_weight, const float* router_bias,
+                                   int64_t num_tokens, int64_t hidden_size, int64_t num_experts, int64_t top_k,
+                                   int64_t n_group, int64_t topk_group, int renormalize, int dtype,
+                                   float* router_logits, float* routing_probs, int32_t* topk_ids, float* topk_weights,
+                                   void* stream) {
+  RETURN_IF_ERR(check_sizes(num_tokens, hidden_size, num_experts, top_k, dtype, true));
+  RETURN_IF_ERR(check_buffer_bytes(num_tokens, hidden_size, 1, 1, dtype));
+  if (n_group < 1 || n_group > 64) return fail(MOE_ERR_INVALID_ARG, "n_group must be in [1, 64]");
+  if (num_experts % n_group != 0) return fail(MOE_ERR_INVALID_ARG, "n_group must divide num_experts");
+  if (topk_group < 1 || topk_group > n_group) return fail(MOE_ERR_INVALID_ARG, "topk_group must be in [1, n_group]");
+  if (top_k > topk_group * (num_experts / n_group))
+    return fail(MOE_ERR_INVALID_ARG, "top_k exceeds the experts of topk_group groups");
+  if (num_tokens == 0) return succeed();
+  REQUIRE_PTR(hidden_states);
+  REQUIRE_PTR(router_weight);
+  REQUIRE_PTR(topk_ids);
+  REQUIRE_PTR(topk_weights);
+  REQUIRE_PTR(router_logits);
+  REQUIRE_ALIGNED(hidden_states);
+  REQUIRE_ALIGNED(router_weight);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = (int)num_tokens, E = (int)num_experts, k = (int)top_k;
+  hipError_t e = run_router(hidden_states, router_weight, router_bias, nullptr, T, (int)hidden_size, E, k,
+                            renormalize ? 1 : 0, dtype, router_logits, nullptr, nullptr, nullptr, nullptr, s, false);
+  if (e == hipSuccess)
+    e = moe::launch_topk(router_logits, T, E, k, renormalize ? 1 : 0, topk_ids, topk_weights, routing_probs, s,
+                         (int)n_group, (int)topk_group);
+  return hip_status(e, "moe_router_topk_grouped");
+}
+
 moe_status moe_dispatch_plan(const int32_t* topk_ids, const float* topk_weights, int64_t num_tokens, int64_t top_k,
                              int64_t num_experts, int32_t* expert_counts, int32_t* expert_offsets,
                              int32_t* token_permutation, int32_t* inverse_permutation, int32_t* packed_token_indices,

@@ -92,8 +92,11 @@ hipError_t launch_ffn_down_f32(const float* h, const int32_t* offsets, const flo
                                int P, int H, int E, int I, float* y, hipStream_t s);
 
 // ---------------------------------------------------------------- router top-k
+// n_group > 1: group-limited selection (n_group <= 64 divides E; topk_group
+// groups kept; k <= topk_group * E / n_group).
 hipError_t launch_topk(const float* logits, int T, int E, int k, int renormalize,
-                       int32_t* ids, float* weights, float* probs, hipStream_t s);
+                       int32_t* ids, float* weights, float* probs, hipStream_t s,
+                       int n_group = 1, int topk_group = 1);
 
 // ---------------------------------------------------------------- EP routing table
 size_t ep_split_scratch_bytes(int64_t P);

@@ -32,12 +32,13 @@ __global__ __launch_bounds__(256) void router_logits_f32_kernel(
 template <int VPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                    int renorm, int32_t* __restrict__ ids,
-                                                   float* __restrict__ weights, float* __restrict__ probs) {
+                                                   float* __restrict__ weights, float* __restrict__ probs,
+                                                   int n_group, int topk_group) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   topk_row<VPL>(logits + (int64_t)t * E, E, k, renorm, ids + (int64_t)t * k, weights + (int64_t)t * k,
-                probs ? probs + (int64_t)t * E : nullptr, lane);
+                probs ? probs + (int64_t)t * E : nullptr, lane, nullptr, n_group, topk_group);
 }
 
 // Router logits for a handful of tokens (decode batches), bf16: workgroup
@@ -131,14 +132,18 @@ hipError_t launch_router_logits_f32(const float* x, const float* wr, const float
 }
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int renormalize, int32_t* ids, float* weights,
-                       float* probs, hipStream_t s) {
+                       float* probs, hipStream_t s, int n_group, int topk_group) {
   if (T == 0) return hipSuccess;
   const dim3 grid((T + 3) / 4), block(256);
-  profile_begin("router_topk", s);
-  if (E <= 64) hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, logits, T, E, k, renormalize, ids, weights, probs);
-  else if (E <= 128) hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, logits, T, E, k, renormalize, ids, weights, probs);
-  else if (E <= 256) hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, logits, T, E, k, renormalize, ids, weights, probs);
-  else hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, T, E, k, renormalize, ids, weights, probs);
+  profile_begin(n_group > 1 ? "router_topk_grouped" : "router_topk", s);
+#define MOE_TOPK(VPL)                                                                                          \
+  hipLaunchKernelGGL(topk_kernel<VPL>, grid, block, 0, s, logits, T, E, k, renormalize, ids, weights, probs,  \
+                     n_group, topk_group)
+  if (E <= 64) MOE_TOPK(1);
+  else if (E <= 128) MOE_TOPK(2);
+  else if (E <= 256) MOE_TOPK(4);
+  else MOE_TOPK(8);
+#undef MOE_TOPK
   profile_end(s);
   return hipGetLastError();
 }

@@ -80,10 +80,18 @@ __device__ __forceinline__ float wave_sum(float v) {
 // ~id and wins.  Winner j is kept by lane j % 64 in slot j / 64.  Weights:
 // exp(l_j - l_max) over the sum of the selected terms (renormalised) or over
 // all E terms (the plain softmax probability).
+//
+// Group-limited selection (n_group > 1; [diffulex.moe "diffulex.moe.topk"]:
+// a router with group-limited expert selection): experts form n_group <= 64
+// contiguous groups of E / n_group; a group's score is the largest key it
+// holds (its largest logit, the lower id on equal logits, so equal group
+// scores go to the lower group); the topk_group best groups stay available
+// and the k rounds run over their experts only.  The softmax terms still
+// cover all E experts.
 template <int VPL>
 __device__ __forceinline__ void topk_row(const float* row, int E, int k, int renorm, int32_t* __restrict__ ids,
                                          float* __restrict__ weights, float* __restrict__ probs, int lane,
-                                         int32_t* ids_copy = nullptr) {
+                                         int32_t* ids_copy = nullptr, int n_group = 1, int topk_group = 1) {
   float v[VPL];
   uint32_t key[VPL];
   uint32_t avail = 0;
@@ -97,6 +105,37 @@ __device__ __forceinline__ void topk_row(const float* row, int E, int k, int ren
     } else {
       v[i] = -INFINITY;
       key[i] = 0;
+    }
+  }
+
+  if (n_group > 1) {
+    const int gs = E / n_group;
+    uint64_t gkey = 0;  // lane g < n_group: group g's score key
+    for (int g = 0; g < n_group; ++g) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int e = lane + 64 * i;
+        if (((avail >> i) & 1u) && e / gs == g) {
+          const uint64_t kk = ((uint64_t)key[i] << 32) | (uint32_t)(~(uint32_t)e);
+          best = kk > best ? kk : best;
+        }
+      }
+      best = wave_max_u64(best);
+      if (lane == g) gkey = best;
+    }
+    uint64_t kept = 0;  // bit g: group g kept
+    bool gfree = lane < n_group;
+    for (int r = 0; r < topk_group; ++r) {
+      const uint64_t b = wave_max_u64(gfree ? gkey : 0);
+      const int gw = __builtin_ctzll(__ballot(gfree && gkey == b));
+      kept |= 1ull << gw;
+      if (lane == gw) gfree = false;
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && !((kept >> (e / gs)) & 1ull)) avail &= ~(1u << i);
     }
   }
 

@@ -74,6 +74,22 @@ def test_router_validation(lib):
     assert router(lib, T=0) == OK and last(lib) == ""
 
 
+def router_grouped(lib, T=4, H=64, E=8, k=2, ng=4, tg=2, x=P16, logits=P16, ids=P16, w=P16):
+    return lib.moe_router_topk_grouped(x, P16, NULL, T, H, E, k, ng, tg, 1, BF16, logits, NULL, ids, w, NULL)
+
+
+def test_router_grouped_validation(lib):
+    assert router_grouped(lib, ng=3) == INVALID and "divide" in last(lib)
+    assert router_grouped(lib, ng=0) == INVALID and "n_group" in last(lib)
+    assert router_grouped(lib, E=128, ng=128, tg=1, k=1) == INVALID and "n_group" in last(lib)
+    assert router_grouped(lib, tg=5) == INVALID and "topk_group" in last(lib)
+    assert router_grouped(lib, tg=0) == INVALID and "topk_group" in last(lib)
+    # two kept groups of two experts hold only four experts
+    assert router_grouped(lib, k=5) == INVALID and "top_k exceeds" in last(lib)
+    assert router_grouped(lib, ids=NULL) == INVALID and last(lib) == "topk_ids is NULL"
+    assert router_grouped(lib, T=0) == OK
+
+
 def dispatch(lib, T=4, k=2, E=8, ids=P16, w=P16, pw=P16, perm=P16, ws=P16, wsb=1 << 20):
     return lib.moe_dispatch_plan(ids, w, T, k, E, P16, P16, perm, P16, P16, pw, ws, wsb, NULL)
 

@@ -333,6 +333,41 @@ def test_forward_bf16_output_and_determinism():
     assert torch.equal(c["out"], a["out"].to(torch.bfloat16))
 
 
+@pytest.mark.parametrize("T,H,E,k,ng,tg,renorm", [
+    (300, 256, 128, 8, 8, 4, True),    # Qwen3-30B-A3B's 128 experts in 8 groups
+    (100, 128, 64, 6, 8, 3, False),
+    (77, 512, 60, 4, 4, 2, True),      # groups of 15 experts
+    (64, 256, 256, 8, 16, 4, True),    # four logits per lane
+    (40, 128, 32, 4, 1, 1, True),      # one group: the plain router
+])
+def test_router_topk_grouped(T, H, E, k, ng, tg, renorm):
+    """Group-limited selection on the GPU's own logits is bit-exact against
+    the oracle's; the logits are the plain router's bit for bit; weights and
+    probabilities follow the plain rule."""
+    log(f"[parity] grouped top-k T={T} E={E} k={k} groups {ng} keep {tg}")
+    cfg = workloads.config("qwen3_30b_a3b_prefill").scaled(
+        name="grouped", num_tokens=T, hidden_size=H, num_experts=E, top_k=k, intermediate_size=64)
+    inp = workloads.generate(cfg, seed=3)
+    dev = device_inputs(inp)
+    r = rdg.moe_router_topk_grouped(dev["x"], dev["router_weight"], k, ng, tg, renormalize=renorm,
+                                    return_probs=True)
+    plain = rdg.moe_router_topk(dev["x"], dev["router_weight"], k, renormalize=renorm)
+    Lg = r["logits"].cpu().numpy().astype(np.float64)
+    assert (r["logits"].cpu().numpy() == plain["logits"].cpu().numpy()).all()
+    ids = r["topk_ids"].cpu().numpy()
+    assert (ids == oracle.select_topk_grouped(Lg, k, ng, tg)).all()
+    if ng == 1:
+        assert (ids == plain["topk_ids"].cpu().numpy()).all()
+    w = r["topk_weights"].cpu().numpy().astype(np.float64)
+    w_ref = oracle.routing_weights(Lg, ids, renorm)
+    assert np.max(np.abs(w - w_ref) / np.maximum(w_ref, 1e-30)) <= 1e-5
+    p_ref = oracle.routing_probs(Lg)
+    assert np.max(np.abs(r["probs"].cpu().numpy() - p_ref)) <= 1e-5 * np.max(p_ref)
+    # selections that differ from the plain top-k exist in the larger cases
+    if ng > 1 and T >= 100:
+        assert (ids != plain["topk_ids"].cpu().numpy()).any()
+
+
 def _scale_bf16_bits(bits: np.ndarray, s: float) -> np.ndarray:
     """bf16 bit patterns times a power of two (exact inside the bf16 range)."""
     f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(s)
