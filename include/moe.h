@@ -36,8 +36,10 @@
  *  - Device-side preconditions that the host cannot see (expert ids in
  *    [0, E), offsets consistent with P) are the caller's contract; the plan
  *    produced by moe_dispatch_plan always satisfies them.
- *  - Limits: 1 <= E <= 512, 1 <= k <= E, T*k < 2^31.  bf16: H and I are
- *    multiples of 64.  f32: H multiple of 8, I multiple of 16.
+ *  - Limits: 1 <= E <= 512, 1 <= k <= E, T*k < 2^31.  bf16: H a multiple of
+ *    64, I (and the shared expert's I) a multiple of 32, which admits the
+ *    expert widths of 8-way tensor-parallel slices (768 / 8 = 96).  f32: H
+ *    multiple of 8, I multiple of 16.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -49,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 #define MOE_MAX_EXPERTS 512
 
 typedef enum moe_status {
@@ -64,6 +66,13 @@ typedef enum moe_dtype {
   MOE_DTYPE_F32 = 0,
   MOE_DTYPE_BF16 = 1
 } moe_dtype;
+
+/* Projection of one expert, as a per-expert checkpoint names it. */
+typedef enum moe_proj {
+  MOE_PROJ_GATE = 0, /* gate_proj (w1) [I, H] */
+  MOE_PROJ_UP = 1,   /* up_proj (w3)   [I, H] */
+  MOE_PROJ_DOWN = 2  /* down_proj (w2) [H, I] */
+} moe_proj;
 
 /* MOE_ABI_VERSION of the built library. */
 int moe_abi_version(void);
@@ -286,6 +295,40 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight,
                        int out_dtype, void* output,
                        int32_t* topk_ids_out, float* topk_weights_out, float* router_logits_out,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Tensor-parallel expert weight loader: one projection of one expert, the
+ * slice that rank tp_rank of tp_size owns, copied into the rank's fused
+ * buffers (the w13 / w2 that moe_grouped_ffn and moe_forward read).
+ * [modelexpress refit test "test_reshard_refit_moe_experts.py": the module
+ *  docstring gives the destination w13 [local_experts, 2*inter_per_tp,
+ *  hidden]; FusedMoEModel._expert_loader takes the rank's rows of the source
+ *  and writes them to the member half of the expert's slot, gate (w1) low,
+ *  up (w3) high]
+ *
+ * With Ip = intermediate_size / tp_size the rank owns the intermediate
+ * indices [tp_rank*Ip, tp_rank*Ip + Ip):
+ *   MOE_PROJ_GATE / MOE_PROJ_UP: src [I, H];
+ *     w13[expert, m*Ip + i, :] = src[tp_rank*Ip + i, :]   (m = 0 gate, 1 up)
+ *     dst is w13 [local_experts, 2*Ip, H].
+ *   MOE_PROJ_DOWN: src [H, I];
+ *     w2[expert, h, i] = src[h, tp_rank*Ip + i]
+ *     dst is w2 [local_experts, H, Ip].  The pages print the w13 loader only;
+ *     the down projection is split along the same intermediate index, its
+ *     columns, which makes the ranks' layer outputs add up to the unsliced
+ *     layer's output (the all-reduce of tensor parallelism).
+ * Elements are copied bit for bit; dtype only gives their size.  Unlike every
+ * other entry point, src may be host or device memory (contiguous row-major);
+ * dst is device memory, caller-owned.  The copy is enqueued on `stream`; a
+ * host src must stay valid until the stream has passed the copy.
+ * Errors: INVALID_ARG for NULL pointers, sizes < 1, tp_size < 1, tp_rank not
+ * in [0, tp_size), expert not in [0, local_experts), an unknown proj, or a
+ * tp_size that does not divide intermediate_size; MOE_ERR_HIP when the copy
+ * cannot be enqueued.
+ */
+moe_status moe_tp_load_expert(const void* src, int proj, int64_t hidden_size, int64_t intermediate_size,
+                              int tp_size, int tp_rank, int64_t expert, int64_t local_experts, int dtype,
+                              void* dst, void* stream);
 
 /*
  * Kernel timing for measurement tools.  While enabled, every kernel the

@@ -8,7 +8,8 @@ Pages cited (by title and section):
 * [diffulex] API reference "diffulex.moe": sections "diffulex.moe.topk",
   "diffulex.moe.layer".
 * [refit] modelexpress test "test_reshard_refit_moe_experts.py": the module
-  docstring and class ``FusedMoEModel`` (fused ``w13`` = gate rows then up rows).
+  docstring and class ``FusedMoEModel`` (fused ``w13`` = gate rows then up rows;
+  its expert loader takes the tensor-parallel rank's rows of each source).
 * [ep_dispatch] metrale "ep_dispatch.rs": ``EpRoutingTable``,
   ``build_ep_routing_table`` and its tests.
 
@@ -31,6 +32,10 @@ design notes of the repository):
   topk_group best groups are kept (equal scores: the lower group), and the
   top-k is taken among their experts by the plain rule.  Weights follow the
   plain router's rule (softmax over all experts, renormalised over the k).
+* tensor parallelism ([refit] slices only the gate/up sources): the down
+  projection ``[H, I]`` is split along the same intermediate index, i.e. its
+  columns, so that the ranks' layer outputs add up to the unsliced layer's;
+  a shared expert is split the same way, router and gate are replicated.
 
 Everything is float64; bf16 inputs are widened exactly and nothing is rounded
 on the way.  This module imports NumPy only.
@@ -60,6 +65,8 @@ __all__ = [
     "forward",
     "token_outputs",
     "ep_routing_table",
+    "tp_load_expert",
+    "tp_slice",
 ]
 
 
@@ -397,3 +404,65 @@ def ep_routing_table(gate_indices, gate_weights, num_tokens: int, top_k: int,
         "remote_expert_ids": gi[~local].astype(np.uint32),
         "remote_weights": gw[~local].astype(np.float32),
     }
+
+
+# --------------------------------------------------------------------------
+# tensor-parallel expert slices  ([refit] module docstring and
+# FusedMoEModel._expert_loader)
+# --------------------------------------------------------------------------
+def tp_load_expert(w13: np.ndarray, w2: np.ndarray, expert: int, gate: np.ndarray, up: np.ndarray,
+                   down: np.ndarray, tp_size: int, tp_rank: int) -> None:
+    """Write rank ``tp_rank``'s slice of one expert into per-rank fused buffers.
+
+    Sources are the expert's full per-expert matrices: ``gate``/``up``
+    ``[I, H]`` (HF ``gate_proj``/``up_proj``) and ``down`` ``[H, I]``
+    (``down_proj``).  With ``Ip = I / tp_size`` the rank owns intermediate
+    indices ``tp_rank*Ip .. tp_rank*Ip + Ip - 1``.  [refit] ``_expert_loader``:
+    the rank's rows of the source go to member half ``member*Ip`` of the
+    destination slot, member 0 for gate (w1) and 1 for up (w3), so
+    ``w13 [E, 2*Ip, H]``.  ``w2 [E, H, Ip]`` receives the same indices as
+    columns of ``down`` (reading: the pages print no down-projection loader).
+    Plain copies of stored values, any stored dtype.  Raises ``ValueError``
+    when ``I`` is not a multiple of ``tp_size`` or a shape disagrees.
+    """
+    I, H = gate.shape
+    if tp_size < 1 or not 0 <= tp_rank < tp_size or I % tp_size:
+        raise ValueError("tp_size must divide the intermediate size and 0 <= tp_rank < tp_size")
+    Ip = I // tp_size
+    if up.shape != (I, H) or down.shape != (H, I) or w13.shape[1:] != (2 * Ip, H) or w2.shape[1:] != (H, Ip):
+        raise ValueError("shape mismatch")
+    rows = slice(tp_rank * Ip, tp_rank * Ip + Ip)
+    for member, src in ((0, gate), (1, up)):
+        w13[expert, member * Ip:member * Ip + Ip, :] = src[rows, :]
+    w2[expert, :, :] = down[:, rows]
+
+
+def tp_slice(inputs: Dict[str, np.ndarray], tp_size: int, tp_rank: int) -> Dict[str, np.ndarray]:
+    """The layer inputs one tensor-parallel rank holds: every routed expert
+    (and the shared expert, as one more slot) loaded by ``tp_load_expert``
+    from its per-expert sources; tokens, router, bias and shared gate are
+    replicated.  Summing ``forward(tp_slice(inputs, G, r))["out"]`` over
+    ``r < G`` gives ``forward(inputs)["out"]`` up to rounding, since the
+    expert MLP is a sum over intermediate indices and everything after it is
+    linear."""
+    res = dict(inputs)
+    pairs = [("w13", "w2")]
+    if "shared_w13" in inputs:
+        pairs.append(("shared_w13", "shared_w2"))
+    for k13, k2 in pairs:
+        full13, full2 = inputs[k13], inputs[k2]
+        stacked = full13.ndim == 2  # the shared expert: one slot, no expert axis
+        f13 = full13[None] if stacked else full13
+        f2 = full2[None] if stacked else full2
+        E, twoI, H = f13.shape
+        I = twoI // 2
+        if I % tp_size:
+            raise ValueError("tp_size must divide the intermediate size")
+        Ip = I // tp_size
+        d13 = np.zeros((E, 2 * Ip, H), dtype=f13.dtype)
+        d2 = np.zeros((E, H, Ip), dtype=f2.dtype)
+        for e in range(E):
+            tp_load_expert(d13, d2, e, w13_gate(f13, e), w13_up(f13, e), f2[e], tp_size, tp_rank)
+        res[k13] = d13[0] if stacked else d13
+        res[k2] = d2[0] if stacked else d2
+    return res

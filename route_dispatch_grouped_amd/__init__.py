@@ -8,8 +8,11 @@ HIP kernels; there is no Python or CPU fallback.  Importing works without a
 GPU; the first call raises if the library is missing.
 
 Entry points (same names as the C ABI):
-  moe_router_topk, moe_dispatch_plan, moe_grouped_ffn, moe_combine, moe_forward
-plus ``MoeLayer``, a bound layer with a reusable workspace (the "explicit
+  moe_router_topk, moe_router_topk_grouped, moe_dispatch_plan,
+  moe_ep_routing_table, moe_grouped_ffn, moe_combine, moe_forward,
+  moe_tp_load_expert
+plus ``moe_tp_slice_experts`` (one tensor-parallel rank's fused weights,
+loaded expert by expert through moe_tp_load_expert) and ``MoeLayer``, a bound layer with a reusable workspace (the "explicit
 layer" of the DWDP README's ``build_reference``).
 """
 from __future__ import annotations
@@ -38,6 +41,11 @@ __all__ = [
     "moe_combine",
     "moe_forward",
     "moe_forward_workspace_size",
+    "moe_tp_load_expert",
+    "moe_tp_slice_experts",
+    "MOE_PROJ_GATE",
+    "MOE_PROJ_UP",
+    "MOE_PROJ_DOWN",
     "MoeLayer",
     "profile_enable",
     "profile_collect",
@@ -46,6 +54,9 @@ __all__ = [
 MOE_OK = 0
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
+MOE_PROJ_GATE = 0
+MOE_PROJ_UP = 1
+MOE_PROJ_DOWN = 2
 
 _c_void_p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -76,6 +87,8 @@ _SIGNATURES = {
     "moe_forward": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                            _i64, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _c_void_p, _c_void_p,
                            _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "moe_tp_load_expert": (_int, [_c_void_p, _int, _i64, _i64, _int, _int, _i64, _i64, _int, _c_void_p,
+                                  _c_void_p]),
     "moe_profile_enable": (None, [_int]),
     "moe_profile_collect": (_int, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(_i64), _int]),
@@ -350,6 +363,67 @@ def moe_combine(packed_expert_outputs: torch.Tensor, inverse_permutation: torch.
                          _dtype_code(out_dtype), _ptr(out), _stream(stream))
     _check("moe_combine", st)
     return out
+
+
+def moe_tp_load_expert(src: torch.Tensor, proj: int, dst: torch.Tensor, tp_size: int, tp_rank: int, expert: int,
+                       stream=None) -> None:
+    """Copy rank ``tp_rank``'s slice of one expert projection into the rank's
+    fused buffer (include/moe.h: moe_tp_load_expert).
+
+    ``src``: the full per-expert matrix, ``[I, H]`` for MOE_PROJ_GATE /
+    MOE_PROJ_UP, ``[H, I]`` for MOE_PROJ_DOWN; a GPU or CPU tensor.  ``dst``:
+    ``w13 [E, 2*Ip, H]`` (gate/up) or ``w2 [E, H, Ip]`` (down) on the GPU,
+    ``Ip = I / tp_size``.  A CPU source is waited for before returning, so the
+    caller may free it at once.
+    """
+    if not isinstance(src, torch.Tensor) or not src.is_contiguous() or src.dim() != 2:
+        raise ValueError("src must be a contiguous 2-D tensor")
+    if src.device.type not in ("cuda", "cpu"):
+        raise ValueError("src must be a GPU or CPU tensor")
+    _need(dst, "dst", None, src.dtype)
+    if dst.dim() != 3:
+        raise ValueError("dst must be [E, 2*Ip, H] or [E, H, Ip]")
+    if proj == MOE_PROJ_DOWN:
+        H, I = src.shape
+    else:
+        I, H = src.shape
+    if tp_size >= 1 and I % tp_size == 0:
+        Ip = I // tp_size
+        want = (dst.shape[0], H, Ip) if proj == MOE_PROJ_DOWN else (dst.shape[0], 2 * Ip, H)
+        _need(dst, "dst", want, src.dtype)
+    lib = load_library()
+    _check("moe_tp_load_expert",
+           lib.moe_tp_load_expert(_ptr(src), int(proj), H, I, int(tp_size), int(tp_rank), int(expert),
+                                  dst.shape[0], _dtype_code(src.dtype), _ptr(dst), _stream(stream)))
+    if src.device.type == "cpu":
+        (stream if stream is not None else torch.cuda.current_stream()).synchronize()
+
+
+def moe_tp_slice_experts(w13: torch.Tensor, w2: torch.Tensor, tp_size: int, tp_rank: int, stream=None):
+    """One tensor-parallel rank's ``(w13 [E, 2*Ip, H], w2 [E, H, Ip])`` from the
+    unsliced fused ``w13 [E, 2I, H]`` and ``w2 [E, H, I]`` (GPU or CPU): the
+    gate rows, up rows and down columns of every expert are loaded by
+    ``moe_tp_load_expert``.  A 2-D ``[2I, H]`` / ``[H, I]`` pair (a shared
+    expert) gives a 2-D pair."""
+    flat = w13.dim() == 2
+    if flat:
+        w13, w2 = w13.unsqueeze(0), w2.unsqueeze(0)
+    if w13.dim() != 3 or w2.dim() != 3 or w13.shape[0] != w2.shape[0] or w13.shape[1] % 2:
+        raise ValueError("w13 must be [E, 2I, H] and w2 [E, H, I]")
+    E, twoI, H = w13.shape
+    I = twoI // 2
+    if tuple(w2.shape) != (E, H, I):
+        raise ValueError(f"w2 length mismatch: expected shape {(E, H, I)}, got {tuple(w2.shape)}")
+    if tp_size < 1 or I % tp_size:
+        raise ValueError("tp_size must divide the intermediate size")
+    Ip = I // tp_size
+    d13 = torch.empty((E, 2 * Ip, H), dtype=w13.dtype, device="cuda")
+    d2 = torch.empty((E, H, Ip), dtype=w2.dtype, device="cuda")
+    for e in range(E):
+        moe_tp_load_expert(w13[e, :I], MOE_PROJ_GATE, d13, tp_size, tp_rank, e, stream)
+        moe_tp_load_expert(w13[e, I:], MOE_PROJ_UP, d13, tp_size, tp_rank, e, stream)
+        moe_tp_load_expert(w2[e], MOE_PROJ_DOWN, d2, tp_size, tp_rank, e, stream)
+    return (d13[0], d2[0]) if flat else (d13, d2)
 
 
 def moe_forward_workspace_size(T: int, H: int, E: int, k: int, I: int, Is: int, dtype: torch.dtype) -> int:

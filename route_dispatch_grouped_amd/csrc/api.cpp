@@ -73,7 +73,7 @@ moe_status check_buffer_bytes(int64_t T, int64_t H, int64_t k, int64_t I, int dt
 
 moe_status check_inter(int64_t I, int dtype, const char* name) {
   if (I < 1) return fail(MOE_ERR_INVALID_ARG, std::string(name) + " must be >= 1");
-  if (dtype == MOE_DTYPE_BF16 && I % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, std::string("bf16 needs ") + name + " % 64 == 0");
+  if (dtype == MOE_DTYPE_BF16 && I % 32 != 0) return fail(MOE_ERR_UNSUPPORTED, std::string("bf16 needs ") + name + " % 32 == 0");
   if (dtype == MOE_DTYPE_F32 && I % 16 != 0) return fail(MOE_ERR_UNSUPPORTED, std::string("f32 needs ") + name + " % 16 == 0");
   return MOE_OK;
 }
@@ -475,6 +475,37 @@ moe_status moe_ep_routing_table(const int32_t* gate_indices, int64_t gate_indice
                                          remote_token_indices, remote_expert_ids, remote_weights, counts, workspace,
                                          s),
                     "moe_ep_routing_table");
+}
+
+moe_status moe_tp_load_expert(const void* src, int proj, int64_t hidden_size, int64_t intermediate_size,
+                              int tp_size, int tp_rank, int64_t expert, int64_t local_experts, int dtype,
+                              void* dst, void* stream) {
+  REQUIRE_PTR(src);
+  REQUIRE_PTR(dst);
+  if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (proj != MOE_PROJ_GATE && proj != MOE_PROJ_UP && proj != MOE_PROJ_DOWN)
+    return fail(MOE_ERR_INVALID_ARG, "unknown proj");
+  if (hidden_size < 1 || intermediate_size < 1 || local_experts < 1)
+    return fail(MOE_ERR_INVALID_ARG, "hidden_size, intermediate_size and local_experts must be >= 1");
+  if (tp_size < 1 || tp_rank < 0 || tp_rank >= tp_size)
+    return fail(MOE_ERR_INVALID_ARG, "tp_rank must lie in [0, tp_size)");
+  if (intermediate_size % tp_size != 0) return fail(MOE_ERR_INVALID_ARG, "tp_size must divide intermediate_size");
+  if (expert < 0 || expert >= local_experts) return fail(MOE_ERR_INVALID_ARG, "expert must lie in [0, local_experts)");
+  const size_t es = dtype_size(dtype);
+  const size_t H = (size_t)hidden_size, I = (size_t)intermediate_size, Ip = I / (size_t)tp_size;
+  const size_t r = (size_t)tp_rank, e = (size_t)expert;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* sb = static_cast<const char*>(src);
+  char* db = static_cast<char*>(dst);
+  if (proj == MOE_PROJ_DOWN)  // H rows of Ip columns, taken from rows of I
+    return hip_status(hipMemcpy2DAsync(db + e * H * Ip * es, Ip * es, sb + r * Ip * es, I * es, Ip * es, H,
+                                       hipMemcpyDefault, s),
+                      "moe_tp_load_expert");
+  // Ip whole rows of H: one contiguous block on both sides
+  const size_t member = (proj == MOE_PROJ_UP) ? 1 : 0;
+  return hip_status(hipMemcpyAsync(db + (e * 2 * Ip + member * Ip) * H * es, sb + r * Ip * H * es, Ip * H * es,
+                                   hipMemcpyDefault, s),
+                    "moe_tp_load_expert");
 }
 
 // Split-K scratch of moe_grouped_ffn; with one expert the offsets may be

@@ -115,10 +115,17 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Per-tile DMA addressing: byte offsets of every slot this lane fetches.
+// a_cb / b_cb: byte offset of the lane's chunk inside a stage row; with
+// ktail (K not a multiple of BK) chunks at or past the end of a row are
+// fetched through an offset past the buffer (zeros).
 template <int BM, int BR>
 struct DmaPlan {
   uint32_t a_off[Tile<BM, BR>::A_MAX];
   uint32_t b_off[Tile<BM, BR>::B_PER];
+  uint32_t a_cb[Tile<BM, BR>::A_MAX];
+  uint32_t b_cb[Tile<BM, BR>::B_PER];
+  uint32_t row_bytes;
+  bool ktail;
 };
 
 // Raw buffer resource (gfx9 V#): 48-bit base, stride 0, size in bytes; loads
@@ -163,12 +170,16 @@ __device__ __forceinline__ void issue_stage(u32x4_t* buf, const DmaPlan<BM, BR>&
 #pragma unroll
   for (int qi = 0; qi < C::A_MAX; ++qi) {
     const int q = qi * 4 + wave;
-    if (qi < C::A_MIN || q < C::A_INSTR) dma16(buf + q * 64, ra, d.a_off[qi], kbytes);
+    uint32_t v = d.a_off[qi];
+    if (d.ktail && d.a_cb[qi] + (uint32_t)kbytes >= d.row_bytes) v = 0x80000000u;
+    if (qi < C::A_MIN || q < C::A_INSTR) dma16(buf + q * 64, ra, v, kbytes);
   }
 #pragma unroll
   for (int qi = 0; qi < C::B_PER; ++qi) {
     const int q = qi * 4 + wave;
-    dma16(buf + BM * 8 + q * 64, rb, d.b_off[qi], kbytes);
+    uint32_t v = d.b_off[qi];
+    if (d.ktail && d.b_cb[qi] + (uint32_t)kbytes >= d.row_bytes) v = 0x80000000u;
+    dma16(buf + BM * 8 + q * 64, rb, v, kbytes);
   }
 }
 
@@ -331,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
   const int per = (total + kXcds - 1) / kXcds;
   const int t_begin = xcd * per;
   const int t_end = min(total, t_begin + per);
-  const int KT_all = p.K / BK;
+  const int KT_all = (p.K + BK - 1) / BK;  // the last stage may be partly past K
   const int KTc = (KT_all + ksplit - 1) / ksplit;
   const uint32_t row_bytes = (uint32_t)p.K * 2u;
 
@@ -362,6 +373,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
       const int rr = min(r, rows - 1);
       const int grow = p.gather ? p.gather[m0 + rr] : (m0 + rr);
       d.a_off[qi] = (uint32_t)grow * row_bytes + (uint32_t)c * 16u;
+      d.a_cb[qi] = (uint32_t)c * 16u;
     }
 #pragma unroll
     for (int qi = 0; qi < C::B_PER; ++qi) {
@@ -373,7 +385,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
       const int col = (EPI == EPI_SWIGLU) ? n0 + (r & 127) : n0 + r;
       const int wr = (EPI == EPI_SWIGLU && r >= 128) ? p.up_row0 + col : col;
       d.b_off[qi] = (col < p.N) ? (uint32_t)wr * row_bytes + (uint32_t)c * 16u : 0x80000000u;
+      d.b_cb[qi] = (uint32_t)c * 16u;
     }
+    d.row_bytes = row_bytes;
+    d.ktail = (p.K % BK) != 0;
     const u32x4_t ra = make_rsrc(p.A, (uint32_t)p.a_rows * row_bytes);
     const int b_rows_total = (EPI == EPI_SWIGLU) ? 2 * p.up_row0 : p.N;
     const u32x4_t rb = make_rsrc(Bg, (uint32_t)b_rows_total * row_bytes);
@@ -1627,7 +1642,7 @@ int ksplit_for(int64_t M, int64_t G, bool grouped, int64_t N, int64_t K, GemmEpi
   }
   const int64_t bn = (epi == EPI_SWIGLU) ? 128 : 256;
   const int64_t tiles = ((M + bm - 1) / bm + (grouped ? groups : 0)) * ((N + bn - 1) / bn);
-  const int64_t KT = K / BK;
+  const int64_t KT = (K + BK - 1) / BK;
   int64_t ks = (kSplitTarget + tiles - 1) / tiles;
   if (ks > KT / kSplitMinStages) ks = KT / kSplitMinStages;
   if (ks <= 1) return 1;

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
     for code, text in [(0, b"MOE_OK"), (1, b"MOE_ERR_INVALID_ARG"), (2, b"MOE_ERR_UNSUPPORTED"),
                        (3, b"MOE_ERR_WORKSPACE"), (4, b"MOE_ERR_HIP")]:
         assert lib.moe_status_string(code) == text
@@ -112,7 +112,9 @@ def ffn(lib, T=4, H=64, E=8, k=2, I=64, dtype=BF16, ydt=F32, gather=P16, off=P16
 
 
 def test_grouped_ffn_validation(lib):
-    assert ffn(lib, I=96) == UNSUP
+    # bf16 expert widths: multiples of 32 (8-way TP slices of 768 are 96)
+    assert ffn(lib, I=80) == UNSUP and "% 32" in last(lib)
+    assert ffn(lib, I=96, wsb=1) == WS
     assert ffn(lib, ydt=3) == INVALID and "expert_out_dtype" in last(lib)
     assert ffn(lib, dtype=F32, ydt=BF16) == UNSUP and "bf16 layer" in last(lib)
     # fp32 expert outputs past 2 GiB would overflow the 32-bit store offsets;
@@ -210,3 +212,19 @@ def test_ep_routing_table_validation(lib):
     assert ep(lib, out=NULL) == INVALID
     need = lib.moe_ep_routing_table_workspace_size(2, 2)
     assert need > 0 and ep(lib, wsb=need - 1) == WS
+
+
+def test_tp_load_expert_validation(lib):
+    def load(src=P16, proj=0, H=64, I=96, G=2, r=0, e=0, E=4, dtype=BF16, dst=P16):
+        return lib.moe_tp_load_expert(src, proj, H, I, G, r, e, E, dtype, dst, NULL)
+    assert load(src=NULL) == INVALID and "src" in last(lib)
+    assert load(dst=NULL) == INVALID and "dst" in last(lib)
+    assert load(proj=3) == INVALID and "proj" in last(lib)
+    assert load(dtype=7) == INVALID and "dtype" in last(lib)
+    assert load(G=0) == INVALID and "tp_rank" in last(lib)
+    assert load(r=2) == INVALID and "tp_rank" in last(lib)
+    assert load(r=-1) == INVALID
+    assert load(G=5) == INVALID and "divide" in last(lib)
+    assert load(e=4) == INVALID and "expert" in last(lib)
+    assert load(e=-1) == INVALID
+    assert load(H=0) == INVALID and load(I=0) == INVALID and load(E=0) == INVALID

@@ -199,3 +199,83 @@ def test_empty_experts_are_skipped():
     ref = oracle.swiglu_expert(x, oracle.w13_gate(inp["w13"].astype(np.float64), 0),
                                oracle.w13_up(inp["w13"].astype(np.float64), 0), inp["w2"][0].astype(np.float64))
     assert np.allclose(y, ref, rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# tensor-parallel slices of the expert weights
+# --------------------------------------------------------------------------
+def test_tp_load_matches_page_bytes():
+    """modelexpress refit test: at TP_SIZE=2, rank 0 pulls INTER_PER_TP*HIDDEN*4
+    bytes from the start of expert 1's up_proj source into the w3 half of
+    expert 1's slot, which begins at byte 192 of the fused fp32 w13."""
+    g = json.load(open(os.path.join(GOLDEN, "w13_layout.json")))
+    H, I, E, G, r = g["hidden"], g["inter"], g["local_experts"], g["tp_size"], g["tp_rank"]
+    Ip = I // G
+    assert Ip == g["inter_per_tp"]
+    # distinct sources, marked so every element names where it came from
+    src = {m: (np.arange(I * H, dtype=np.float32) + 1000 * (m + 1)).reshape(I, H) for m in range(3)}
+    down = np.zeros((H, I), np.float32)
+    w13 = np.zeros((E, 2 * Ip, H), np.float32)
+    w2 = np.zeros((E, H, Ip), np.float32)
+    oracle.tp_load_expert(w13, w2, g["expert"], src[0], src[1], down, G, r)
+    flat = w13.reshape(-1)
+    landed = np.nonzero(flat >= 2000)[0]  # the up source's values (member 1)
+    assert landed.size * g["elsize"] == g["expected_pulled_bytes"]
+    assert landed.min() * g["elsize"] == g["expected_byte_offset"]
+    assert (np.diff(landed) == 1).all()
+    src_idx = flat[landed].astype(np.int64) - 2000
+    assert src_idx.min() * g["elsize"] == g["expected_src_min_byte"]
+    # the gate source fills the w1 half just below, expert 0 is untouched
+    gate_landed = np.nonzero((flat >= 1000) & (flat < 2000))[0]
+    assert gate_landed.min() * g["elsize"] == g["expected_byte_offset"] - Ip * H * g["elsize"]
+    assert not w13[0].any()
+    # rank 1 reads the next INTER_PER_TP rows of every source
+    oracle.tp_load_expert(w13, w2, 0, src[0], src[1], src[2].T.copy(), G, 1)
+    assert (w13[0, :Ip] == src[0][Ip:]).all() and (w13[0, Ip:] == src[1][Ip:]).all()
+    assert (w2[0] == src[2].T[:, Ip:]).all()
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4])
+def test_tp_ranks_sum_to_full_layer(G):
+    """The ranks' outputs add up to the unsliced layer (routed experts and the
+    gated shared expert), since the MLP sums over intermediate indices; a
+    slice that pairs the wrong gate/up/down indices breaks the sum."""
+    cfg, inp = tiny(seed=3, num_tokens=11, hidden_size=16, num_experts=6, top_k=3, intermediate_size=12,
+                    shared_intermediate_size=24)
+    assert "shared_w13" in inp
+    full = oracle.forward(inp, cfg.top_k)["out"]
+    parts = [oracle.forward(oracle.tp_slice(inp, G, r), cfg.top_k) for r in range(G)]
+    total = sum(p["out"] for p in parts)
+    assert np.max(np.abs(total - full)) <= 1e-12 * np.max(np.abs(full))
+    # every rank routes identically (router replicated)
+    for p in parts:
+        assert (p["ids"] == parts[0]["ids"]).all()
+    if G == 1:
+        s = oracle.tp_slice(inp, 1, 0)
+        for key in ("w13", "w2", "shared_w13", "shared_w2"):
+            assert (s[key] == inp[key]).all()
+
+
+def test_tp_rank_slices_partition_the_weights():
+    """Every stored value of the full layer lands in exactly one rank, once."""
+    cfg, inp = tiny(seed=4, intermediate_size=8)
+    G = 4
+    s = [oracle.tp_slice(inp, G, r) for r in range(G)]
+    I = cfg.intermediate_size
+    Ip = I // G
+    gate = np.concatenate([x["w13"][:, :Ip] for x in s], axis=1)
+    up = np.concatenate([x["w13"][:, Ip:] for x in s], axis=1)
+    assert (gate == inp["w13"][:, :I]).all() and (up == inp["w13"][:, I:]).all()
+    assert (np.concatenate([x["w2"] for x in s], axis=2) == inp["w2"]).all()
+
+
+def test_tp_load_rejects_bad_shapes():
+    w13 = np.zeros((2, 4, 3), np.float32)
+    w2 = np.zeros((2, 3, 2), np.float32)
+    src = np.zeros((4, 3), np.float32)
+    with pytest.raises(ValueError):
+        oracle.tp_load_expert(w13, w2, 0, src, src, np.zeros((3, 4), np.float32), 3, 0)  # 4 % 3
+    with pytest.raises(ValueError):
+        oracle.tp_load_expert(w13, w2, 0, src, src, np.zeros((3, 4), np.float32), 2, 2)  # rank >= size
+    with pytest.raises(ValueError):
+        oracle.tp_load_expert(w13, w2, 0, src, src, np.zeros((4, 3), np.float32), 2, 0)  # down transposed
