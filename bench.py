@@ -42,14 +42,13 @@ def log(msg):
 
 def y_bytes_per_value(cfg):
     """Bytes per packed expert output value as the layer forward stores them:
-    bf16 layers whose down projection runs on the pipelined 256-row kernel (at
-    least 96 rows per expert on average, I/32 a multiple of 4 and at least 8)
-    keep fp16 values plus one int32 exponent per 64 columns; otherwise fp32."""
+    bf16 layers whose down projection runs on a 256-row kernel (at least 96
+    rows per expert on average) keep fp16 values plus one int32 exponent per
+    64 columns; otherwise fp32."""
     P = cfg.num_tokens * cfg.top_k
     groups = min(cfg.num_experts, P)
     avg = (P + groups - 1) // groups
-    kt = cfg.intermediate_size // 32
-    if cfg.dtype == "bf16" and avg >= 96 and kt >= 8 and kt % 4 == 0:
+    if cfg.dtype == "bf16" and avg >= 96 and cfg.hidden_size % 64 == 0:
         return 2.0 + 4.0 / 64
     return 4.0
 
@@ -218,6 +217,53 @@ def decode_measure(rdg, torch, seed, steps=400, warmup=50):
             "value": round(cfg.num_tokens / dt, 1), "unit": "tokens/s", "experts_touched": touched,
             "weight_bytes_per_step": nbytes, "achieved": round(gbs, 1), "achieved_unit": "GB/s",
             "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def tp_measure(rdg, torch, cfg, d, steps, warmup=10, sizes=(2, 4, 8)):
+    """One tensor-parallel rank's layer at the headline shape: the experts'
+    intermediate size split over tp ranks (weights sliced from the full ones
+    by moe_tp_load_expert), router replicated.  Per rank: ms per forward and
+    the grouped FFN's fraction of the bf16 peak (its flops are 1/tp of the
+    full layer's).  The cross-rank sum of the outputs is not part of it."""
+    res = []
+    for tp in sizes:
+        if cfg.intermediate_size % tp:
+            continue
+        w13, w2 = rdg.moe_tp_slice_experts(d["w13"], d["w2"], tp, 0)
+        layer = rdg.MoeLayer(d["router_weight"], w13, w2, cfg.top_k, router_bias=d.get("router_bias"),
+                             renormalize=cfg.renormalize)
+        x = d["x"]
+        layer.reserve(cfg.num_tokens, x.device)
+        for _ in range(warmup):
+            layer(x)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            layer(x)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        rdg.profile_enable(True)
+        for _ in range(steps):
+            layer(x)
+        torch.cuda.synchronize()
+        rdg.profile_enable(False)
+        k = rdg.profile_collect()
+        Ip = cfg.intermediate_size // tp
+        ent = {"tp": tp, "intermediate_size": Ip, "ms_per_step": round(dt * 1e3, 4),
+               "value": round(cfg.num_tokens / dt, 1), "unit": "tokens/s",
+               "kernels_us": {n: round(ms / c * 1e3, 2) for n, (ms, c) in k.items()}}
+        if "ffn_gate_up_bf16" in k and "ffn_down_bf16" in k:
+            t_ffn = sum(k[n][0] / k[n][1] for n in ("ffn_gate_up_bf16", "ffn_down_bf16")) / 1e3
+            fl = 6.0 * cfg.num_tokens * cfg.top_k * cfg.hidden_size * Ip
+            ent["grouped_ffn"] = {"tflops": round(fl / t_ffn / 1e12, 2),
+                                  "frac_bf16_peak": round(fl / t_ffn / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                  "us": round(t_ffn * 1e6, 2)}
+        res.append(ent)
+        log(f"[bench] tp{tp} rank layer (I={Ip}): {ent['ms_per_step']} ms/step, "
+            f"ffn {ent.get('grouped_ffn')}")
+        del layer, w13, w2
+        torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -400,6 +446,10 @@ def main():
         log(f"[bench] {SECONDARY_WORKLOAD}: {secondary['ms_per_step']} ms/step, {secondary['achieved']} GB/s "
             f"({100 * secondary['frac_hbm_peak']:.1f} % of HBM peak)")
 
+    tp = None
+    if not args.no_secondary and cfg.name == DEFAULT_WORKLOAD and cfg.dtype == "bf16":
+        tp = tp_measure(rdg, torch, cfg, d, args.steps)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
@@ -430,6 +480,7 @@ def main():
         "ep_routing_table": ep,
         "router_topk_grouped": grouped,
         "decode": secondary,
+        "tp_sliced": tp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

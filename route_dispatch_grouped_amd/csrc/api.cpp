@@ -714,7 +714,7 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
       if (e != hipSuccess) return hip_status(e, "moe_forward(join)");
     }
   }
-  // Large batches (the pipelined 256-row down kernel): the packed expert
+  // Large batches (the 256-row down kernels): the packed expert
   // outputs go out as fp16 with a power-of-two scale per (row, 64 columns),
   // half the bytes of fp32 for the down projection to write and the combine
   // to read, with 11 significant bits (bf16 storage would keep 8 and about
@@ -728,7 +728,7 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
     probe.G = E;
     probe.offsets = L.offsets;
     probe.K = I;
-    if (moe::grouped_gemm_uses_pipe(probe) && H % moe::kF16SegCols == 0) {
+    if (moe::grouped_gemm_has_f16s(probe) && H % moe::kF16SegCols == 0) {
       y_format = moe::Y_F16S;
       y_scale = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(L.y) + align_up((size_t)P * H * 2));
     }

@@ -90,6 +90,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
 }
 
+// Exponent k that brings a segment whose largest magnitude is m into
+// [2^14, 2^15) (0 for an all-zero segment; below the normal range the
+// smallest normal's k is used, and Inf/NaN keep their value).
+__device__ __forceinline__ int f16s_exponent(float m) {
+  const uint32_t eb = (__float_as_uint(m) >> 23) & 0xFFu;
+  if (m == 0.f) return 0;
+  const int e = (eb == 0) ? -126 : (int)eb - 127;
+  return 14 - e;
+}
+
+// two values rounded to fp16 (nearest even; one v_cvt_pk_f16_f32), the first
+// in the low half
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
 // silu(g) * u = g * u / (1 + e^-g), with the hardware reciprocal (about 1 ulp)
 // instead of an IEEE division: the result is rounded to bf16 right after.
 // e^-g overflowing to +inf gives exactly 0, the limit of silu at -inf.
@@ -851,6 +870,16 @@ __device__ __forceinline__ void big_issue(u32x4_t* buf, const BigPlan& d, u32x4_
   for (int qi = 0; qi < 4; ++qi) dma16(buf + Big::A_SLOTS + (qi * 4 + wave) * 64, rb, d.b_off[qi], kbytes);
 }
 
+// Buffer resource for the stage at byte offset kbytes of a row: a stage at or
+// past the end of K (a K loop padded to whole groups of four stages) reads
+// through a zero-length buffer, which lands zeros in LDS and moves no data.
+// PAD false (K a whole number of groups): the resource unchanged, no test.
+template <bool PAD>
+__device__ __forceinline__ u32x4_t stage_rsrc(u32x4_t r, int kbytes, uint32_t row_bytes) {
+  if (PAD && (uint32_t)kbytes >= row_bytes) r[2] = 0u;
+  return r;
+}
+
 // Fragments of one stage for one wave: [k16 half][sub-tile].
 struct BigFrags {
   bf16x8_t a[2][4];
@@ -1119,6 +1148,38 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_big_kernel(GemmArg
             *reinterpret_cast<uint2*>(out + col) = v;
           }
         }
+      } else if (EPI == EPI_F16S) {
+        // as in the pipelined kernel: per 64-column segment of the row, one
+        // exponent (from this lane's 32 values and those of lane ^ 32, which
+        // holds the same row) and 64 scaled fp16 values; N % 64 == 0, so a
+        // segment is live or dead as a whole
+        uint16_t* out = reinterpret_cast<uint16_t*>(p.out) + (int64_t)(m0 + row) * p.ldo;
+        const int64_t nseg = p.ldo / kF16SegCols;
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) {
+          float m = 0.f;
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(acc[i][2 * sg + jj][e]));
+          m = fmaxf(m, __shfl_xor(m, 32, 64));
+          const int kx = f16s_exponent(m);
+          const int seg_col = n0 + 128 * wn + 64 * sg;
+          if (seg_col >= p.N) continue;
+          if (lane < 32) p.scale_out[(int64_t)(m0 + row) * nseg + seg_col / kF16SegCols] = kx;
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * sg + jj;
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int col = n0 + 128 * wn + 32 * j + 8 * gq + 4 * (lane >> 5);
+              uint2 v;
+              v.x = pack_f16x2(ldexpf(acc[i][j][4 * gq], kx), ldexpf(acc[i][j][4 * gq + 1], kx));
+              v.y = pack_f16x2(ldexpf(acc[i][j][4 * gq + 2], kx), ldexpf(acc[i][j][4 * gq + 3], kx));
+              *reinterpret_cast<uint2*>(out + col) = v;
+            }
+          }
+        }
       } else if (EPI == EPI_BF16) {
         uint16_t* out = reinterpret_cast<uint16_t*>(p.out) + (int64_t)(m0 + row) * p.ldo;
 #pragma unroll
@@ -1179,25 +1240,6 @@ struct PipeEpi {
   static constexpr int kStores = (EPI == EPI_SWIGLU) ? 32 : (EPI == EPI_F16S) ? 72 : 64;
 };
 
-// Exponent k that brings a segment whose largest magnitude is m into
-// [2^14, 2^15) (0 for an all-zero segment; below the normal range the
-// smallest normal's k is used, and Inf/NaN keep their value).
-__device__ __forceinline__ int f16s_exponent(float m) {
-  const uint32_t eb = (__float_as_uint(m) >> 23) & 0xFFu;
-  if (m == 0.f) return 0;
-  const int e = (eb == 0) ? -126 : (int)eb - 127;
-  return 14 - e;
-}
-
-// two values rounded to fp16 (nearest even; one v_cvt_pk_f16_f32), the first
-// in the low half
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-  const f32x2_t v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_clamped() {
   wait_vmcnt<(N > 63 ? 63 : N)>();
@@ -1238,8 +1280,9 @@ struct PipeNext {
 // One tile's K loop.  On entry stages 0..3 of this tile are in flight (or
 // landed); `after_epi` says whether the previous tile's epilogue stores were
 // issued after them.  With nx.has, the loop stages the next tile's row
-// indices, builds its plan into `dn` and issues its stages 0..3.
-template <int EPI, int LIVE>
+// indices, builds its plan into `dn` and issues its stages 0..3.  PAD: the
+// K loop is padded to whole groups of 4 stages.
+template <int EPI, int LIVE, bool PAD>
 __device__ __forceinline__ void pipe_kloop(f32x16_t (&acc)[4][4], u32x4_t* s0, u32x4_t* s1, u32x4_t* s2,
                                            u32x4_t* s3, int* s_gidx, const GemmArgs& p, const BigPlan& d,
                                            u32x4_t ra, u32x4_t rb, BigPlan& dn, u32x4_t rbn, const PipeNext& nx,
@@ -1288,17 +1331,19 @@ __device__ __forceinline__ void pipe_kloop(f32x16_t (&acc)[4][4], u32x4_t* s0, u
       }
       const BigPlan& dd = last ? dn : d;
       const u32x4_t rbs = last ? rbn : rb;
+      const u32x4_t ras = stage_rsrc<PAD>(ra, kbytes, row_bytes);
+      const u32x4_t rbk = stage_rsrc<PAD>(rbs, kbytes, row_bytes);
       if constexpr (LIVE >= 1) {
-        big_step<EPI, LIVE>(acc, cur, nxt, bufs[u], bufs[(u + 1) & 3], dma, kbytes, dd, ra, rbs, wave, a_slot,
+        big_step<EPI, LIVE>(acc, cur, nxt, bufs[u], bufs[(u + 1) & 3], dma, kbytes, dd, ras, rbk, wave, a_slot,
                             b_slot);
       } else {
-        if (dma) big_issue(bufs[u], dd, ra, rbs, wave, kbytes);
+        if (dma) big_issue(bufs[u], dd, ras, rbk, wave, kbytes);
       }
     }
   }
 }
 
-template <int EPI>
+template <int EPI, bool PAD>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmArgs p) {
   constexpr int BM = Big::BM;
   constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
@@ -1328,7 +1373,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
   const int per = (total + kXcds - 1) / kXcds;
   const int t_begin = xcd * per;
   const int t_end = min(total, t_begin + per);
-  const int KT = p.K / Big::KB;
+  const int KT = (p.K / Big::KB + 3) & ~3;  // whole groups of 4 stages; stages past K read zeros
   const uint32_t row_bytes = (uint32_t)p.K * 2u;
   int t = t_begin + slot;
   if (t >= t_end) return;  // whole workgroup, after the last barrier it takes part in
@@ -1376,9 +1421,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
   }
   u32x4_t rb = make_rsrc(p.B + (int64_t)tc.g * p.b_group_stride, b_bytes);
   big_issue(st0, d, ra, rb, wave, 0);
-  big_issue(st1, d, ra, rb, wave, 1 * Big::KB * 2);
-  big_issue(st2, d, ra, rb, wave, 2 * Big::KB * 2);
-  big_issue(st3, d, ra, rb, wave, 3 * Big::KB * 2);
+  big_issue(st1, d, stage_rsrc<PAD>(ra, 1 * Big::KB * 2, row_bytes), stage_rsrc<PAD>(rb, 1 * Big::KB * 2, row_bytes),
+            wave, 1 * Big::KB * 2);
+  big_issue(st2, d, stage_rsrc<PAD>(ra, 2 * Big::KB * 2, row_bytes), stage_rsrc<PAD>(rb, 2 * Big::KB * 2, row_bytes),
+            wave, 2 * Big::KB * 2);
+  big_issue(st3, d, stage_rsrc<PAD>(ra, 3 * Big::KB * 2, row_bytes), stage_rsrc<PAD>(rb, 3 * Big::KB * 2, row_bytes),
+            wave, 3 * Big::KB * 2);
 
   bool after_epi = false;
   while (true) {
@@ -1404,10 +1452,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
     const int units = (rows + 31) >> 5;
     const int live = __builtin_amdgcn_readfirstlane(min(4, (units - wm + 1) >> 1));
     switch (live) {
-#define MOE_PIPE_CASE(n)                                                                                       \
-  case n:                                                                                                      \
-    pipe_kloop<EPI, n>(acc, st0, st1, st2, st3, s_gidx, p, d, ra, rb, dn, rbn, nx, after_epi, wave, lane, KT, \
-                       row_bytes, a_slot, b_slot);                                                             \
+#define MOE_PIPE_CASE(n)                                                                                        \
+  case n:                                                                                                       \
+    pipe_kloop<EPI, n, PAD>(acc, st0, st1, st2, st3, s_gidx, p, d, ra, rb, dn, rbn, nx, after_epi, wave, lane, \
+                            KT, row_bytes, a_slot, b_slot);                                                     \
     break;
       MOE_PIPE_CASE(0) MOE_PIPE_CASE(1) MOE_PIPE_CASE(2) MOE_PIPE_CASE(3) MOE_PIPE_CASE(4)
 #undef MOE_PIPE_CASE
@@ -1758,9 +1806,23 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t s, const char* name) {
   grid = ((grid + kXcds - 1) / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
   profile_begin(name, s);
-  hipLaunchKernelGGL((grouped_gemm_bf16_pipe_kernel<EPI>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  if ((a.K / Big::KB) % 4 != 0)
+    hipLaunchKernelGGL((grouped_gemm_bf16_pipe_kernel<EPI, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((grouped_gemm_bf16_pipe_kernel<EPI, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   profile_end(s);
   return hipGetLastError();
+}
+
+// The pipelined 256-row kernel runs K loops in whole groups of four stages,
+// padding with stages that read zeros; it takes a K loop when the padding
+// adds at most a third to it, and with gathered rows only from 8 stages on
+// (the next tile's row indices are staged 8 steps before its first DMA).
+bool pipe_fits(const GemmArgs& a) {
+  const int64_t KT = a.K / Big::KB;
+  const int64_t KTp = (KT + 3) & ~(int64_t)3;
+  if (3 * KTp > 4 * KT) return false;
+  return a.gather ? KTp >= 8 : KTp >= 4;
 }
 
 template <int EPI>
@@ -1775,8 +1837,7 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s, const char* name) {
     case 128: return launch_bm<128, EPI>(a, s, name);
     default: break;
   }
-  const int64_t KT = a.K / Big::KB;
-  if (KT >= 8 && KT % 4 == 0) return launch_pipe<EPI>(a, s, name);
+  if (pipe_fits(a)) return launch_pipe<EPI>(a, s, name);
   return launch_big<EPI>(a, s, name);
 }
 
@@ -1803,18 +1864,18 @@ size_t grouped_gemm_partial_bytes(int64_t M, int64_t G, bool grouped, int64_t N,
   return (size_t)ks * (size_t)M * (size_t)ldp * sizeof(float);
 }
 
-bool grouped_gemm_uses_pipe(const GemmArgs& a) {
+bool grouped_gemm_has_f16s(const GemmArgs& a) {
   const int64_t groups = a.offsets ? (a.G < a.M ? a.G : a.M) : 1;
-  const int64_t KT = a.K / Big::KB;
-  return a.M > 0 && pick_bm(a.M, groups) == 0 && KT >= 8 && KT % 4 == 0;
+  return a.M > 0 && pick_bm(a.M, groups) == 0;
 }
 
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, GemmEpilogue epi, hipStream_t s, const char* name) {
   if (a.M <= 0) return hipSuccess;
   if (epi == EPI_F16S) {
-    if (!grouped_gemm_uses_pipe(a) || a.scale_out == nullptr || a.N % kF16SegCols != 0 || a.ldo % kF16SegCols != 0)
+    if (!grouped_gemm_has_f16s(a) || a.scale_out == nullptr || a.N % kF16SegCols != 0 || a.ldo % kF16SegCols != 0)
       return hipErrorInvalidValue;
-    return launch_pipe<EPI_F16S>(a, s, name);
+    if (pipe_fits(a)) return launch_pipe<EPI_F16S>(a, s, name);
+    return launch_big<EPI_F16S>(a, s, name);
   }
   switch (epi) {
     case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(a, s, name);

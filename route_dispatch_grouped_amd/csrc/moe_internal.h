@@ -60,9 +60,9 @@ constexpr int kTileCounterInts = 8;
 // True when the grouped GEMM for `a` runs the large-group kernel (which uses
 // a.tile_counter when given).
 bool grouped_gemm_uses_counter(const GemmArgs& a);
-// True when `a` runs on the pipelined 256-row kernel (the only one with the
-// EPI_F16S epilogue).
-bool grouped_gemm_uses_pipe(const GemmArgs& a);
+// True when `a` runs on a 256-row kernel (plain or pipelined), the kernels
+// with the EPI_F16S epilogue.
+bool grouped_gemm_has_f16s(const GemmArgs& a);
 hipError_t launch_zero_ints(int* p, int n, hipStream_t s);
 
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, GemmEpilogue epi, hipStream_t s, const char* name);

@@ -391,12 +391,15 @@ def _scale_bf16_bits(bits: np.ndarray, s: float) -> np.ndarray:
 
 
 @pytest.mark.parametrize("scale", [2.0 ** 12, 2.0 ** -20])
-def test_forward_large_batch_output_range(scale):
+@pytest.mark.parametrize("name", ["bf16_pipe_tiles", "bf16_tp_big"])
+def test_forward_large_batch_output_range(scale, name):
     """Large batches keep the packed expert outputs as fp16 with a power-of-two
-    scale per 64 columns.  Activations scaled by 2^12 (outputs near 1e5, past
-    fp16's 65504) and by 2^-20 (outputs near 1e-14, below fp16's normal range)
-    must still match the oracle within the bf16 bound."""
-    cfg = SMALL["bf16_pipe_tiles"]
+    scale per 64 columns (down projection on the pipelined 256-row kernel, or
+    on the plain one for K loops it cannot pipeline).  Activations scaled by
+    2^12 (outputs near 1e5, past fp16's 65504) and by 2^-20 (outputs near
+    1e-14, below fp16's normal range) must still match the oracle within the
+    bf16 bound."""
+    cfg = SMALL[name]
     log(f"[parity] output range, x scaled by {scale:g}")
     inp = dict(workloads.generate(cfg, seed=2))
     inp["x"] = _scale_bf16_bits(inp["x"], scale)
