@@ -190,6 +190,10 @@ def test_forward_validation(lib):
     big = lib.moe_forward_workspace_size(8192, 2048, 128, 8, 768, 0, BF16)
     # y [P,H] f32 dominates: 65536 * 2048 * 4 bytes
     assert big > 65536 * 2048 * 4
+    # the largest batch of the Qwen3-30B-A3B layer: y [P, H] f32 must stay
+    # under 2 GiB (32-bit buffer offsets), so T = 32767 is the last valid one
+    assert lib.moe_forward_workspace_size(32767, 2048, 128, 8, 768, 0, BF16) > 32767 * 8 * 2048 * 4
+    assert forward(lib, T=32768, H=2048, E=128, k=8, I=768, wsb=1 << 40) == UNSUP and "2 GiB" in last(lib)
 
 
 def test_profile_collect_empty(lib):

@@ -245,6 +245,36 @@ def test_full_size_forward_sampled(name):
     torch.cuda.empty_cache()
 
 
+def test_forward_largest_batch_sampled():
+    """The largest batch the bf16 layer takes at the Qwen3-30B-A3B shape:
+    T = 32767 tokens, so that y [T*8, 2048] in fp32 is just under 2 GiB, the
+    limit of the kernels' 32-bit buffer offsets (T = 32768 is rejected on the
+    host).  Routing and the plan bit-exact for every token, the output on
+    sampled tokens (first, last and random) against the oracle."""
+    cfg = workloads.config("qwen3_30b_a3b_prefill").scaled(name="qwen3_largest_batch", num_tokens=32767)
+    assert cfg.num_tokens * cfg.top_k * cfg.hidden_size * 4 < 2 ** 31
+    inp = workloads.generate(cfg, seed=4)
+    log("[parity-full] largest batch: generated")
+    dev = device_inputs(inp)
+    f = gpu_forward(cfg, dev)
+    torch.cuda.synchronize()
+    log("[parity-full] largest batch: GPU forward done")
+    ids = f["topk_ids"].cpu().numpy()
+    w = f["topk_weights"].cpu().numpy().astype(np.float64)
+    assert (ids == oracle.select_topk(f["logits"].cpu().numpy().astype(np.float64), cfg.top_k)).all()
+    g = rdg.moe_dispatch_plan(f["topk_ids"], f["topk_weights"], cfg.num_experts)
+    check_plan_equal(g, oracle.dispatch_plan(ids, f["topk_weights"].cpu().numpy(), cfg.num_experts))
+    T = cfg.num_tokens
+    tokens = np.unique(np.concatenate([np.arange(8), np.arange(T - 8, T),
+                                       np.random.default_rng(9).choice(T, size=48, replace=False)]))
+    ref = oracle.token_outputs(inp, tokens, ids, w)
+    err, rms = rel_max_err(f["out"].cpu().numpy().astype(np.float64)[tokens], ref)
+    log(f"[parity-full] largest batch: sampled {len(tokens)} tokens max|err|/rms = {err / rms:.3e}")
+    assert err <= tol_for(cfg) * rms
+    del dev, f, g
+    torch.cuda.empty_cache()
+
+
 def test_dispatch_edge_cases():
     cases = []
     rng = np.random.default_rng(5)
