@@ -73,7 +73,7 @@ moe_status check_buffer_bytes(int64_t T, int64_t H, int64_t k, int64_t I, int dt
 
 moe_status check_inter(int64_t I, int dtype, const char* name) {
   if (I < 1) return fail(MOE_ERR_INVALID_ARG, std::string(name) + " must be >= 1");
-  if (dtype == MOE_DTYPE_BF16 && I % 32 != 0) return fail(MOE_ERR_UNSUPPORTED, std::string("bf16 needs ") + name + " % 32 == 0");
+  if (dtype == MOE_DTYPE_BF16 && I % 16 != 0) return fail(MOE_ERR_UNSUPPORTED, std::string("bf16 needs ") + name + " % 16 == 0");
   if (dtype == MOE_DTYPE_F32 && I % 16 != 0) return fail(MOE_ERR_UNSUPPORTED, std::string("f32 needs ") + name + " % 16 == 0");
   return MOE_OK;
 }

@@ -870,14 +870,29 @@ __device__ __forceinline__ void big_issue(u32x4_t* buf, const BigPlan& d, u32x4_
   for (int qi = 0; qi < 4; ++qi) dma16(buf + Big::A_SLOTS + (qi * 4 + wave) * 64, rb, d.b_off[qi], kbytes);
 }
 
-// Buffer resource for the stage at byte offset kbytes of a row: a stage at or
-// past the end of K (a K loop padded to whole groups of four stages) reads
-// through a zero-length buffer, which lands zeros in LDS and moves no data.
-// PAD false (K a whole number of groups): the resource unchanged, no test.
+// Byte position of this lane's 16-byte chunk inside a 64-byte stage row.  A
+// lane fetches chunk (lane & 3) ^ big_swz(r) of row r = 16 q + (lane >> 2),
+// and big_swz(r) = (lane >> 4) & 3 for every q, so the chunk depends on the
+// lane only.
+__device__ __forceinline__ uint32_t big_chunk_bytes(int lane) {
+  return (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
+}
+
+// The plan of the stage at byte offset kbytes of a row.  PAD (a K loop padded
+// to whole groups of four stages, K possibly ending inside a stage): chunks at
+// or past the end of the row fetch through an offset past the buffer, which
+// lands zeros in LDS and moves no data.  PAD false: the plan unchanged.
 template <bool PAD>
-__device__ __forceinline__ u32x4_t stage_rsrc(u32x4_t r, int kbytes, uint32_t row_bytes) {
-  if (PAD && (uint32_t)kbytes >= row_bytes) r[2] = 0u;
-  return r;
+__device__ __forceinline__ BigPlan stage_plan(const BigPlan& d, uint32_t cb, int kbytes, uint32_t row_bytes) {
+  if constexpr (!PAD) return d;
+  BigPlan m;
+  const bool dead = cb + (uint32_t)kbytes >= row_bytes;
+#pragma unroll
+  for (int qi = 0; qi < 4; ++qi) {
+    m.a_off[qi] = dead ? 0x80000000u : d.a_off[qi];
+    m.b_off[qi] = dead ? 0x80000000u : d.b_off[qi];
+  }
+  return m;
 }
 
 // Fragments of one stage for one wave: [k16 half][sub-tile].
@@ -1331,13 +1346,12 @@ __device__ __forceinline__ void pipe_kloop(f32x16_t (&acc)[4][4], u32x4_t* s0, u
       }
       const BigPlan& dd = last ? dn : d;
       const u32x4_t rbs = last ? rbn : rb;
-      const u32x4_t ras = stage_rsrc<PAD>(ra, kbytes, row_bytes);
-      const u32x4_t rbk = stage_rsrc<PAD>(rbs, kbytes, row_bytes);
+      const BigPlan dk = stage_plan<PAD>(dd, big_chunk_bytes(lane), kbytes, row_bytes);
       if constexpr (LIVE >= 1) {
-        big_step<EPI, LIVE>(acc, cur, nxt, bufs[u], bufs[(u + 1) & 3], dma, kbytes, dd, ras, rbk, wave, a_slot,
+        big_step<EPI, LIVE>(acc, cur, nxt, bufs[u], bufs[(u + 1) & 3], dma, kbytes, dk, ra, rbs, wave, a_slot,
                             b_slot);
       } else {
-        if (dma) big_issue(bufs[u], dd, ras, rbk, wave, kbytes);
+        if (dma) big_issue(bufs[u], dk, ra, rbs, wave, kbytes);
       }
     }
   }
@@ -1373,7 +1387,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
   const int per = (total + kXcds - 1) / kXcds;
   const int t_begin = xcd * per;
   const int t_end = min(total, t_begin + per);
-  const int KT = (p.K / Big::KB + 3) & ~3;  // whole groups of 4 stages; stages past K read zeros
+  const int KT = ((p.K + Big::KB - 1) / Big::KB + 3) & ~3;  // whole groups of 4 stages; chunks past K read zeros
   const uint32_t row_bytes = (uint32_t)p.K * 2u;
   int t = t_begin + slot;
   if (t >= t_end) return;  // whole workgroup, after the last barrier it takes part in
@@ -1420,13 +1434,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
     }
   }
   u32x4_t rb = make_rsrc(p.B + (int64_t)tc.g * p.b_group_stride, b_bytes);
-  big_issue(st0, d, ra, rb, wave, 0);
-  big_issue(st1, d, stage_rsrc<PAD>(ra, 1 * Big::KB * 2, row_bytes), stage_rsrc<PAD>(rb, 1 * Big::KB * 2, row_bytes),
-            wave, 1 * Big::KB * 2);
-  big_issue(st2, d, stage_rsrc<PAD>(ra, 2 * Big::KB * 2, row_bytes), stage_rsrc<PAD>(rb, 2 * Big::KB * 2, row_bytes),
-            wave, 2 * Big::KB * 2);
-  big_issue(st3, d, stage_rsrc<PAD>(ra, 3 * Big::KB * 2, row_bytes), stage_rsrc<PAD>(rb, 3 * Big::KB * 2, row_bytes),
-            wave, 3 * Big::KB * 2);
+  {
+    const uint32_t cb = big_chunk_bytes(lane);
+    big_issue(st0, stage_plan<PAD>(d, cb, 0, row_bytes), ra, rb, wave, 0);
+    big_issue(st1, stage_plan<PAD>(d, cb, 1 * Big::KB * 2, row_bytes), ra, rb, wave, 1 * Big::KB * 2);
+    big_issue(st2, stage_plan<PAD>(d, cb, 2 * Big::KB * 2, row_bytes), ra, rb, wave, 2 * Big::KB * 2);
+    big_issue(st3, stage_plan<PAD>(d, cb, 3 * Big::KB * 2, row_bytes), ra, rb, wave, 3 * Big::KB * 2);
+  }
 
   bool after_epi = false;
   while (true) {
@@ -1780,6 +1794,7 @@ int resident_big_per_cu() {
 template <int EPI>
 hipError_t launch_big(const GemmArgs& a, hipStream_t s, const char* name) {
   constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
+  if (a.K % Big::KB != 0) return hipErrorInvalidValue;  // whole 32-wide stages only
   const int64_t nblk = (a.N + BN_OUT - 1) / BN_OUT;
   int64_t ub_m = (a.M + Big::BM - 1) / Big::BM;
   if (a.offsets) ub_m += (a.G < a.M ? a.G : a.M);
@@ -1806,7 +1821,7 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t s, const char* name) {
   grid = ((grid + kXcds - 1) / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
   profile_begin(name, s);
-  if ((a.K / Big::KB) % 4 != 0)
+  if (a.K % (4 * Big::KB) != 0)
     hipLaunchKernelGGL((grouped_gemm_bf16_pipe_kernel<EPI, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL((grouped_gemm_bf16_pipe_kernel<EPI, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
@@ -1814,13 +1829,17 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t s, const char* name) {
   return hipGetLastError();
 }
 
-// The pipelined 256-row kernel runs K loops in whole groups of four stages,
-// padding with stages that read zeros; it takes a K loop when the padding
-// adds at most a third to it, and with gathered rows only from 8 stages on
-// (the next tile's row indices are staged 8 steps before its first DMA).
+// The pipelined 256-row kernel runs K loops in whole groups of four 32-wide
+// stages, padding with chunks that read zeros; it takes a K loop when the
+// padding adds at most a third to it, and with gathered rows only from 8
+// stages on (the next tile's row indices are staged 8 steps before its first
+// DMA).  K not a multiple of 32 (possible for the down projection only, whose
+// rows are not gathered) always runs here: the plain 256-row kernel needs
+// whole stages.
 bool pipe_fits(const GemmArgs& a) {
-  const int64_t KT = a.K / Big::KB;
+  const int64_t KT = (a.K + Big::KB - 1) / Big::KB;
   const int64_t KTp = (KT + 3) & ~(int64_t)3;
+  if (a.K % Big::KB != 0) return a.gather == nullptr;
   if (3 * KTp > 4 * KT) return false;
   return a.gather ? KTp >= 8 : KTp >= 4;
 }

@@ -113,7 +113,8 @@ def ffn(lib, T=4, H=64, E=8, k=2, I=64, dtype=BF16, ydt=F32, gather=P16, off=P16
 
 def test_grouped_ffn_validation(lib):
     # bf16 expert widths: multiples of 32 (8-way TP slices of 768 are 96)
-    assert ffn(lib, I=80) == UNSUP and "% 32" in last(lib)
+    assert ffn(lib, I=72) == UNSUP and "% 16" in last(lib)
+    assert ffn(lib, I=80, wsb=1) == WS
     assert ffn(lib, I=96, wsb=1) == WS
     assert ffn(lib, ydt=3) == INVALID and "expert_out_dtype" in last(lib)
     assert ffn(lib, dtype=F32, ydt=BF16) == UNSUP and "bf16 layer" in last(lib)

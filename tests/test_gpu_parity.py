@@ -84,6 +84,17 @@ SMALL = {
         name="bf16_tp_big", num_tokens=1200, hidden_size=320, num_experts=4, top_k=2, intermediate_size=160),
     "bf16_tp_pipe": workloads.config("qwen3_30b_a3b_prefill").scaled(
         name="bf16_tp_pipe", num_tokens=4096, hidden_size=512, num_experts=16, top_k=8, intermediate_size=96),
+    # widths that are multiples of 16 only: the down GEMM's K ends inside a
+    # 32-wide stage (pipelined kernel, padded), inside a 64-wide stage
+    # (64-row tiles), inside a 256-wide stage (streaming kernel: Qwen1.5-MoE's
+    # 8-way slices, I = 1408 / 8 = 176 and Is = 5632 / 8 = 704)
+    "bf16_i80_pipe": workloads.config("qwen3_30b_a3b_prefill").scaled(
+        name="bf16_i80_pipe", num_tokens=1200, hidden_size=320, num_experts=4, top_k=2, intermediate_size=80),
+    "bf16_i112_mid_rows": workloads.config("qwen3_30b_a3b_prefill").scaled(
+        name="bf16_i112_mid_rows", num_tokens=333, hidden_size=128, num_experts=16, top_k=3, intermediate_size=112),
+    "bf16_i176_decode": workloads.config("qwen15_moe_decode").scaled(
+        name="bf16_i176_decode", num_tokens=16, hidden_size=256, num_experts=60, top_k=4, intermediate_size=176,
+        shared_intermediate_size=704),
 }
 
 
@@ -701,3 +712,28 @@ def test_tp8_rank_of_qwen3_prefill_sampled():
     assert err <= tol_for(cfg) * rms
     del dev
     torch.cuda.empty_cache()
+
+
+def test_tp8_rank_of_qwen15_decode():
+    """One rank (5 of 8) of the full-size Qwen1.5-MoE decode layer: routed
+    experts I = 1408 / 8 = 176 and shared expert Is = 5632 / 8 = 704, sliced
+    on the GPU; every token against the oracle's rank layer fed the GPU
+    routing."""
+    cfg, inp = full_inputs("qwen15_moe_decode")
+    dev = device_inputs(inp)
+    G, r = 8, 5
+    w13, w2 = rdg.moe_tp_slice_experts(dev["w13"], dev["w2"], G, r)
+    s13, s2 = rdg.moe_tp_slice_experts(dev["shared_w13"], dev["shared_w2"], G, r)
+    assert w13.shape[1] == 2 * 176 and s13.shape[0] == 2 * 704
+    ref_in = oracle.tp_slice(inp, G, r)
+    for got, key in ((w13, "w13"), (w2, "w2"), (s13, "shared_w13"), (s2, "shared_w2")):
+        assert (got.view(torch.int16).cpu().numpy().view(np.uint16) == ref_in[key]).all(), key
+    f = rdg.moe_forward(dev["x"], dev["router_weight"], w13, w2, cfg.top_k, router_bias=dev.get("router_bias"),
+                        shared_w13=s13, shared_w2=s2, shared_gate=dev["shared_gate"], renormalize=cfg.renormalize,
+                        return_routing=True)
+    ids = f["topk_ids"].cpu().numpy()
+    w = f["topk_weights"].cpu().numpy().astype(np.float64)
+    ref = oracle.forward(ref_in, cfg.top_k, cfg.renormalize, ids=ids, weights=w)["out"]
+    err, rms = rel_max_err(f["out"].cpu().numpy().astype(np.float64), ref)
+    log(f"[parity-full] qwen15 decode tp8 rank 5: max|err|/rms = {err / rms:.3e}")
+    assert err <= tol_for(cfg) * rms
