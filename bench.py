@@ -213,10 +213,33 @@ def decode_measure(rdg, torch, seed, steps=400, warmup=50):
     H, I, Is, E = cfg.hidden_size, cfg.intermediate_size, cfg.shared_intermediate_size, cfg.num_experts
     nbytes = touched * 3 * I * H * 2 + 3 * Is * H * 2 + (E + 1) * H * 2
     gbs = nbytes / dt / 1e9
-    return {"workload": cfg.name, "steps": steps, "warmup": warmup, "ms_per_step": round(dt * 1e3, 4),
-            "value": round(cfg.num_tokens / dt, 1), "unit": "tokens/s", "experts_touched": touched,
-            "weight_bytes_per_step": nbytes, "achieved": round(gbs, 1), "achieved_unit": "GB/s",
-            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    res = {"workload": cfg.name, "steps": steps, "warmup": warmup, "ms_per_step": round(dt * 1e3, 4),
+           "value": round(cfg.num_tokens / dt, 1), "unit": "tokens/s", "experts_touched": touched,
+           "weight_bytes_per_step": nbytes, "achieved": round(gbs, 1), "achieved_unit": "GB/s",
+           "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    # one rank of an 8-way tensor-parallel split (I / 8 and Is / 8, router and
+    # gate replicated): the same tokens stream an eighth of the expert weights
+    G = 8
+    if I % (16 * G) == 0 and Is % (16 * G) == 0:
+        w13, w2 = rdg.moe_tp_slice_experts(d["w13"], d["w2"], G, 0)
+        s13, s2 = rdg.moe_tp_slice_experts(d["shared_w13"], d["shared_w2"], G, 0)
+        rank = rdg.MoeLayer(d["router_weight"], w13, w2, cfg.top_k, router_bias=d.get("router_bias"),
+                            shared_w13=s13, shared_w2=s2, shared_gate=d.get("shared_gate"),
+                            renormalize=cfg.renormalize)
+        rank.reserve(cfg.num_tokens, x.device)
+        for _ in range(warmup):
+            rank(x)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            rank(x)
+        torch.cuda.synchronize()
+        dtr = (time.perf_counter() - t0) / steps
+        nb = (touched * 3 * I * H * 2 + 3 * Is * H * 2) // G + (E + 1) * H * 2
+        res["tp8_rank"] = {"intermediate_size": I // G, "shared_intermediate_size": Is // G,
+                           "ms_per_step": round(dtr * 1e3, 4), "weight_bytes_per_step": nb,
+                           "achieved": round(nb / dtr / 1e9, 1), "achieved_unit": "GB/s"}
+    return res
 
 
 def tp_measure(rdg, torch, cfg, d, steps, warmup=10, sizes=(2, 4, 8)):

@@ -878,13 +878,12 @@ __device__ __forceinline__ uint32_t big_chunk_bytes(int lane) {
   return (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
 }
 
-// The plan of the stage at byte offset kbytes of a row.  PAD (a K loop padded
-// to whole groups of four stages, K possibly ending inside a stage): chunks at
+// The plan of the stage at byte offset kbytes of a row in a K loop padded to
+// whole groups of four stages (K possibly ending inside a stage): chunks at
 // or past the end of the row fetch through an offset past the buffer, which
-// lands zeros in LDS and moves no data.  PAD false: the plan unchanged.
-template <bool PAD>
+// lands zeros in LDS and moves no data.  Unpadded loops use the plan as is
+// (no copy: a copied plan changes the register allocation of the hot loop).
 __device__ __forceinline__ BigPlan stage_plan(const BigPlan& d, uint32_t cb, int kbytes, uint32_t row_bytes) {
-  if constexpr (!PAD) return d;
   BigPlan m;
   const bool dead = cb + (uint32_t)kbytes >= row_bytes;
 #pragma unroll
@@ -1346,12 +1345,21 @@ __device__ __forceinline__ void pipe_kloop(f32x16_t (&acc)[4][4], u32x4_t* s0, u
       }
       const BigPlan& dd = last ? dn : d;
       const u32x4_t rbs = last ? rbn : rb;
-      const BigPlan dk = stage_plan<PAD>(dd, big_chunk_bytes(lane), kbytes, row_bytes);
-      if constexpr (LIVE >= 1) {
-        big_step<EPI, LIVE>(acc, cur, nxt, bufs[u], bufs[(u + 1) & 3], dma, kbytes, dk, ra, rbs, wave, a_slot,
-                            b_slot);
+      if constexpr (PAD) {
+        const BigPlan dk = stage_plan(dd, big_chunk_bytes(lane), kbytes, row_bytes);
+        if constexpr (LIVE >= 1) {
+          big_step<EPI, LIVE>(acc, cur, nxt, bufs[u], bufs[(u + 1) & 3], dma, kbytes, dk, ra, rbs, wave, a_slot,
+                              b_slot);
+        } else {
+          if (dma) big_issue(bufs[u], dk, ra, rbs, wave, kbytes);
+        }
       } else {
-        if (dma) big_issue(bufs[u], dk, ra, rbs, wave, kbytes);
+        if constexpr (LIVE >= 1) {
+          big_step<EPI, LIVE>(acc, cur, nxt, bufs[u], bufs[(u + 1) & 3], dma, kbytes, dd, ra, rbs, wave, a_slot,
+                              b_slot);
+        } else {
+          if (dma) big_issue(bufs[u], dd, ra, rbs, wave, kbytes);
+        }
       }
     }
   }
@@ -1387,7 +1395,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
   const int per = (total + kXcds - 1) / kXcds;
   const int t_begin = xcd * per;
   const int t_end = min(total, t_begin + per);
-  const int KT = ((p.K + Big::KB - 1) / Big::KB + 3) & ~3;  // whole groups of 4 stages; chunks past K read zeros
+  // whole groups of 4 stages (PAD: chunks past K read zeros; otherwise K is a
+  // multiple of 4 stages already)
+  const int KT = PAD ? ((p.K + Big::KB - 1) / Big::KB + 3) & ~3 : p.K / Big::KB;
   const uint32_t row_bytes = (uint32_t)p.K * 2u;
   int t = t_begin + slot;
   if (t >= t_end) return;  // whole workgroup, after the last barrier it takes part in
@@ -1434,12 +1444,17 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
     }
   }
   u32x4_t rb = make_rsrc(p.B + (int64_t)tc.g * p.b_group_stride, b_bytes);
-  {
+  if constexpr (PAD) {
     const uint32_t cb = big_chunk_bytes(lane);
-    big_issue(st0, stage_plan<PAD>(d, cb, 0, row_bytes), ra, rb, wave, 0);
-    big_issue(st1, stage_plan<PAD>(d, cb, 1 * Big::KB * 2, row_bytes), ra, rb, wave, 1 * Big::KB * 2);
-    big_issue(st2, stage_plan<PAD>(d, cb, 2 * Big::KB * 2, row_bytes), ra, rb, wave, 2 * Big::KB * 2);
-    big_issue(st3, stage_plan<PAD>(d, cb, 3 * Big::KB * 2, row_bytes), ra, rb, wave, 3 * Big::KB * 2);
+    big_issue(st0, stage_plan(d, cb, 0, row_bytes), ra, rb, wave, 0);
+    big_issue(st1, stage_plan(d, cb, 1 * Big::KB * 2, row_bytes), ra, rb, wave, 1 * Big::KB * 2);
+    big_issue(st2, stage_plan(d, cb, 2 * Big::KB * 2, row_bytes), ra, rb, wave, 2 * Big::KB * 2);
+    big_issue(st3, stage_plan(d, cb, 3 * Big::KB * 2, row_bytes), ra, rb, wave, 3 * Big::KB * 2);
+  } else {
+    big_issue(st0, d, ra, rb, wave, 0);
+    big_issue(st1, d, ra, rb, wave, 1 * Big::KB * 2);
+    big_issue(st2, d, ra, rb, wave, 2 * Big::KB * 2);
+    big_issue(st3, d, ra, rb, wave, 3 * Big::KB * 2);
   }
 
   bool after_epi = false;
