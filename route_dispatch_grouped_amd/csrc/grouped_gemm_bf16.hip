@@ -8,7 +8,7 @@
 //   EPI_F32     down projection y = W2[e] h, fp32 out.  [DWDP README "Executor Module"]
 //   EPI_BF16    the same, y rounded once to bf16 (RNE).
 //   EPI_F16S    the same, y as fp16 with a power-of-two scale per (row, 64
-//               columns) (pipelined 256-row kernel only).
+//               columns) (256-row kernels only).
 //   EPI_ROUTER  router logits x Wr^T (+ bias).          [DWDP README "Router Module"]
 //
 // Scheduling: the packed rows of each group (expert) form expert-major execution
@@ -22,7 +22,8 @@
 // of an m-tile and all m-tiles of an expert close together in time.
 //
 // Tile: BM rows x 256 weight rows (EPI_SWIGLU: 128 gate + the matching 128 up
-// rows; otherwise 256 output columns), BK = 64 (128 bytes per row).  Both
+// rows; otherwise 256 output columns), BK = 64 (128 bytes per row); K needs
+// only to be a multiple of 8 (16-byte chunks): chunks past K read zeros.  Both
 // operands stream through an NS-stage LDS ring filled by direct global->LDS
 // DMA (buffer_load_dwordx4 ... lds): no staging registers, NS-1 K-steps in
 // flight.  Each stage is its own __shared__ object, so the compiler tracks the
@@ -831,7 +832,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_stream_kernel(Gemm
 // does so at one wave per SIMD.  Per stage a wave issues 16 fragment reads for
 // 32 MFMAs, and the CU streams 64 KB per 2 x 256 x 256 x 64 flops, about 31
 // bytes per clock at the MFMA rate, below the ~52 B/clk/CU that the
-// L2 -> LDS DMA path sustains.
+// L2 -> LDS DMA path sustains.  The plain kernel takes K in whole stages (a
+// multiple of 32); the pipelined one below also pads K to whole groups of
+// four stages.
 //
 // LDS layout: a row holds four 16-byte chunks (64 bytes); chunk c of row r sits
 // at position c ^ ((r >> 2) & 3).  For the 32-row fragment reads (lane l: row
