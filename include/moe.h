@@ -207,6 +207,28 @@ moe_status moe_ep_routing_table(const int32_t* gate_indices, int64_t gate_indice
                                 int32_t* counts, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Expert-parallel send counts: how many rows of the expert-major packed order
+ * (the dispatch plan) go to each of num_ranks ranks that own contiguous
+ * expert ranges, and where each rank's segment starts.
+ * [metrale_model_layers ep_dispatch.rs: one rank's local_expert_start and
+ *  local_expert_end; DWDP README "Dispatcher Module": expert-major layout
+ *  with per-expert offsets]
+ *
+ * Rank r owns experts [floor(r*E/G), floor((r+1)*E/G)) (G = num_ranks; the
+ * pages fix one rank's range, not how ranges are chosen: contiguous, every
+ * expert once, sizes within one of each other).  Then
+ *   send_counts[r]  = expert_offsets[(r+1)*E/G] - expert_offsets[r*E/G]   [G] int32
+ *   send_offsets[r] = expert_offsets[r*E/G],  send_offsets[G] = expert_offsets[E]   [G+1] int32
+ * which are the all-to-all-v send counts and displacements of the packed rows.
+ * expert_offsets [E+1] int32 (device, as moe_dispatch_plan writes it);
+ * send_counts [G] int32 device; send_offsets [G+1] int32 device or NULL.
+ * Errors: INVALID_ARG for NULL pointers, num_experts outside [1, 512],
+ * num_ranks outside [1, num_experts].
+ */
+moe_status moe_ep_rank_counts(const int32_t* expert_offsets, int64_t num_experts, int64_t num_ranks,
+                              int32_t* send_counts, int32_t* send_offsets, void* stream);
+
+/*
  * Grouped expert SwiGLU FFN over the expert-major layout.
  * [DWDP README "Executor Module": gather token activations per expert range,
  *  run the expert, write packed expert outputs; modelexpress refit test,

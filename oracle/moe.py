@@ -65,6 +65,8 @@ __all__ = [
     "forward",
     "token_outputs",
     "ep_routing_table",
+    "ep_rank_ranges",
+    "ep_rank_counts",
     "tp_load_expert",
     "tp_slice",
 ]
@@ -405,6 +407,28 @@ def ep_routing_table(gate_indices, gate_weights, num_tokens: int, top_k: int,
         "remote_weights": gw[~local].astype(np.float32),
     }
 
+
+
+def ep_rank_ranges(num_experts: int, num_ranks: int):
+    """Contiguous expert ranges of ``num_ranks`` expert-parallel ranks:
+    rank r owns ``[floor(r*E/G), floor((r+1)*E/G))`` (reading: the pages give
+    one rank's ``local_expert_start``/``local_expert_end`` [ep_dispatch] and
+    no rule for choosing them; this split is contiguous, covers every expert
+    once and differs by at most one expert between ranks)."""
+    return [((r * num_experts) // num_ranks, ((r + 1) * num_experts) // num_ranks) for r in range(num_ranks)]
+
+
+def ep_rank_counts(ids: np.ndarray, num_experts: int, num_ranks: int) -> Dict[str, np.ndarray]:
+    """Per-rank send counts of the expert-major packed order: how many
+    assignments go to each rank's experts (``ep_rank_ranges``), and where each
+    rank's segment starts in the packed order (exclusive scan, G+1 entries).
+    Counted directly from the assignments, one range at a time, as the local
+    bucket of ``ep_routing_table`` with that rank's range would count them."""
+    ids = np.asarray(ids).reshape(-1).astype(np.int64)
+    counts = np.array([int(((ids >= lo) & (ids < hi)).sum()) for lo, hi in ep_rank_ranges(num_experts, num_ranks)],
+                      dtype=np.int64)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    return {"send_counts": counts.astype(np.int32), "send_offsets": offsets.astype(np.int32)}
 
 # --------------------------------------------------------------------------
 # tensor-parallel expert slices  ([refit] module docstring and

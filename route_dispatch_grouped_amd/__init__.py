@@ -9,8 +9,8 @@ GPU; the first call raises if the library is missing.
 
 Entry points (same names as the C ABI):
   moe_router_topk, moe_router_topk_grouped, moe_dispatch_plan,
-  moe_ep_routing_table, moe_grouped_ffn, moe_combine, moe_forward,
-  moe_tp_load_expert
+  moe_ep_routing_table, moe_ep_rank_counts, moe_grouped_ffn, moe_combine,
+  moe_forward, moe_tp_load_expert
 plus ``moe_tp_slice_experts`` (one tensor-parallel rank's fused weights,
 loaded expert by expert through moe_tp_load_expert) and ``MoeLayer``, a bound layer with a reusable workspace (the "explicit
 layer" of the DWDP README's ``build_reference``).
@@ -37,6 +37,7 @@ __all__ = [
     "moe_router_topk_grouped",
     "moe_dispatch_plan",
     "moe_ep_routing_table",
+    "moe_ep_rank_counts",
     "moe_grouped_ffn",
     "moe_combine",
     "moe_forward",
@@ -87,6 +88,7 @@ _SIGNATURES = {
     "moe_forward": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                            _i64, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _c_void_p, _c_void_p,
                            _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "moe_ep_rank_counts": (_int, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
     "moe_tp_load_expert": (_int, [_c_void_p, _int, _i64, _i64, _int, _int, _i64, _i64, _int, _c_void_p,
                                   _c_void_p]),
     "moe_profile_enable": (None, [_int]),
@@ -305,6 +307,22 @@ def moe_ep_routing_table(gate_indices: torch.Tensor, gate_weights: torch.Tensor,
             elif name.startswith("remote_"):
                 out[name] = out[name][:nr]
     return out
+
+
+def moe_ep_rank_counts(expert_offsets: torch.Tensor, num_ranks: int, stream=None) -> Dict[str, torch.Tensor]:
+    """Rows of the expert-major packed order per expert-parallel rank with
+    contiguous expert ranges (include/moe.h: moe_ep_rank_counts): send_counts
+    [G] and send_offsets [G+1], int32 on the GPU."""
+    _need(expert_offsets, "expert_offsets", None, torch.int32)
+    if expert_offsets.dim() != 1 or expert_offsets.numel() < 2:
+        raise ValueError("expert_offsets must be [E+1]")
+    E = expert_offsets.numel() - 1
+    counts = torch.empty((max(int(num_ranks), 0),), dtype=torch.int32, device=expert_offsets.device)
+    starts = torch.empty((max(int(num_ranks), 0) + 1,), dtype=torch.int32, device=expert_offsets.device)
+    lib = load_library()
+    _check("moe_ep_rank_counts", lib.moe_ep_rank_counts(_ptr(expert_offsets), E, int(num_ranks), _ptr(counts),
+                                                        _ptr(starts), _stream(stream)))
+    return {"send_counts": counts, "send_offsets": starts}
 
 
 def moe_grouped_ffn(hidden_states: torch.Tensor, packed_token_indices: Optional[torch.Tensor],

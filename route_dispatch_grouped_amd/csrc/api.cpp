@@ -508,6 +508,18 @@ moe_status moe_tp_load_expert(const void* src, int proj, int64_t hidden_size, in
                     "moe_tp_load_expert");
 }
 
+moe_status moe_ep_rank_counts(const int32_t* expert_offsets, int64_t num_experts, int64_t num_ranks,
+                              int32_t* send_counts, int32_t* send_offsets, void* stream) {
+  REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(send_counts);
+  if (num_experts < 1 || num_experts > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_INVALID_ARG, "num_experts must be in [1, 512]");
+  if (num_ranks < 1 || num_ranks > num_experts) return fail(MOE_ERR_INVALID_ARG, "num_ranks must be in [1, num_experts]");
+  return hip_status(moe::launch_ep_rank_counts(expert_offsets, (int)num_experts, (int)num_ranks, send_counts,
+                                               send_offsets, static_cast<hipStream_t>(stream)),
+                    "moe_ep_rank_counts");
+}
+
 // Split-K scratch of moe_grouped_ffn; with one expert the offsets may be
 // absent (one ungrouped block) or present, and the two can split differently.
 size_t grouped_ffn_partial_bytes(int64_t P, int64_t H, int64_t E, int64_t I, int dtype) {

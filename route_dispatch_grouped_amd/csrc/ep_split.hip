@@ -11,6 +11,11 @@
 //             local entry a at base + rank and remote entry a at a - (locals
 //             before a).  Workgroup 0 writes counts = {local, remote}.
 // No atomics: the result does not depend on timing.
+//
+// Also the per-rank send counts of the expert-major packed order when G ranks
+// own contiguous expert ranges (each rank's local_expert_start/end as in
+// ep_dispatch.rs): differences of the dispatch plan's expert offsets at the
+// range boundaries.
 #include "moe_internal.h"
 
 namespace moe {
@@ -113,9 +118,38 @@ __global__ __launch_bounds__(kEpThreads) void ep_split_kernel(
   }
 }
 
+// Per-rank send counts of the expert-major packed order for G expert-parallel
+// ranks with contiguous expert ranges: rank r owns [r*E/G, (r+1)*E/G) (floor),
+// so its segment of the packed order starts at offsets[r*E/G] and holds
+// offsets[(r+1)*E/G] - offsets[r*E/G] rows.  Thread r < G writes counts[r] and
+// starts[r]; thread G writes starts[G] = offsets[E].
+__global__ __launch_bounds__(256) void ep_rank_counts_kernel(const int32_t* __restrict__ offsets, int E, int G,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ starts) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r > G) return;
+  if (r == G) {
+    if (starts != nullptr) starts[G] = offsets[E];
+    return;
+  }
+  const int lo = (int)(((int64_t)r * E) / G);
+  const int hi = (int)(((int64_t)(r + 1) * E) / G);
+  counts[r] = offsets[hi] - offsets[lo];
+  if (starts != nullptr) starts[r] = offsets[lo];
+}
+
 }  // namespace
 
 size_t ep_split_scratch_bytes(int64_t P) { return (size_t)((P + kEpSeg - 1) / kEpSeg) * sizeof(int32_t); }
+
+hipError_t launch_ep_rank_counts(const int32_t* offsets, int E, int G, int32_t* counts, int32_t* starts,
+                                 hipStream_t s) {
+  profile_begin("ep_rank_counts", s);
+  hipLaunchKernelGGL(ep_rank_counts_kernel, dim3((G + 1 + 255) / 256), dim3(256), 0, s, offsets, E, G, counts,
+                     starts);
+  profile_end(s);
+  return hipGetLastError();
+}
 
 hipError_t launch_ep_split(const int32_t* ids, const float* w, int T, int k, int64_t start, int64_t end,
                            int32_t* l_tok, int32_t* l_eid, float* l_w, int32_t* r_tok, int32_t* r_eid, float* r_w,

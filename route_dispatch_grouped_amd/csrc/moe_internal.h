@@ -103,6 +103,11 @@ size_t ep_split_scratch_bytes(int64_t P);
 hipError_t launch_ep_split(const int32_t* ids, const float* w, int T, int k, int64_t start, int64_t end,
                            int32_t* l_tok, int32_t* l_eid, float* l_w, int32_t* r_tok, int32_t* r_eid, float* r_w,
                            int32_t* counts, void* scratch, hipStream_t s);
+// counts[r] / starts[r]: rows of rank r's experts [r*E/G, (r+1)*E/G) in the
+// expert-major order and where they start; starts[G] = offsets[E] (starts may
+// be NULL).
+hipError_t launch_ep_rank_counts(const int32_t* offsets, int E, int G, int32_t* counts, int32_t* starts,
+                                 hipStream_t s);
 
 // ---------------------------------------------------------------- dispatch
 constexpr int kDispatchSegment = 128;  // assignments per wave-segment

@@ -233,3 +233,13 @@ def test_tp_load_expert_validation(lib):
     assert load(e=4) == INVALID and "expert" in last(lib)
     assert load(e=-1) == INVALID
     assert load(H=0) == INVALID and load(I=0) == INVALID and load(E=0) == INVALID
+
+
+def test_ep_rank_counts_validation(lib):
+    def rc(off=P16, E=8, G=2, cnt=P16, st=P16):
+        return lib.moe_ep_rank_counts(off, E, G, cnt, st, NULL)
+    assert rc(off=NULL) == INVALID and "expert_offsets" in last(lib)
+    assert rc(cnt=NULL) == INVALID and "send_counts" in last(lib)
+    assert rc(G=0) == INVALID and "num_ranks" in last(lib)
+    assert rc(G=9) == INVALID and "num_ranks" in last(lib)
+    assert rc(E=0) == INVALID and rc(E=513, G=2) == INVALID

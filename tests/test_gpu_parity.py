@@ -560,6 +560,34 @@ def test_ep_routing_table():
         rdg.moe_ep_routing_table(to_device(np.zeros(6, np.int32)), to_device(np.zeros(5, np.float32)), 3, 2, 0, 1)
 
 
+def test_ep_rank_counts():
+    """Per-rank send counts and displacements from the GPU plan's offsets,
+    bit-exact against the oracle (counted from the assignments), for the
+    page's 2-rank split of 512 experts and for uneven splits."""
+    import json
+    import os
+    vec = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "ep_dispatch_vectors.json")))
+    for case in vec["cases"]:
+        ids = np.asarray(case["indices"], dtype=np.int32)
+        plan = rdg.moe_dispatch_plan(to_device(ids.reshape(case["num_tokens"], case["top_k"])), None, 512)
+        g = rdg.moe_ep_rank_counts(plan["offsets"], 2)
+        ref = oracle.ep_rank_counts(ids, 512, 2)
+        assert (g["send_counts"].cpu().numpy() == ref["send_counts"]).all(), case["name"]
+        assert (g["send_offsets"].cpu().numpy() == ref["send_offsets"]).all(), case["name"]
+    rng = np.random.default_rng(12)
+    for T, k, E, G in [(8192, 8, 128, 8), (16, 4, 60, 8), (513, 2, 64, 3), (1, 1, 4, 4), (300, 5, 512, 512),
+                       (77, 3, 7, 1)]:
+        log(f"[parity] ep rank counts T={T} k={k} E={E} G={G}")
+        ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+        plan = rdg.moe_dispatch_plan(to_device(ids), None, E)
+        g = rdg.moe_ep_rank_counts(plan["offsets"], G)
+        ref = oracle.ep_rank_counts(ids, E, G)
+        assert (g["send_counts"].cpu().numpy() == ref["send_counts"]).all()
+        assert (g["send_offsets"].cpu().numpy() == ref["send_offsets"]).all()
+    with pytest.raises(rdg.MoeError, match="num_ranks"):
+        rdg.moe_ep_rank_counts(plan["offsets"], E + 1)
+
+
 @pytest.mark.parametrize("name", ["bf16_decode_shared", "bf16_pipe_tiles"])
 def test_forward_graph_capture(name):
     """The whole forward captured into a HIP graph (through torch's graph API)

@@ -172,3 +172,49 @@ def test_ep_routing_table_length_errors(case):
     with pytest.raises(ValueError, match=case["message"]):
         oracle.ep_routing_table(case["indices"], case["weights"], case["num_tokens"], case["top_k"],
                                 case["start"], case["end"])
+
+
+# --------------------------------------------------------------------------
+# expert-parallel send counts per rank
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("case", _load("ep_dispatch_vectors.json")["cases"], ids=lambda c: c["name"])
+def test_ep_rank_counts_match_printed_vectors(case):
+    """Two ranks over 512 experts ([0, 256) and [256, 512), the ranges the
+    page's tests use): the send counts are the printed local/remote counts of
+    rank 0 (rank 1 for the rank-1 perspective)."""
+    c = oracle.ep_rank_counts(case["indices"], 512, 2)
+    assert oracle.ep_rank_ranges(512, 2) == [(0, 256), (256, 512)]
+    ex = case["expect"]
+    mine = 0 if case["start"] == 0 else 1
+    assert c["send_counts"][mine] == ex["local_count"]
+    if "remote_count" in ex:
+        assert c["send_counts"][1 - mine] == ex["remote_count"]
+    assert c["send_offsets"].tolist() == [0, int(c["send_counts"][0]), len(case["indices"])]
+
+
+@pytest.mark.parametrize("E,G", [(128, 8), (60, 8), (7, 3), (5, 5), (9, 1), (512, 7)])
+def test_ep_rank_ranges_partition_the_experts(E, G):
+    r = oracle.ep_rank_ranges(E, G)
+    assert r[0][0] == 0 and r[-1][1] == E
+    assert all(r[i][1] == r[i + 1][0] for i in range(G - 1))
+    sizes = [hi - lo for lo, hi in r]
+    assert max(sizes) - min(sizes) <= 1 and min(sizes) >= 1
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_ep_rank_counts_agree_with_plan_and_table(seed):
+    """The counts are the plan's offsets at the rank boundaries and each
+    rank's local bucket of the routing table (two independently pinned
+    functions)."""
+    rng = np.random.default_rng(seed)
+    E, k, T = [(128, 8, 300), (60, 4, 16), (64, 2, 513), (16, 3, 1)][seed]
+    G = [8, 8, 3, 16][seed]
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)])
+    c = oracle.ep_rank_counts(ids, E, min(G, E))
+    plan = oracle.dispatch_plan(ids, np.ones_like(ids, dtype=np.float64), E)
+    for r, (lo, hi) in enumerate(oracle.ep_rank_ranges(E, min(G, E))):
+        assert c["send_offsets"][r] == plan["offsets"][lo]
+        assert c["send_counts"][r] == plan["offsets"][hi] - plan["offsets"][lo]
+        t = oracle.ep_routing_table(ids.reshape(-1), np.ones(T * k), T, k, lo, hi)
+        assert c["send_counts"][r] == len(t["local_token_indices"])
+    assert c["send_offsets"][-1] == T * k
