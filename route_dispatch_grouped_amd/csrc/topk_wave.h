@@ -54,6 +54,18 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return best;
 }
 
+// Wave-wide maximum of a 32-bit key, wave-uniform (same exchange pattern).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));
+  uint32_t best = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) best = max(best, (uint32_t)__builtin_amdgcn_readlane((int)v, 16 * r));
+  return best;
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_add_step(float v) {
   return v + __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF,
@@ -108,7 +120,47 @@ __device__ __forceinline__ void topk_row(const float* row, int E, int k, int ren
     }
   }
 
-  if (n_group > 1) {
+  if (n_group > 1 && (E / n_group) <= 16 && ((E / n_group) & (E / n_group - 1)) == 0) {
+    // Groups of gs = 1, 2, 4, 8 or 16 experts occupy aligned gs-lane segments
+    // of one slot (expert e = lane + 64 i lies in group e / gs = lane / gs +
+    // i * 64 / gs), so the first DPP steps of a wave reduction, stopped at the
+    // segment size, leave each lane holding its group's largest key.
+    const int gs = E / n_group;
+    uint32_t gk[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      uint32_t v = ((avail >> i) & 1u) ? key[i] : 0u;
+      if (gs >= 2) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
+      if (gs >= 4) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
+      if (gs >= 8) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));
+      if (gs >= 16) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));
+      gk[i] = v;
+    }
+    // topk_group rounds: the largest group score, the lowest group holding it
+    // (groups past n_group hold no expert: score 0, below every real one)
+    uint64_t kept = 0;
+    for (int r = 0; r < topk_group; ++r) {
+      uint32_t mine = 0;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) mine = max(mine, gk[i]);
+      const uint32_t best = wave_max_u32(mine);
+      int g = 0;
+#pragma unroll
+      for (int i = VPL - 1; i >= 0; --i) {
+        const uint64_t hit = __ballot(gk[i] == best);
+        if (hit != 0) g = __builtin_ctzll(hit) / gs + i * (64 / gs);
+      }
+      kept |= 1ull << g;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (lane / gs + i * (64 / gs) == g) gk[i] = 0;
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && !((kept >> (e / gs)) & 1ull)) avail &= ~(1u << i);
+    }
+  } else if (n_group > 1) {
     const int gs = E / n_group;
     uint64_t gkey = 0;  // lane g < n_group: group g's score key
     for (int g = 0; g < n_group; ++g) {
@@ -139,6 +191,10 @@ __device__ __forceinline__ void topk_row(const float* row, int E, int k, int ren
     }
   }
 
+  // Each round: the largest available key over the wave (32-bit), then the
+  // lowest expert id holding it: slots are scanned in id order (slot i holds
+  // ids 64 i .. 64 i + 63), the first slot with a match gives its lowest lane.
+  // Key 0 lies below every float's key, so it marks a taken or absent slot.
   int my_id[VPL];
   float my_val[VPL];
 #pragma unroll
@@ -147,20 +203,21 @@ __device__ __forceinline__ void topk_row(const float* row, int E, int k, int ren
     my_val[c] = 0.f;
     const int jn = min(64, k - 64 * c);
     for (int jj = 0; jj < jn; ++jj) {
-      uint64_t best = 0;
+      uint32_t mine = 0;
 #pragma unroll
-      for (int i = 0; i < VPL; ++i) {
-        if ((avail >> i) & 1u) {
-          const uint64_t kk = ((uint64_t)key[i] << 32) | (uint32_t)(~(uint32_t)(lane + 64 * i));
-          best = kk > best ? kk : best;
-        }
+      for (int i = 0; i < VPL; ++i)
+        if ((avail >> i) & 1u) mine = max(mine, key[i]);
+      const uint32_t best = wave_max_u32(mine);
+      int id = 0;
+#pragma unroll
+      for (int i = VPL - 1; i >= 0; --i) {
+        const uint64_t hit = __ballot(((avail >> i) & 1u) && key[i] == best);
+        if (hit != 0) id = 64 * i + __builtin_ctzll(hit);
       }
-      best = wave_max_u64(best);
-      const int id = (int)(~(uint32_t)(best & 0xFFFFFFFFu));
       if ((id & 63) == lane) avail &= ~(1u << (id >> 6));
       if (jj == lane) {
         my_id[c] = id;
-        my_val[c] = order_value((uint32_t)(best >> 32));
+        my_val[c] = order_value(best);
       }
     }
   }

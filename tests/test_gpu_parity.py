@@ -396,6 +396,10 @@ def test_forward_bf16_output_and_determinism():
     (77, 512, 60, 4, 4, 2, True),      # groups of 15 experts
     (64, 256, 256, 8, 16, 4, True),    # four logits per lane
     (40, 128, 32, 4, 1, 1, True),      # one group: the plain router
+    (50, 128, 32, 5, 8, 4, True),      # groups of 4 (segmented lane reductions)
+    (64, 128, 96, 5, 48, 10, True),    # groups of 2, half of the second slot absent
+    (33, 64, 16, 3, 16, 8, False),     # groups of one expert
+    (70, 256, 160, 6, 10, 3, True),    # groups of 16 across a partly filled third slot
 ])
 def test_router_topk_grouped(T, H, E, k, ng, tg, renorm):
     """Group-limited selection on the GPU's own logits is bit-exact against
@@ -423,6 +427,27 @@ def test_router_topk_grouped(T, H, E, k, ng, tg, renorm):
     # selections that differ from the plain top-k exist in the larger cases
     if ng > 1 and T >= 100:
         assert (ids != plain["topk_ids"].cpu().numpy()).any()
+
+
+@pytest.mark.parametrize("E,ng,tg", [(64, 4, 1), (64, 4, 2), (128, 8, 3), (60, 4, 1)])
+def test_router_topk_grouped_tied_groups(E, ng, tg):
+    """Groups 1 and 2 have identical router rows, so their scores tie on
+    every token: the lower group must win (bit-exact against the oracle)."""
+    gs = E // ng
+    cfg = workloads.config("qwen3_30b_a3b_prefill").scaled(
+        name="grouped_ties", num_tokens=96, hidden_size=128, num_experts=E, top_k=4, intermediate_size=64)
+    inp = dict(workloads.generate(cfg, seed=5))
+    wr = inp["router_weight"].copy()
+    wr[2 * gs:3 * gs] = wr[gs:2 * gs]
+    inp["router_weight"] = wr
+    dev = device_inputs(inp)
+    r = rdg.moe_router_topk_grouped(dev["x"], dev["router_weight"], 4, ng, tg)
+    Lg = r["logits"].cpu().numpy().astype(np.float64)
+    assert (Lg[:, gs:2 * gs] == Lg[:, 2 * gs:3 * gs]).all()
+    ids = r["topk_ids"].cpu().numpy()
+    assert (ids == oracle.select_topk_grouped(Lg, 4, ng, tg)).all()
+    # wherever group 2's score would make the cut, group 1's equal score makes it first
+    assert not ((ids >= 2 * gs) & (ids < 3 * gs)).all(axis=1).any()
 
 
 def _scale_bf16_bits(bits: np.ndarray, s: float) -> np.ndarray:
