@@ -27,9 +27,8 @@ def header_functions():
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(rdg.LIB_PATH):
-        pytest.fail("libmoe_mi355x.so is not built (run __graft_entry__.build())")
-    return rdg.load_library()
+    from conftest import ensure_library
+    return ensure_library()
 
 
 def test_exports_every_declared_symbol(lib):

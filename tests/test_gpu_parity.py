@@ -33,7 +33,8 @@ rdg = pytest.importorskip("route_dispatch_grouped_amd")
 def _gpu():
     if not torch.cuda.is_available():
         pytest.fail("no GPU visible")
-    rdg.load_library()
+    from conftest import ensure_library
+    ensure_library()
     yield
     torch.cuda.synchronize()
 
