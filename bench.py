@@ -317,6 +317,10 @@ def main():
 
     import route_dispatch_grouped_amd as rdg
 
+    if not os.path.exists(rdg.LIB_PATH):  # a fresh checkout: build once, otherwise load what is built
+        from route_dispatch_grouped_amd.build import build
+        build()
+
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
