@@ -308,9 +308,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU: the single-GPU MoE layer forward has no "
-                                   "multi-GPU path (expert/tensor parallel designs are not part of it); "
-                                   "run with --gpus 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU: the MoE layer forward runs on a single GPU "
+                                   "and has no multi-GPU path (its expert- and tensor-parallel pieces are "
+                                   "single-GPU building blocks, with no collectives); run with --gpus 1"}))
         sys.exit(2)
 
     import torch
