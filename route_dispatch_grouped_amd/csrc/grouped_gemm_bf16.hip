@@ -1850,8 +1850,8 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t s, const char* name) {
 // The pipelined 256-row kernel runs K loops in whole groups of four 32-wide
 // stages, padding with chunks that read zeros; it takes a K loop when the
 // padding adds at most a third to it, and with gathered rows only from 8
-// stages on (the next tile's row indices are staged 8 steps before its first
-// DMA).  K not a multiple of 32 (possible for the down projection only, whose
+// stages on (the next tile's row indices are staged at step KT - 8, four
+// steps before its first DMA).  K not a multiple of 32 (possible for the down projection only, whose
 // rows are not gathered) always runs here: the plain 256-row kernel needs
 // whole stages.
 bool pipe_fits(const GemmArgs& a) {
