@@ -287,6 +287,26 @@ def test_forward_largest_batch_sampled():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("T,H,I,dtype", [(16, 256, 192, "bf16"), (80, 128, 96, "bf16"), (1000, 256, 160, "bf16"),
+                                          (4096, 512, 256, "bf16"), (37, 64, 48, "f32")])
+def test_grouped_ffn_dense_single_expert(T, H, I, dtype):
+    """moe_grouped_ffn with no packed token indices and no offsets (one
+    expert owning every row, row p reading token p): a dense SwiGLU MLP,
+    against the oracle's expert MLP on all rows.  Covers the streaming,
+    middle and 256-row GEMMs without a gather."""
+    base = "qwen3_30b_a3b_prefill" if dtype == "bf16" else "tiny_fp32"
+    cfg = workloads.config(base).scaled(name="dense_ffn", num_tokens=T, hidden_size=H, num_experts=1, top_k=1,
+                                        intermediate_size=I)
+    inp = workloads.generate(cfg, seed=7)
+    dev = device_inputs(inp)
+    y = rdg.moe_grouped_ffn(dev["x"], None, None, dev["w13"], dev["w2"], 1)
+    W13 = oracle.widen(inp["w13"])[0]
+    ref = oracle.swiglu_expert(oracle.widen(inp["x"]), W13[:I], W13[I:], oracle.widen(inp["w2"])[0])
+    err, rms = rel_max_err(y.cpu().numpy().astype(np.float64), ref)
+    log(f"[parity] dense ffn T={T} H={H} I={I} {dtype}: max|err|/rms = {err / rms:.3e}")
+    assert err <= tol_for(cfg) * rms
+
+
 def test_dispatch_edge_cases():
     cases = []
     rng = np.random.default_rng(5)
