@@ -634,6 +634,38 @@ def test_ep_rank_counts():
         rdg.moe_ep_rank_counts(plan["offsets"], E + 1)
 
 
+def test_forward_on_two_streams():
+    """Two layers (one with a shared expert, whose work goes through the
+    library's second stream) enqueued alternately on two caller streams,
+    each with its own workspace: every output equals that layer's forward
+    run alone, bit for bit."""
+    cfg_a, cfg_b = SMALL["bf16_decode_shared"], SMALL["bf16_multi_tile"]
+    layers, xs, refs = [], [], []
+    for cfg, seed in ((cfg_a, 21), (cfg_b, 22)):
+        inp = workloads.generate(cfg, seed=seed)
+        dev = device_inputs(inp)
+        layer = rdg.MoeLayer(dev["router_weight"], dev["w13"], dev["w2"], cfg.top_k,
+                             router_bias=dev.get("router_bias"), shared_w13=dev.get("shared_w13"),
+                             shared_w2=dev.get("shared_w2"), shared_gate=dev.get("shared_gate"),
+                             renormalize=cfg.renormalize)
+        layers.append(layer)
+        xs.append(dev["x"])
+        refs.append(layer(dev["x"]).clone())
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = [[], []]
+    for rep in range(6):
+        for i in (0, 1):
+            with torch.cuda.stream(streams[i]):
+                outs[i].append(layers[i](xs[i]).clone())
+    torch.cuda.synchronize()
+    for i in (0, 1):
+        for rep, o in enumerate(outs[i]):
+            assert torch.equal(o, refs[i]), f"layer {i} repeat {rep}"
+
+
 @pytest.mark.parametrize("name", ["bf16_decode_shared", "bf16_pipe_tiles"])
 def test_forward_graph_capture(name):
     """The whole forward captured into a HIP graph (through torch's graph API)
