@@ -78,6 +78,10 @@ def kernel_work(name, cfg, touched, touched_shared=True):
         return 2.0 * T * H * C, T * H * es + C * H * es + T * C * 4
     if name == "router_topk":
         return 0.0, T * E * 4 + 2 * P * 4
+    if name == "router_topk_hist":
+        # logits read, ids and weights written, the per-segment histogram written
+        U = (P + 127) // 128
+        return 0.0, T * E * 4 + 2 * P * 4 + U * E * 4
     if name == "topk_dispatch_small":
         return 0.0, T * E * 4 + 2 * P * 4 + 3 * P * 4 + (2 * E + 1) * 4
     if name == "dispatch_hist":

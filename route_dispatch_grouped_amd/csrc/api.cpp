@@ -694,10 +694,16 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
       if (e != hipSuccess) return hip_status(e, "moe_forward(fork)");
     }
   }
-  // decode batches: top-k and the plan in one single-workgroup launch
+  // decode batches: top-k and the plan in one single-workgroup launch; large
+  // batches with k dividing a dispatch segment: top-k fused with the
+  // dispatch histogram
   const bool small = T <= moe::kTopkDispatchSmallT && P <= moe::kDispatchSmallP;
+  const bool fused_hist = !small && moe::dispatch_takes_hist(T, k);
   e = run_router(hidden_states, router_weight, router_bias, Is ? shared_gate : nullptr, T, H, E, k,
-                 renormalize ? 1 : 0, dtype, logits, nullptr, ids, weights, Is ? L.gate_logit : nullptr, s, !small);
+                 renormalize ? 1 : 0, dtype, logits, nullptr, ids, weights, Is ? L.gate_logit : nullptr, s,
+                 !small && !fused_hist);
+  if (e == hipSuccess && fused_hist)
+    e = moe::launch_topk_hist(logits, T, E, k, renormalize ? 1 : 0, ids, weights, L.dispatch_scratch, s);
   if (e != hipSuccess) return hip_status(e, "moe_forward(router)");
   // the dispatch also zeroes the tile counters of the routed GEMMs
   if (small)
@@ -705,7 +711,7 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
                                         L.perm, L.inv, L.packed_ids, s, L.counters, 2 * moe::kTileCounterInts);
   else
     e = moe::launch_dispatch(ids, nullptr, T, k, E, L.counts, L.offsets, L.perm, L.inv, L.packed_ids, nullptr,
-                             L.dispatch_scratch, s, L.counters, 2 * moe::kTileCounterInts);
+                             L.dispatch_scratch, s, L.counters, 2 * moe::kTileCounterInts, fused_hist);
   if (e != hipSuccess) return hip_status(e, "moe_forward(dispatch)");
   if (Is) {
     hipStream_t ss = aux != nullptr ? aux->stream : s;

@@ -53,6 +53,39 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __res
     for (int e = lane; e < E; e += 64) cnt[(int64_t)e * U + u] = h[w][e];
 }
 
+// Top-k of the tokens of one dispatch segment, then that segment's expert
+// histogram, for k dividing the segment size: workgroup u owns assignments
+// [u*kSeg, (u+1)*kSeg), i.e. tokens [u*kSeg/k, (u+1)*kSeg/k).  Its 16 waves
+// select those tokens' top-k with topk_row (the same ids and weights as the
+// router's top-k kernel; the ids also go to LDS), then the workgroup counts
+// the segment's ids in LDS and writes cnt[e][u] exactly as
+// dispatch_hist_kernel does, which saves that launch.
+template <int VPL>
+__global__ __launch_bounds__(1024) void topk_hist_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                         int renorm, int32_t* __restrict__ ids,
+                                                         float* __restrict__ weights, int U,
+                                                         int32_t* __restrict__ cnt) {
+  __shared__ int s_ids[kSeg];
+  __shared__ int h[kMaxE];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int u = blockIdx.x;
+  const int tpw = kSeg / k;  // tokens per segment
+  const int t0 = u * tpw;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) h[e] = 0;
+  for (int j = w; j < tpw; j += (int)(blockDim.x >> 6)) {
+    const int t = t0 + j;
+    if (t >= T) break;  // wave-uniform
+    topk_row<VPL>(logits + (int64_t)t * E, E, k, renorm, ids + (int64_t)t * k, weights + (int64_t)t * k, nullptr,
+                  lane, s_ids + j * k);
+  }
+  __syncthreads();
+  const int a = u * kSeg + (int)threadIdx.x;
+  if (threadIdx.x < kSeg && a < T * k) atomicAdd(&h[s_ids[threadIdx.x]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[(int64_t)e * U + u] = h[e];
+}
+
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -331,11 +364,35 @@ size_t dispatch_scratch_bytes(int64_t P, int64_t E) {
   return (size_t)(2 * U * E * (int64_t)sizeof(int32_t));  // counts, then bases
 }
 
+bool dispatch_takes_hist(int T, int k) {
+  const int64_t P = (int64_t)T * k;
+  return P > kDispatchSmallP && kSeg % k == 0;
+}
+
+hipError_t launch_topk_hist(const float* logits, int T, int E, int k, int renorm, int32_t* ids, float* weights,
+                            void* scratch, hipStream_t s) {
+  if (!dispatch_takes_hist(T, k)) return hipErrorInvalidValue;
+  const int P = T * k;
+  const int U = (P + kSeg - 1) / kSeg;
+  int32_t* cnt = static_cast<int32_t*>(scratch);
+  profile_begin("router_topk_hist", s);
+#define MOE_TOPK_HIST(VPL) \
+  hipLaunchKernelGGL(topk_hist_kernel<VPL>, dim3(U), dim3(1024), 0, s, logits, T, E, k, renorm, ids, weights, U, cnt)
+  if (E <= 64) MOE_TOPK_HIST(1);
+  else if (E <= 128) MOE_TOPK_HIST(2);
+  else if (E <= 256) MOE_TOPK_HIST(4);
+  else MOE_TOPK_HIST(8);
+#undef MOE_TOPK_HIST
+  profile_end(s);
+  return hipGetLastError();
+}
+
 hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int E, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* packed_ids, float* packed_w,
-                           void* scratch, hipStream_t s, int* zero_ints, int n_zero) {
+                           void* scratch, hipStream_t s, int* zero_ints, int n_zero, bool have_hist) {
   const int P = T * k;
   if (P == 0) return hipSuccess;
+  if (have_hist && !dispatch_takes_hist(T, k)) return hipErrorInvalidValue;
   if (P <= kDispatchSmallP) {
     profile_begin("dispatch_small", s);
     hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), (size_t)kSmallWaves * E * sizeof(int), s, ids, w,
@@ -347,9 +404,11 @@ hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int
   int32_t* cnt = reinterpret_cast<int32_t*>(scratch);
   int32_t* base = cnt + (int64_t)U * E;
   const unsigned blocks = (unsigned)((U + 3) / 4);
-  profile_begin("dispatch_hist", s);
-  hipLaunchKernelGGL(dispatch_hist_kernel, dim3(blocks), dim3(256), 0, s, ids, P, E, U, cnt);
-  profile_end(s);
+  if (!have_hist) {
+    profile_begin("dispatch_hist", s);
+    hipLaunchKernelGGL(dispatch_hist_kernel, dim3(blocks), dim3(256), 0, s, ids, P, E, U, cnt);
+    profile_end(s);
+  }
   profile_begin("dispatch_scan", s);
   const dim3 sgrid((unsigned)((E + 3) / 4));
   if (U <= 64)

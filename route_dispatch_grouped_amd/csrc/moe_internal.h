@@ -113,10 +113,21 @@ hipError_t launch_ep_rank_counts(const int32_t* offsets, int E, int G, int32_t* 
 constexpr int kDispatchSegment = 128;  // assignments per wave-segment
 constexpr int kDispatchSmallP = 4096;  // up to this many assignments: one workgroup, all in LDS
 size_t dispatch_scratch_bytes(int64_t P, int64_t E);
+// have_hist: the segment histogram is already in the scratch (written by
+// launch_topk_hist), so the histogram launch is skipped.
 hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int E,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                            int32_t* packed_ids, float* packed_w, void* scratch, hipStream_t s,
-                           int* zero_ints = nullptr, int n_zero = 0);
+                           int* zero_ints = nullptr, int n_zero = 0, bool have_hist = false);
+// True when launch_dispatch(T, k) runs the segmented passes and k divides a
+// segment, so that launch_topk_hist can stand in for the top-k and the
+// histogram.
+bool dispatch_takes_hist(int T, int k);
+// The router's top-k (ids and weights, no probabilities) fused with the
+// dispatch histogram written into `scratch` (the dispatch scratch of the same
+// T, k, E).
+hipError_t launch_topk_hist(const float* logits, int T, int E, int k, int renorm, int32_t* ids, float* weights,
+                            void* scratch, hipStream_t s);
 
 // Top-k of T <= kTopkDispatchSmallT tokens fused with the one-workgroup plan
 // (T*k <= kDispatchSmallP): the same ids, weights and plan as launch_topk

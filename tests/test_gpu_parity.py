@@ -382,6 +382,31 @@ def test_forward_degenerate_shapes(k, E):
         assert (w == 1.0).all()
 
 
+@pytest.mark.parametrize("T,E,k", [(700, 128, 8), (5000, 32, 1), (1200, 96, 4), (600, 128, 16), (4100, 16, 2),
+                                   (2000, 64, 3), (900, 60, 6), (1000, 512, 5)])
+def test_forward_routing_paths_large_batches(T, E, k):
+    """Batches past the single-workgroup plan: with k dividing a dispatch
+    segment the forward fuses the top-k with the dispatch histogram, otherwise
+    it runs them apart.  Either way the forward's ids and weights equal the
+    router entry point's bit for bit, and the output (through the plan)
+    matches the oracle fed that routing."""
+    cfg = workloads.config("qwen3_30b_a3b_prefill").scaled(
+        name="routing_paths", num_tokens=T, hidden_size=128, num_experts=E, top_k=k, intermediate_size=64)
+    assert T * k > 4096
+    inp = workloads.generate(cfg, seed=T + E + k)
+    dev = device_inputs(inp)
+    f = gpu_forward(cfg, dev)
+    r = rdg.moe_router_topk(dev["x"], dev["router_weight"], k, renormalize=cfg.renormalize)
+    assert torch.equal(f["topk_ids"], r["topk_ids"])
+    assert torch.equal(f["topk_weights"].view(torch.int32), r["topk_weights"].view(torch.int32))
+    ids = f["topk_ids"].cpu().numpy()
+    w = f["topk_weights"].cpu().numpy().astype(np.float64)
+    res = oracle.forward(inp, k, cfg.renormalize, ids=ids, weights=w)
+    err, rms = rel_max_err(f["out"].cpu().numpy().astype(np.float64), res["out"])
+    log(f"[parity] routing paths T={T} E={E} k={k}: max|err|/rms = {err / rms:.3e}")
+    assert err <= tol_for(cfg) * rms
+
+
 def test_forward_zero_tokens_and_one_token():
     cfg = workloads.config("qwen3_30b_a3b_prefill").scaled(num_tokens=1, hidden_size=128, num_experts=16,
                                                            intermediate_size=64)
