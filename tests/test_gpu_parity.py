@@ -383,6 +383,7 @@ def test_forward_degenerate_shapes(k, E):
 
 
 @pytest.mark.parametrize("T,E,k", [(700, 128, 8), (5000, 32, 1), (1200, 96, 4), (600, 128, 16), (4100, 16, 2),
+                                   (600, 512, 8), (300, 256, 16), (70, 128, 64),
                                    (2000, 64, 3), (900, 60, 6), (1000, 512, 5)])
 def test_forward_routing_paths_large_batches(T, E, k):
     """Batches past the single-workgroup plan: with k dividing a dispatch
