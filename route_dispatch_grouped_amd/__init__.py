@@ -535,6 +535,11 @@ class MoeLayer:
             self._out = torch.empty((num_tokens, self.hidden_size), dtype=self.out_dtype, device=device)
 
     def forward(self, x: torch.Tensor, stream=None) -> torch.Tensor:
+        """The layer's output ``[T, H]`` for ``x [T, H]``, enqueued on ``stream``
+        (torch's current stream by default).  The result is a view of the
+        layer's own output buffer, which the next call overwrites (clone it to
+        keep it); the workspace is the layer's too, so calls of one layer that
+        may overlap in time must be on one stream."""
         T = x.shape[0]
         self.reserve(T, x.device)
         out = self._out[:T]
