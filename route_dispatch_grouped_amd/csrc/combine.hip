@@ -5,7 +5,8 @@
 //            (+ sigmoid(gate[t]) * shared[t])
 // y is fp32, bf16, or fp16 with a power-of-two exponent per (row, 64 columns)
 // (every format widened exactly); shared is fp32, or bf16 with bf16 y; the sum
-// is fp32 in every case.  One workgroup per token; each thread owns groups of
+// is fp32 in every case.  One workgroup per token (for small batches, one
+// wave per 64 column groups of a token); each thread owns groups of
 // VEC consecutive columns (one 16-byte load per packed row: 4 fp32 or 8
 // 16-bit values), so every packed row is read once, fully coalesced.
 #include <math.h>
@@ -64,7 +65,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   const int HV = H / VEC;
   float gate = 1.f;
   if (shared_ != nullptr && sgl != nullptr) gate = 1.0f / (1.0f + expf(-sgl[t]));
-  for (int cbase = 0; cbase < HV; cbase += CPT * (int)blockDim.x) {
+  // gridDim.y workgroups share a token's columns (small batches), one pass each
+  const int step = CPT * (int)blockDim.x;
+  for (int cbase = (int)blockIdx.y * step; cbase < HV; cbase += step * (int)gridDim.y) {
     float acc[CPT][VEC];
     int col[CPT];
 #pragma unroll
@@ -152,6 +155,14 @@ void launch_typed(const void* y, const int32_t* ys, const int32_t* inv, const fl
                   const float* shared_gate_logit, int T, int H, int k, int out_bf16, void* out, hipStream_t s) {
   // 16-byte column groups: up to 256 threads, each owning CPT groups
   const int HV = H / (MODE == Y_F32 ? 4 : 8);
+  if (T < 256 && HV > 64) {
+    // few tokens: one wave per 64 column groups, so the chip has work and each
+    // workgroup is done after one round of loads
+    const dim3 grid((unsigned)T, (unsigned)((HV + 63) / 64));
+    hipLaunchKernelGGL((combine_kernel<8, 1, MODE>), grid, dim3(64), 0, s, y, ys, inv, w, shared, shared_gate_logit, H,
+                       k, out_bf16, out);
+    return;
+  }
   const int threads = HV > 256 ? 256 : ((HV + 63) / 64) * 64;
   const int cpt = (HV + threads - 1) / threads;
   if (cpt <= 1)
