@@ -545,7 +545,8 @@ def test_no_renormalize():
 
 
 @pytest.mark.parametrize("ydt", ["f32", "bf16"])
-@pytest.mark.parametrize("T,H,k", [(5, 4160, 2), (9, 24, 10), (3, 8, 1), (17, 1032, 9), (4, 4096, 3)])
+@pytest.mark.parametrize("T,H,k", [(5, 4160, 2), (9, 24, 10), (3, 8, 1), (17, 1032, 9), (4, 4096, 3),
+                                   (300, 2048, 8)])
 def test_combine_shapes(T, H, k, ydt):
     """Combine over row widths that need several column passes (H = 4160),
     partial column groups (H = 24, 8, 1032) and more slots than one gather pass
@@ -580,6 +581,12 @@ def test_combine_shapes(T, H, k, ydt):
                             shared_gate_logit=to_device(gl)).cpu().numpy().astype(np.float64)
     err_s, rms_s = rel_max_err(out_s, ref_s)
     assert err_s <= 1e-5 * rms_s + 1e-30
+    # bf16 output: the same fp32 sums, each rounded once to nearest even
+    out_b = rdg.moe_combine(dev_y(y), to_device(inv), to_device(w), shared_output=dev_y(shared),
+                            shared_gate_logit=to_device(gl), out_dtype=torch.bfloat16)
+    out_f = rdg.moe_combine(dev_y(y), to_device(inv), to_device(w), shared_output=dev_y(shared),
+                            shared_gate_logit=to_device(gl))
+    assert torch.equal(out_b.view(torch.int16), out_f.to(torch.bfloat16).view(torch.int16))
 
 
 def _ep_check(ids, w, T, k, start, end):
