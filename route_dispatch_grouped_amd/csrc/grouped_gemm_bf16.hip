@@ -43,6 +43,8 @@
 // in the same lane of the accumulators).  Rows past the end of a group read a
 // clamped (valid) row and are never stored; 16-row sub-tiles wholly past the
 // end skip their MFMAs (a straight-line K loop per live sub-tile count).
+#include <atomic>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -1655,21 +1657,26 @@ __global__ void zero_ints_kernel(int* p, int n) {
   if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
 }
 
+// Workgroups of `kernel` (kThreads threads, no dynamic LDS) that fit on one
+// CU, queried once per device and kept in `cache`.
+template <typename Kern>
+int occupancy_per_cu(std::atomic<int> (&cache)[64], Kern kernel) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, 0) != hipSuccess || n < 1) n = 1;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // Resident workgroups per CU for one instantiation (the persistent grid must
 // fit in one wave of residency, or the static tile split would serialise).
 template <int BM, int EPI, int BR>
 int resident_blocks_per_cu() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grouped_gemm_bf16_kernel<BM, EPI, BR>, kThreads, 0) !=
-            hipSuccess || n < 1)
-      n = 1;
-    cached[dev] = n;
-  }
-  return cached[dev];
+  static std::atomic<int> cache[64];
+  return occupancy_per_cu(cache, grouped_gemm_bf16_kernel<BM, EPI, BR>);
 }
 
 // m-tile height the grouped GEMM picks for M rows in `groups` groups (0: the
@@ -1756,17 +1763,8 @@ hipError_t launch_bm(const GemmArgs& a_in, hipStream_t s, const char* name) {
 
 template <int BM, int EPI>
 int resident_stream_per_cu() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grouped_gemm_bf16_stream_kernel<BM, EPI>, kThreads, 0) !=
-            hipSuccess || n < 1)
-      n = 1;
-    cached[dev] = n;
-  }
-  return cached[dev];
+  static std::atomic<int> cache[64];
+  return occupancy_per_cu(cache, grouped_gemm_bf16_stream_kernel<BM, EPI>);
 }
 
 template <int BM, int EPI>
@@ -1796,17 +1794,8 @@ hipError_t launch_stream(const GemmArgs& a_in, hipStream_t s, const char* name) 
 
 template <int EPI>
 int resident_big_per_cu() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grouped_gemm_bf16_big_kernel<EPI>, kThreads, 0) !=
-            hipSuccess || n < 1)
-      n = 1;
-    cached[dev] = n;
-  }
-  return cached[dev];
+  static std::atomic<int> cache[64];
+  return occupancy_per_cu(cache, grouped_gemm_bf16_big_kernel<EPI>);
 }
 
 template <int EPI>
