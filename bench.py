@@ -152,43 +152,111 @@ def roofline_entry(name, cfg, avg_s, touched):
             "avg_us": round(avg_s * 1e6, 2), "algorithmic_flops": flops, "algorithmic_bytes": nbytes}
 
 
-def cpu_baseline(cfg, inp, sample_tokens, target_s):
-    """Time the float64 oracle on the first `sample_tokens` tokens of the workload."""
-    import oracle
+def host_info():
+    """The host CPU model, the threads available to this process, and the BLAS
+    library NumPy runs on with its thread count."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = "unknown", None
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        for d in threadpool_info():
+            if d.get("user_api") == "blas":
+                blas = f"{d.get('internal_api')} {d.get('version')} ({os.path.basename(d.get('filepath', ''))})"
+                threads = int(d.get("num_threads", 1))
+                break
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
+    return {"cpu_model": model, "affinity_cpus": affinity, "blas": blas,
+            "blas_threads": threads if threads is not None else affinity}
+
+
+def cpu_baseline(cfg, inp, sample_tokens, target_s, repeats=3):
+    """Time the float64 oracle on the first `sample_tokens` tokens of the
+    workload (grown toward `target_s` seconds per run, at most the whole
+    batch); the median of `repeats` runs."""
+    import oracle
+    info = host_info()
     S = min(sample_tokens, cfg.num_tokens)
     sub = dict(inp)
-    sub["x"] = inp["x"][:S]
-    t0 = time.perf_counter()
-    oracle.forward(sub, cfg.top_k, cfg.renormalize)
-    dt = time.perf_counter() - t0
+
+    def run(n):
+        sub["x"] = inp["x"][:n]
+        t0 = time.perf_counter()
+        oracle.forward(sub, cfg.top_k, cfg.renormalize)
+        return time.perf_counter() - t0
+
+    dt = run(S)
     # grow the sample once if it was far below the target duration
     if dt < target_s / 3 and S < cfg.num_tokens:
         S2 = min(cfg.num_tokens, int(S * min(8.0, target_s / max(dt, 1e-3))))
         if S2 > S:
             S = S2
-            sub["x"] = inp["x"][:S]
-            t0 = time.perf_counter()
-            oracle.forward(sub, cfg.top_k, cfg.renormalize)
-            dt = time.perf_counter() - t0
-    return {"value": round(S / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            dt = run(S)
+    times = [dt] + [run(S) for _ in range(repeats - 1)]
+    med = float(np.median(times))
+    return {"value": round(S / med, 2), "unit": "tokens/s", "cores": int(info["blas_threads"]), "kind": "oracle",
             "sample": f"float64 NumPy oracle forward (router, top-k, dispatch plan, per-expert SwiGLU, combine) "
-                      f"over the first {S} of {cfg.num_tokens} tokens with the full layer weights; {dt:.2f} s",
-            "seconds": round(dt, 3)}
+                      f"over the first {S} of {cfg.num_tokens} tokens with the full layer weights; median of "
+                      f"{len(times)} runs {med:.2f} s",
+            "seconds": round(med, 3), "runs_s": [round(t, 3) for t in times], **info}
+
+
+def y_storage(cfg):
+    """How the forward stores the packed expert outputs y, i.e. the byte basis
+    of the down projection's and the combine's algorithmic bytes."""
+    b = y_bytes_per_value(cfg)
+    fmt = ("fp16 values scaled by a power of two, one int32 exponent per (row, 64 columns)" if b < 4
+           else "fp32")
+    return {"bytes_per_value": b, "format": fmt,
+            "note": "down and combine algorithmic bytes count y at bytes_per_value; at fp32 y (4 B/value) they "
+                    "would count P*H*(4 - bytes_per_value) more bytes each"}
 
 
 SECONDARY_WORKLOAD = "qwen15_moe_decode"
 
 
-def decode_measure(rdg, torch, seed, steps=400, warmup=50):
+def _percentiles(ms):
+    a = np.asarray(ms, dtype=np.float64)
+    return {"p10_ms": round(float(np.percentile(a, 10)), 4), "p50_ms": round(float(np.percentile(a, 50)), 4),
+            "p90_ms": round(float(np.percentile(a, 90)), 4), "mean_ms": round(float(a.mean()), 4)}
+
+
+def timed_forwards(torch, fwd, steps, flush=None):
+    """Per-forward durations (ms) from HIP events on the current stream, which
+    the forward joins back to (its shared expert's stream included).  With
+    `flush`, a scratch stream of memory runs before every forward, outside
+    the events, so each forward starts with cold caches (L2 and the MALL)."""
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        if flush is not None:
+            flush()
+        a.record(st)
+        fwd()
+        b.record(st)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def decode_measure(rdg, torch, seed, steps=400, warmup=50, flushed_steps=100, flush_mib=1024):
     """The memory-bound decode shape beside the headline: one forward per
     step, reported as tokens/s and as weight bytes streamed per second against
     the HBM peak.  Bytes per step: the touched experts' w13 and w2, the shared
-    expert's weights, the router and gate rows (activations are negligible)."""
+    expert's weights, the router and gate rows (activations are negligible).
+    Two regimes: back-to-back forwards (weights may stay in the 256 MB MALL
+    between steps) and forwards each preceded by a copy of `flush_mib` MiB
+    (the weights come from HBM), each with event-timed p10/p50/p90."""
     cfg = workloads.config(SECONDARY_WORKLOAD)
     inp = workloads.generate(cfg, seed=seed)
 
@@ -211,16 +279,31 @@ def decode_measure(rdg, torch, seed, steps=400, warmup=50):
         layer(x)
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
+    warm = timed_forwards(torch, lambda: layer(x), steps)
+    n = flush_mib * (1 << 20) // 4
+    fa = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    fb = torch.empty_like(fa)
+    cold = timed_forwards(torch, lambda: layer(x), flushed_steps, flush=lambda: fb.copy_(fa))
+    del fa, fb
     r = rdg.moe_router_topk(x, d["router_weight"], cfg.top_k, renormalize=cfg.renormalize)
     counts = rdg.moe_dispatch_plan(r["topk_ids"], None, cfg.num_experts)["counts"].cpu().numpy()
     touched = int((counts > 0).sum())
     H, I, Is, E = cfg.hidden_size, cfg.intermediate_size, cfg.shared_intermediate_size, cfg.num_experts
     nbytes = touched * 3 * I * H * 2 + 3 * Is * H * 2 + (E + 1) * H * 2
     gbs = nbytes / dt / 1e9
+
+    def regime(ms, label):
+        p = _percentiles(ms)
+        gb = {f"gbs_{q}": round(nbytes / (p[f"{q}_ms"] * 1e-3) / 1e9, 1) for q in ("p10", "p50", "p90")}
+        return {"caches": label, "forwards": len(ms), **p, **gb,
+                "frac_hbm_peak_p50": round(gb["gbs_p50"] / PEAK_HBM_GBS, 4)}
+
     res = {"workload": cfg.name, "steps": steps, "warmup": warmup, "ms_per_step": round(dt * 1e3, 4),
            "value": round(cfg.num_tokens / dt, 1), "unit": "tokens/s", "experts_touched": touched,
            "weight_bytes_per_step": nbytes, "achieved": round(gbs, 1), "achieved_unit": "GB/s",
-           "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+           "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+           "unflushed": regime(warm, "back-to-back forwards (weights may stay in the MALL)"),
+           "flushed": regime(cold, f"a {flush_mib} MiB device copy before every forward (cold L2 and MALL)")}
     # one rank of an 8-way tensor-parallel split (I / 8 and Is / 8, router and
     # gate replicated): the same tokens stream an eighth of the expert weights
     G = 8
@@ -475,7 +558,9 @@ def main():
         log(f"[bench] secondary: {SECONDARY_WORKLOAD}")
         secondary = decode_measure(rdg, torch, args.seed)
         log(f"[bench] {SECONDARY_WORKLOAD}: {secondary['ms_per_step']} ms/step, {secondary['achieved']} GB/s "
-            f"({100 * secondary['frac_hbm_peak']:.1f} % of HBM peak)")
+            f"({100 * secondary['frac_hbm_peak']:.1f} % of HBM peak); p50 unflushed "
+            f"{secondary['unflushed']['p50_ms']} ms ({secondary['unflushed']['gbs_p50']} GB/s), flushed "
+            f"{secondary['flushed']['p50_ms']} ms ({secondary['flushed']['gbs_p50']} GB/s)")
 
     tp = None
     if not args.no_secondary and cfg.name == DEFAULT_WORKLOAD and cfg.dtype == "bf16":
@@ -506,6 +591,7 @@ def main():
                    "seed": args.seed, "experts_touched": touched, "max_expert_rows": int(counts.max()),
                    "inputs": "x~N(0,1), weights~N(0,0.02), bf16 RNE; seeded PCG64 streams"},
         "roofline": roof,
+        "y_storage": y_storage(cfg),
         "grouped_ffn": ffn,
         "kernels": per_kernel,
         "ep_routing_table": ep,

@@ -102,9 +102,10 @@ const char* moe_last_error_message(void);
  *
  * hidden_states [T,H] dtype; router_weight [E,H] dtype; router_bias [E] f32 or
  * NULL (added before the softmax, so it moves the selection and the weights);
- * shared_gate [H] dtype or NULL; router_logits [T,E] f32 (required: the
- * top-k stage reads it back); routing_probs [T,E] f32 or NULL; topk_ids [T,k]
- * int32 (required);
+ * shared_gate [H] dtype or NULL; router_logits [T,E] f32 (required, never
+ * NULL: the top-k stage reads the logits back from this buffer, and the
+ * library allocates no memory of its own to hold them); routing_probs [T,E]
+ * f32 or NULL; topk_ids [T,k] int32 (required);
  * topk_weights [T,k] f32 (required); shared_gate_logit [T] f32, required iff
  * shared_gate != NULL.
  * Errors: INVALID_ARG for a NULL required pointer, k < 1 or k > E, negative
@@ -302,8 +303,16 @@ moe_status moe_combine(const void* packed_expert_outputs, const int32_t* inverse
  * Optional outputs (NULL to skip): topk_ids_out [T,k] int32, topk_weights_out
  * [T,k] f32, router_logits_out [T,E] f32.
  * workspace: moe_forward_workspace_size(...) bytes; it holds the routing, the
- * plan, h and the packed expert outputs (fp32: bf16 storage would about
- * double the output error of a bf16 layer).
+ * plan, h and the packed expert outputs y in a slot of P*H*4 bytes.  What y
+ * holds there depends on the batch: fp32 values for f32 layers and for bf16
+ * layers with fewer than 96 packed rows per expert on average (decode-sized
+ * batches); for bf16 layers with at least 96 (prefill-sized batches) and H a
+ * multiple of 64, fp16 values y*2^s (P*H*2 bytes) followed by one int32
+ * exponent s per (row, 64 columns) (P*H/16 bytes), s chosen per segment from
+ * its largest magnitude so the fp16 values keep 11 significant bits without
+ * overflow.  Both carry about 8x the precision of bf16 storage, which would
+ * about double the output error of a bf16 layer.  The y slot is internal to
+ * the forward (moe_grouped_ffn returns fp32 or bf16 expert outputs).
  */
 size_t moe_forward_workspace_size(int64_t num_tokens, int64_t hidden_size, int64_t num_experts,
                                   int64_t top_k, int64_t intermediate_size,

@@ -17,6 +17,7 @@ layer" of the DWDP README's ``build_reference``).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Dict, Optional
@@ -156,6 +157,16 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream=None):
+    """Context in which outputs and workspaces are allocated: torch's current
+    stream switched to ``stream``, the stream the library's kernels run on.
+    torch's caching allocator hands a freed block only to later allocations on
+    the stream it was allocated on, which run after those kernels; a block
+    allocated on another stream could be reused while they still read or write
+    it."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _need(t: torch.Tensor, name: str, shape, dtype=None) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -188,15 +199,16 @@ def moe_router_topk(hidden_states: torch.Tensor, router_weight: torch.Tensor, to
     if shared_gate is not None:
         _need(shared_gate, "shared_gate", (H,), dt)
     dev = hidden_states.device
-    out = {
-        "logits": torch.empty((T, E), dtype=torch.float32, device=dev),
-        "topk_ids": torch.empty((T, top_k), dtype=torch.int32, device=dev),
-        "topk_weights": torch.empty((T, top_k), dtype=torch.float32, device=dev),
-    }
-    if return_probs:
-        out["probs"] = torch.empty((T, E), dtype=torch.float32, device=dev)
-    if shared_gate is not None:
-        out["shared_gate_logit"] = torch.empty((T,), dtype=torch.float32, device=dev)
+    with _on(stream):
+        out = {
+            "logits": torch.empty((T, E), dtype=torch.float32, device=dev),
+            "topk_ids": torch.empty((T, top_k), dtype=torch.int32, device=dev),
+            "topk_weights": torch.empty((T, top_k), dtype=torch.float32, device=dev),
+        }
+        if return_probs:
+            out["probs"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+        if shared_gate is not None:
+            out["shared_gate_logit"] = torch.empty((T,), dtype=torch.float32, device=dev)
     st = lib.moe_router_topk(_ptr(hidden_states), _ptr(router_weight), _ptr(router_bias), _ptr(shared_gate),
                              T, H, E, int(top_k), int(bool(renormalize)), _dtype_code(dt),
                              _ptr(out["logits"]), _ptr(out.get("probs")), _ptr(out["topk_ids"]),
@@ -222,13 +234,14 @@ def moe_router_topk_grouped(hidden_states: torch.Tensor, router_weight: torch.Te
     if router_bias is not None:
         _need(router_bias, "router_bias", (E,), torch.float32)
     dev = hidden_states.device
-    out = {
-        "logits": torch.empty((T, E), dtype=torch.float32, device=dev),
-        "topk_ids": torch.empty((T, top_k), dtype=torch.int32, device=dev),
-        "topk_weights": torch.empty((T, top_k), dtype=torch.float32, device=dev),
-    }
-    if return_probs:
-        out["probs"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+    with _on(stream):
+        out = {
+            "logits": torch.empty((T, E), dtype=torch.float32, device=dev),
+            "topk_ids": torch.empty((T, top_k), dtype=torch.int32, device=dev),
+            "topk_weights": torch.empty((T, top_k), dtype=torch.float32, device=dev),
+        }
+        if return_probs:
+            out["probs"] = torch.empty((T, E), dtype=torch.float32, device=dev)
     st = lib.moe_router_topk_grouped(_ptr(hidden_states), _ptr(router_weight), _ptr(router_bias), T, H, E,
                                      int(top_k), int(n_group), int(topk_group), int(bool(renormalize)),
                                      _dtype_code(dt), _ptr(out["logits"]), _ptr(out.get("probs")),
@@ -249,8 +262,18 @@ def moe_dispatch_plan(topk_ids: torch.Tensor, topk_weights: Optional[torch.Tenso
     _need(topk_ids, "topk_ids", (T, k), torch.int32)
     if topk_weights is not None:
         _need(topk_weights, "topk_weights", (T, k), torch.float32)
-    dev = topk_ids.device
-    P = T * k
+    with _on(stream):
+        out = _plan_outputs(T * k, num_experts, topk_ids.device, topk_weights is not None)
+        ws_bytes = lib.moe_dispatch_workspace_size(T, k, num_experts)
+        ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=topk_ids.device)
+    st = lib.moe_dispatch_plan(_ptr(topk_ids), _ptr(topk_weights), T, k, int(num_experts), _ptr(out["counts"]),
+                               _ptr(out["offsets"]), _ptr(out["perm"]), _ptr(out["inv"]), _ptr(out["packed_ids"]),
+                               _ptr(out.get("packed_w")), _ptr(ws), ws.numel(), _stream(stream))
+    _check("moe_dispatch_plan", st)
+    return out
+
+
+def _plan_outputs(P: int, num_experts: int, dev, with_weights: bool) -> Dict[str, torch.Tensor]:
     out = {
         "counts": torch.empty((num_experts,), dtype=torch.int32, device=dev),
         "offsets": torch.empty((num_experts + 1,), dtype=torch.int32, device=dev),
@@ -258,14 +281,8 @@ def moe_dispatch_plan(topk_ids: torch.Tensor, topk_weights: Optional[torch.Tenso
         "inv": torch.empty((P,), dtype=torch.int32, device=dev),
         "packed_ids": torch.empty((P,), dtype=torch.int32, device=dev),
     }
-    if topk_weights is not None:
+    if with_weights:
         out["packed_w"] = torch.empty((P,), dtype=torch.float32, device=dev)
-    ws_bytes = lib.moe_dispatch_workspace_size(T, k, num_experts)
-    ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
-    st = lib.moe_dispatch_plan(_ptr(topk_ids), _ptr(topk_weights), T, k, int(num_experts), _ptr(out["counts"]),
-                               _ptr(out["offsets"]), _ptr(out["perm"]), _ptr(out["inv"]), _ptr(out["packed_ids"]),
-                               _ptr(out.get("packed_w")), _ptr(ws), ws.numel(), _stream(stream))
-    _check("moe_dispatch_plan", st)
     return out
 
 
@@ -286,12 +303,13 @@ def moe_ep_routing_table(gate_indices: torch.Tensor, gate_weights: torch.Tensor,
         raise TypeError("gate_indices must be an int32 and gate_weights a float32 device tensor")
     dev = gi.device
     P = max(int(num_tokens) * int(top_k), 0)
-    out = {name: torch.empty((P,), dtype=torch.float32 if name.endswith("weights") else torch.int32, device=dev)
-           for name in ("local_token_indices", "local_expert_ids", "local_weights", "remote_token_indices",
-                        "remote_expert_ids", "remote_weights")}
-    out["counts"] = torch.empty((2,), dtype=torch.int32, device=dev)
-    ws_bytes = lib.moe_ep_routing_table_workspace_size(int(num_tokens), int(top_k))
-    ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
+    with _on(stream):
+        out = {name: torch.empty((P,), dtype=torch.float32 if name.endswith("weights") else torch.int32, device=dev)
+               for name in ("local_token_indices", "local_expert_ids", "local_weights", "remote_token_indices",
+                            "remote_expert_ids", "remote_weights")}
+        out["counts"] = torch.empty((2,), dtype=torch.int32, device=dev)
+        ws_bytes = lib.moe_ep_routing_table_workspace_size(int(num_tokens), int(top_k))
+        ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
     st = lib.moe_ep_routing_table(_ptr(gi), gi.numel(), _ptr(gw), gw.numel(), int(num_tokens), int(top_k),
                                   int(local_expert_start), int(local_expert_end), _ptr(out["local_token_indices"]),
                                   _ptr(out["local_expert_ids"]), _ptr(out["local_weights"]),
@@ -300,6 +318,8 @@ def moe_ep_routing_table(gate_indices: torch.Tensor, gate_weights: torch.Tensor,
                                   _stream(stream))
     _check("moe_ep_routing_table", st)
     if trim:
+        if stream is not None:
+            stream.synchronize()
         nl, nr = (int(v) for v in out["counts"].cpu().tolist())
         for name in list(out):
             if name.startswith("local_"):
@@ -317,8 +337,9 @@ def moe_ep_rank_counts(expert_offsets: torch.Tensor, num_ranks: int, stream=None
     if expert_offsets.dim() != 1 or expert_offsets.numel() < 2:
         raise ValueError("expert_offsets must be [E+1]")
     E = expert_offsets.numel() - 1
-    counts = torch.empty((max(int(num_ranks), 0),), dtype=torch.int32, device=expert_offsets.device)
-    starts = torch.empty((max(int(num_ranks), 0) + 1,), dtype=torch.int32, device=expert_offsets.device)
+    with _on(stream):
+        counts = torch.empty((max(int(num_ranks), 0),), dtype=torch.int32, device=expert_offsets.device)
+        starts = torch.empty((max(int(num_ranks), 0) + 1,), dtype=torch.int32, device=expert_offsets.device)
     lib = load_library()
     _check("moe_ep_rank_counts", lib.moe_ep_rank_counts(_ptr(expert_offsets), E, int(num_ranks), _ptr(counts),
                                                         _ptr(starts), _stream(stream)))
@@ -347,9 +368,10 @@ def moe_grouped_ffn(hidden_states: torch.Tensor, packed_token_indices: Optional[
     if expert_offsets is not None:
         _need(expert_offsets, "expert_offsets", (E + 1,), torch.int32)
     dev = hidden_states.device
-    y = torch.empty((P, H), dtype=out_dtype, device=dev)
-    ws_bytes = lib.moe_grouped_ffn_workspace_size(T, H, top_k, E, I, _dtype_code(dt))
-    ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
+    with _on(stream):
+        y = torch.empty((P, H), dtype=out_dtype, device=dev)
+        ws_bytes = lib.moe_grouped_ffn_workspace_size(T, H, top_k, E, I, _dtype_code(dt))
+        ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
     st = lib.moe_grouped_ffn(_ptr(hidden_states), _ptr(packed_token_indices), _ptr(expert_offsets), _ptr(w13),
                              _ptr(w2), T, H, E, int(top_k), I, _dtype_code(dt), _dtype_code(out_dtype), _ptr(y),
                              _ptr(ws), ws.numel(), _stream(stream))
@@ -375,7 +397,8 @@ def moe_combine(packed_expert_outputs: torch.Tensor, inverse_permutation: torch.
         _need(shared_output, "shared_output", (T, H), ydt)
     if shared_gate_logit is not None:
         _need(shared_gate_logit, "shared_gate_logit", (T,), torch.float32)
-    out = torch.empty((T, H), dtype=out_dtype, device=packed_expert_outputs.device)
+    with _on(stream):
+        out = torch.empty((T, H), dtype=out_dtype, device=packed_expert_outputs.device)
     st = lib.moe_combine(_ptr(packed_expert_outputs), _ptr(inverse_permutation), _ptr(topk_weights),
                          _ptr(shared_output), _ptr(shared_gate_logit), T, H, k, _dtype_code(ydt),
                          _dtype_code(out_dtype), _ptr(out), _stream(stream))
@@ -476,18 +499,19 @@ def moe_forward(hidden_states: torch.Tensor, router_weight: torch.Tensor, w13: t
         _need(shared_w2, "shared_w2", (H, Is), dt)
         _need(shared_gate, "shared_gate", (H,), dt)
     dev = hidden_states.device
-    if out is None:
-        out = torch.empty((T, H), dtype=out_dtype, device=dev)
-    else:
-        _need(out, "out", (T, H), out_dtype)
-    ws_bytes = lib.moe_forward_workspace_size(T, H, E, top_k, I, Is, _dtype_code(dt))
-    if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
-    ids = wts = logits = None
-    if return_routing:
-        ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
-        wts = torch.empty((T, top_k), dtype=torch.float32, device=dev)
-        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((T, H), dtype=out_dtype, device=dev)
+        else:
+            _need(out, "out", (T, H), out_dtype)
+        ws_bytes = lib.moe_forward_workspace_size(T, H, E, top_k, I, Is, _dtype_code(dt))
+        if workspace is None or workspace.numel() < ws_bytes:
+            workspace = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
+        ids = wts = logits = None
+        if return_routing:
+            ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+            wts = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+            logits = torch.empty((T, E), dtype=torch.float32, device=dev)
     st = lib.moe_forward(_ptr(hidden_states), _ptr(router_weight), _ptr(router_bias), _ptr(w13), _ptr(w2),
                          _ptr(shared_w13), _ptr(shared_w2), _ptr(shared_gate), T, H, E, int(top_k), I, Is,
                          int(bool(renormalize)), _dtype_code(dt), _dtype_code(out_dtype), _ptr(out), _ptr(ids),
@@ -522,17 +546,30 @@ class MoeLayer:
         self.shared_intermediate_size = 0 if shared_w13 is None else shared_w13.shape[0] // 2
         self._ws = None
         self._out = None
+        self._last_stream = None
 
     def workspace_bytes(self, num_tokens: int) -> int:
         return moe_forward_workspace_size(num_tokens, self.hidden_size, self.num_experts, self.top_k,
                                           self.intermediate_size, self.shared_intermediate_size, self.w13.dtype)
 
-    def reserve(self, num_tokens: int, device) -> None:
+    def reserve(self, num_tokens: int, device, stream=None) -> None:
+        """Grow the workspace and output buffer to ``num_tokens`` tokens.  New
+        buffers are allocated on ``stream``; a replaced buffer is released only
+        after the work already enqueued on the stream of the layer's last
+        forward (which may still use it)."""
         need = max(self.workspace_bytes(num_tokens), 256)
-        if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty((need,), dtype=torch.uint8, device=device)
-        if self._out is None or self._out.shape[0] < num_tokens:
-            self._out = torch.empty((num_tokens, self.hidden_size), dtype=self.out_dtype, device=device)
+        grow_ws = self._ws is None or self._ws.numel() < need
+        grow_out = self._out is None or self._out.shape[0] < num_tokens
+        if not (grow_ws or grow_out):
+            return
+        for old, grow in ((self._ws, grow_ws), (self._out, grow_out)):
+            if grow and old is not None and self._last_stream is not None:
+                old.record_stream(self._last_stream)
+        with _on(stream):
+            if grow_ws:
+                self._ws = torch.empty((need,), dtype=torch.uint8, device=device)
+            if grow_out:
+                self._out = torch.empty((num_tokens, self.hidden_size), dtype=self.out_dtype, device=device)
 
     def forward(self, x: torch.Tensor, stream=None) -> torch.Tensor:
         """The layer's output ``[T, H]`` for ``x [T, H]``, enqueued on ``stream``
@@ -541,7 +578,8 @@ class MoeLayer:
         keep it); the workspace is the layer's too, so calls of one layer that
         may overlap in time must be on one stream."""
         T = x.shape[0]
-        self.reserve(T, x.device)
+        self.reserve(T, x.device, stream)
+        self._last_stream = stream if stream is not None else torch.cuda.current_stream()
         out = self._out[:T]
         return moe_forward(x, self.router_weight, self.w13, self.w2, self.top_k, self.router_bias, self.shared_w13,
                            self.shared_w2, self.shared_gate, self.renormalize, self.out_dtype,

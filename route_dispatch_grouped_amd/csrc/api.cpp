@@ -119,7 +119,7 @@ struct ForwardLayout {
   int32_t* packed_ids;
   void* dispatch_scratch;
   void* h;
-  float* y;  // packed expert outputs (fp32: bf16 would double the layer's output error)
+  float* y;  // packed expert outputs, a P*H*4-byte slot: fp32, or fp16 + per-(row, 64 columns) exponents
   void* hs;
   float* ys;
   int* counters;  // tile counters of the four grouped GEMMs (routed, shared)
@@ -262,40 +262,62 @@ struct ProfRecord {
   hipEvent_t stop;
 };
 // Second stream for the shared expert, which depends only on the input and
-// runs concurrently with the routed experts: created once per device on first
-// use, default priority, joined back through events (a pattern that HIP graph
-// capture records as a fork and a join).
-struct AuxStream {
+// runs concurrently with the routed experts: one per (device, caller stream),
+// created on first use, default priority, joined back through its own pair of
+// events (a pattern that HIP graph capture records as a fork and a join).
+// Keying by the caller's stream keeps independent caller streams independent:
+// their shared experts neither queue behind each other on one aux stream nor
+// share an event, and a graph capture on one caller stream never sees another
+// stream's work.  A slot's own mutex covers the enqueue of one forward (its
+// events are re-recorded by every forward on that caller stream); the table
+// lock is held only for the lookup.
+struct AuxSlot {
+  int dev = -1;
+  hipStream_t caller = nullptr;
   hipStream_t stream = nullptr;
   hipEvent_t fork = nullptr;
   hipEvent_t join = nullptr;
   bool ok = false;
-  bool tried = false;
+  std::mutex mu;
 };
-std::mutex g_aux_mu;
-AuxStream g_aux[64];
+constexpr int kMaxAuxSlots = 256;
+std::mutex g_aux_table_mu;
+AuxSlot g_aux_slots[kMaxAuxSlots];
+int g_aux_used = 0;
 
-// Returns the device's aux stream (with g_aux_mu held by the caller), or
-// nullptr when it cannot be created: the caller then stays on one stream.
-AuxStream* aux_stream() {
+// The aux slot of `caller` on the current device, or nullptr when there is
+// none and none can be made: the caller then runs the shared expert on its own
+// stream.  A slot is never created while `caller` is being captured into a
+// graph (creating streams and events there could invalidate the capture); a
+// caller that wants the fork inside a captured graph runs one forward on the
+// capture stream before capturing.
+AuxSlot* aux_slot(hipStream_t caller) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  AuxStream& a = g_aux[dev];
-  if (!a.tried) {
-    a.tried = true;
-    // The join only orders device work after device work (the shared
-    // expert's kernels before the combine), so it needs no system-scope
-    // fence; the fork keeps it, because the aux stream's first reads may
-    // follow a host-to-device copy on the caller's stream.
-    a.ok = hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking) == hipSuccess &&
-           hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) == hipSuccess &&
-           hipEventCreateWithFlags(&a.join, hipEventDisableTiming | hipEventDisableSystemFence) == hipSuccess;
-  }
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lk(g_aux_table_mu);
+  for (int i = 0; i < g_aux_used; ++i)
+    if (g_aux_slots[i].dev == dev && g_aux_slots[i].caller == caller)
+      return g_aux_slots[i].ok ? &g_aux_slots[i] : nullptr;
+  if (g_aux_used == kMaxAuxSlots) return nullptr;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(caller, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return nullptr;
+  AuxSlot& a = g_aux_slots[g_aux_used++];
+  a.dev = dev;
+  a.caller = caller;
+  // The join only orders device work after device work (the shared
+  // expert's kernels before the combine), so it needs no system-scope
+  // fence; the fork keeps it, because the aux stream's first reads may
+  // follow a host-to-device copy on the caller's stream.
+  a.ok = hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking) == hipSuccess &&
+         hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) == hipSuccess &&
+         hipEventCreateWithFlags(&a.join, hipEventDisableTiming | hipEventDisableSystemFence) == hipSuccess;
   return a.ok ? &a : nullptr;
 }
 
+// Kernel timing state.  g_prof_on is read without the lock first, so that a
+// launch with profiling off takes no process-wide lock.
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+std::atomic<bool> g_prof_on{false};
 std::vector<ProfRecord> g_prof;
 thread_local int g_prof_open = -1;
 
@@ -304,9 +326,10 @@ thread_local int g_prof_open = -1;
 namespace moe {
 
 void profile_begin(const char* name, hipStream_t s) {
-  std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_open = -1;
-  if (!g_prof_on) return;
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
   ProfRecord r{name, nullptr, nullptr};
   if (hipEventCreate(&r.start) != hipSuccess) return;
   if (hipEventCreate(&r.stop) != hipSuccess) {
@@ -319,6 +342,7 @@ void profile_begin(const char* name, hipStream_t s) {
 }
 
 void profile_end(hipStream_t s) {
+  if (g_prof_open < 0) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (g_prof_open < 0 || g_prof_open >= (int)g_prof.size()) return;
   (void)hipEventRecord(g_prof[g_prof_open].stop, s);
@@ -683,12 +707,12 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
   // routed experts; the join comes before the combine.  The routing launches
   // are enqueued first, so that the host's launch latency delays the shared
   // expert rather than the critical path.
-  std::unique_lock<std::mutex> aux_lock(g_aux_mu, std::defer_lock);
-  AuxStream* aux = nullptr;
+  std::unique_lock<std::mutex> aux_lock;
+  AuxSlot* aux = nullptr;
   if (Is) {
-    aux_lock.lock();
-    aux = aux_stream();
+    aux = aux_slot(s);
     if (aux != nullptr) {
+      aux_lock = std::unique_lock<std::mutex>(aux->mu);
       e = hipEventRecord(aux->fork, s);
       if (e == hipSuccess) e = hipStreamWaitEvent(aux->stream, aux->fork, 0);
       if (e != hipSuccess) return hip_status(e, "moe_forward(fork)");
@@ -767,7 +791,7 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
 
 void moe_profile_enable(int enable) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof_on = enable != 0;
+  g_prof_on.store(enable != 0, std::memory_order_relaxed);
 }
 
 int moe_profile_collect(const char** names, double* total_ms, int64_t* launches, int capacity) {

@@ -6,7 +6,8 @@
 //
 // For P <= kDispatchSmallP one workgroup does all of it in LDS
 // (dispatch_small_kernel).  Otherwise the P = T*k assignments are cut into
-// segments of 256 consecutive indices, one wavefront per segment.
+// segments of kDispatchSegment (128) consecutive indices, one wavefront per
+// segment.
 //   1. hist    each wave counts its segment per expert in LDS and writes
 //              cnt[e][u] (expert-major, U = number of segments).
 //   2. scan    one wave per expert: an exclusive scan of cnt[e][0..U) into

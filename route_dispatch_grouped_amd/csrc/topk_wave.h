@@ -87,9 +87,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 // One wavefront selects the top-k of one token's logits row[0..E) (global or
 // LDS memory) and writes ids[0..k), weights[0..k) and, when probs != NULL, the
 // full softmax probs[0..E).  Lane l holds experts l, l+64, ... (VPL >= E/64).
-// k rounds of a wave-wide max over the 64-bit key (order key << 32 | ~id): the
-// larger logit wins, and on equal logits the lower expert id has the larger
-// ~id and wins.  Winner j is kept by lane j % 64 in slot j / 64.  Weights:
+// k rounds; each takes a wave-wide max of the 32-bit order-preserving key of
+// the logits still available, then the lowest expert id holding that key (a
+// ballot per slot, slots scanned in id order): the larger logit wins and, on
+// equal logits, the lower expert id.  Winner j is kept by lane j % 64 in slot
+// j / 64.  Weights:
 // exp(l_j - l_max) over the sum of the selected terms (renormalised) or over
 // all E terms (the plain softmax probability).
 //

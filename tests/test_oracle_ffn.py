@@ -189,6 +189,43 @@ def test_shared_expert_special_cases():
     assert np.allclose(sample, res["out"][[1, 4]], rtol=1e-12, atol=1e-14)
 
 
+def test_shared_gate_sign_and_dot_product():
+    """The shared expert's gate is sigmoid(+x.g): with x.g far above zero the
+    term is the whole shared expert (out = routed + s), far below zero it
+    vanishes (out = routed).  Two tokens are +v and -v and g = 8 sign(v), so
+    x.g = +-8 sum|v| (about +-100): sigmoid(-x.g), a dropped gate, or a dot
+    product with another row fails one of the two.  The gate logits equal the
+    closed form 8 sum|v| exactly and torch's fp64 product on every token; the
+    gate factor on every token equals torch.sigmoid of them."""
+    cfg = workloads.config("qwen15_moe_decode").scaled(num_tokens=6, hidden_size=16, num_experts=6,
+                                                        top_k=2, intermediate_size=8, shared_intermediate_size=12)
+    inp = dict(workloads.generate(cfg, seed=3))
+    v = oracle.widen(inp["x"][0])
+    x = inp["x"].copy()
+    x[1] = x[0] ^ np.uint16(0x8000)  # -v, exactly (bf16 sign bit)
+    inp["x"] = x
+    inp["shared_gate"] = workloads.round_to_bf16_bits((8.0 * np.sign(v)).astype(np.float32))
+    res = oracle.forward(inp, cfg.top_k)
+    X = oracle.widen(x)
+    W = oracle.widen(inp["shared_w13"])
+    Is = cfg.shared_intermediate_size
+    s = (oracle.silu(X @ W[:Is].T) * (X @ W[Is:].T)) @ oracle.widen(inp["shared_w2"]).T
+    routed = _dense_reference({k: oracle.widen(a) if a.dtype == np.uint16 else a for k, a in inp.items()},
+                              res["ids"], res["weights"])
+    gl = res["shared_gate_logit"]
+    assert gl[0] == 8.0 * np.sum(np.abs(v)) and gl[1] == -gl[0] and gl[0] > 60.0
+    assert np.allclose(res["out"][0], routed[0] + s[0], rtol=1e-12, atol=1e-14)
+    assert np.allclose(res["out"][1], routed[1], rtol=1e-12, atol=1e-14)
+    assert not np.allclose(res["out"][1], routed[1] + s[1], rtol=1e-6, atol=1e-9)
+    # every token: the logit is torch's fp64 product, the factor torch.sigmoid
+    Xt = torch.from_numpy(X)
+    gt = torch.from_numpy(oracle.widen(inp["shared_gate"]))
+    assert np.allclose(gl, (Xt @ gt).numpy(), rtol=1e-14, atol=1e-14)
+    sig = torch.sigmoid(torch.from_numpy(gl)).numpy()
+    assert np.allclose(res["out"] - routed, sig[:, None] * s, rtol=1e-10, atol=1e-14)
+    assert np.allclose(res["shared"], sig[:, None] * s, rtol=1e-12, atol=1e-15)
+
+
 def test_empty_experts_are_skipped():
     cfg, inp = tiny(seed=8, num_tokens=6, num_experts=8, top_k=1)
     ids = np.zeros((6, 1), np.int32)  # every token to expert 0
