@@ -175,6 +175,33 @@ moe_status moe_dispatch_plan(const int32_t* topk_ids, const float* topk_weights,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Dispatch plan without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).
+ *
+ * Same arguments, outputs, determinism and errors as moe_dispatch_plan, minus
+ * the workspace: the plan's scratch (per-segment expert counts and bases) is a
+ * fixed device array inside the library, moe_dispatch_noalloc_max_workspace()
+ * bytes (8 MiB) per GPU, held by each GPU the library runs on until the
+ * process ends.  The call allocates and frees nothing.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (different
+ * streams, or different host threads without ordering) race on it and must
+ * not be issued.  Nothing in it needs clearing: each call writes every entry
+ * it later reads.
+ * Errors: as moe_dispatch_plan; UNSUPPORTED when the plan's scratch,
+ * moe_dispatch_workspace_size(T, k, E), exceeds the fixed size (for example
+ * E = 128 allows up to T*k = 2^20 assignments); MOE_ERR_HIP when the array's
+ * device address cannot be looked up.
+ */
+size_t moe_dispatch_noalloc_max_workspace(void);
+moe_status moe_dispatch_plan_noalloc(const int32_t* topk_ids, const float* topk_weights,
+                                     int64_t num_tokens, int64_t top_k, int64_t num_experts,
+                                     int32_t* expert_counts, int32_t* expert_offsets,
+                                     int32_t* token_permutation, int32_t* inverse_permutation,
+                                     int32_t* packed_token_indices, float* packed_routing_weights,
+                                     void* stream);
+
+/*
  * Expert-parallel routing table: the assignments split into this rank's
  * experts and the rest.
  * [metrale_model_layers ep_dispatch.rs: build_ep_routing_table,

@@ -37,6 +37,7 @@ __all__ = [
     "moe_router_topk",
     "moe_router_topk_grouped",
     "moe_dispatch_plan",
+    "moe_dispatch_plan_noalloc",
     "moe_ep_routing_table",
     "moe_ep_rank_counts",
     "moe_grouped_ffn",
@@ -76,6 +77,9 @@ _SIGNATURES = {
     "moe_dispatch_workspace_size": (_size, [_i64, _i64, _i64]),
     "moe_dispatch_plan": (_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "moe_dispatch_noalloc_max_workspace": (_size, []),
+    "moe_dispatch_plan_noalloc": (_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "moe_ep_routing_table_workspace_size": (_size, [_i64, _i64]),
     "moe_ep_routing_table": (_int, [_c_void_p, _i64, _c_void_p, _i64, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p,
                                     _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size,
@@ -283,6 +287,36 @@ def _plan_outputs(P: int, num_experts: int, dev, with_weights: bool) -> Dict[str
     }
     if with_weights:
         out["packed_w"] = torch.empty((P,), dtype=torch.float32, device=dev)
+    return out
+
+
+def moe_dispatch_plan_noalloc(topk_ids: torch.Tensor, topk_weights: Optional[torch.Tensor], num_experts: int,
+                              out: Dict[str, torch.Tensor], stream=None) -> Dict[str, torch.Tensor]:
+    """The dispatch plan into caller-provided outputs, with the library's fixed
+    scratch instead of a workspace (include/moe.h: moe_dispatch_plan_noalloc).
+
+    ``out`` holds int32 ``counts [E]``, ``offsets [E+1]``, ``perm``, ``inv``,
+    ``packed_ids`` ``[P]`` and, with weights, f32 ``packed_w [P]``; nothing is
+    allocated here or in the library.  Calls that overlap in time on one GPU
+    race on the shared scratch.
+    """
+    lib = load_library()
+    T, k = topk_ids.shape
+    P = T * k
+    _need(topk_ids, "topk_ids", (T, k), torch.int32)
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", (T, k), torch.float32)
+        _need(out["packed_w"], "packed_w", (P,), torch.float32)
+    _need(out["counts"], "counts", (num_experts,), torch.int32)
+    _need(out["offsets"], "offsets", (num_experts + 1,), torch.int32)
+    for name in ("perm", "inv", "packed_ids"):
+        _need(out[name], name, (P,), torch.int32)
+    st = lib.moe_dispatch_plan_noalloc(_ptr(topk_ids), _ptr(topk_weights), T, k, int(num_experts),
+                                       _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["perm"]),
+                                       _ptr(out["inv"]), _ptr(out["packed_ids"]),
+                                       _ptr(out.get("packed_w") if topk_weights is not None else None),
+                                       _stream(stream))
+    _check("moe_dispatch_plan_noalloc", st)
     return out
 
 

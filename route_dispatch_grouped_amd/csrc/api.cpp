@@ -462,6 +462,38 @@ moe_status moe_dispatch_plan(const int32_t* topk_ids, const float* topk_weights,
                     "moe_dispatch_plan");
 }
 
+size_t moe_dispatch_noalloc_max_workspace(void) { return moe::kDispatchStaticScratchBytes; }
+
+moe_status moe_dispatch_plan_noalloc(const int32_t* topk_ids, const float* topk_weights, int64_t num_tokens,
+                                     int64_t top_k, int64_t num_experts, int32_t* expert_counts,
+                                     int32_t* expert_offsets, int32_t* token_permutation,
+                                     int32_t* inverse_permutation, int32_t* packed_token_indices,
+                                     float* packed_routing_weights, void* stream) {
+  RETURN_IF_ERR(check_sizes(num_tokens, 1, num_experts, top_k, MOE_DTYPE_F32, false));
+  if (num_tokens == 0) return succeed();
+  REQUIRE_PTR(topk_ids);
+  REQUIRE_PTR(expert_counts);
+  REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(token_permutation);
+  REQUIRE_PTR(inverse_permutation);
+  REQUIRE_PTR(packed_token_indices);
+  if ((topk_weights == nullptr) != (packed_routing_weights == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "topk_weights and packed_routing_weights must be given together");
+  const size_t need = moe_dispatch_workspace_size(num_tokens, top_k, num_experts);
+  if (need > moe::kDispatchStaticScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED, "num_tokens * top_k and num_experts need " + std::to_string(need) +
+                                         " bytes of dispatch scratch, above the fixed " +
+                                         std::to_string(moe::kDispatchStaticScratchBytes));
+  void* scratch = nullptr;
+  hipError_t e = moe::dispatch_static_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "moe_dispatch_plan_noalloc(scratch)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(moe::launch_dispatch(topk_ids, topk_weights, (int)num_tokens, (int)top_k, (int)num_experts,
+                                         expert_counts, expert_offsets, token_permutation, inverse_permutation,
+                                         packed_token_indices, packed_routing_weights, scratch, s),
+                    "moe_dispatch_plan_noalloc");
+}
+
 size_t moe_ep_routing_table_workspace_size(int64_t num_tokens, int64_t top_k) {
   if (num_tokens < 0 || top_k < 1) return 0;
   return align_up(moe::ep_split_scratch_bytes(num_tokens * top_k)) + kAlign;

@@ -21,6 +21,8 @@
 //              count for that expert plus the staged base is the assignment's
 //              position p.  Equal ids therefore keep index order (stability),
 //              and no position depends on the timing of atomics.
+#include <mutex>
+
 #include "moe_internal.h"
 #include "topk_wave.h"
 
@@ -358,6 +360,40 @@ hipError_t launch_topk_dispatch_small(const float* logits, int T, int E, int k, 
                        weights, counts, offsets, perm, inv, packed_ids, zero_ints, n_zero);
   profile_end(s);
   return hipGetLastError();
+}
+
+// Scratch of the dispatch plan for callers that cannot allocate: a fixed
+// device array of kDispatchStaticScratchBytes, one copy per GPU, alive until
+// the process ends.  Host code never passes the array's name to a kernel (on
+// the host it is only a stand-in for the symbol); it passes the device address
+// that hipGetSymbolAddress returns, looked up once per device with that device
+// current.  Every call on a GPU shares that GPU's copy: calls that overlap in
+// time on one GPU race on it.  The plan writes every (expert, segment) count
+// and base it later reads, so nothing in it needs clearing between calls.
+__device__ __align__(256) unsigned char scratch[kDispatchStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t dispatch_static_scratch(void** out) {
+  *out = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 size_t dispatch_scratch_bytes(int64_t P, int64_t E) {

@@ -113,6 +113,12 @@ hipError_t launch_ep_rank_counts(const int32_t* offsets, int E, int G, int32_t* 
 constexpr int kDispatchSegment = 128;  // assignments per wave-segment
 constexpr int kDispatchSmallP = 4096;  // up to this many assignments: one workgroup, all in LDS
 size_t dispatch_scratch_bytes(int64_t P, int64_t E);
+// Size of the library's fixed dispatch scratch (see dispatch_static_scratch).
+constexpr size_t kDispatchStaticScratchBytes = (size_t)8 << 20;
+// Device address of the current device's fixed dispatch scratch of
+// kDispatchStaticScratchBytes (looked up on the device's first call, then
+// kept): the workspace of moe_dispatch_plan_noalloc.
+hipError_t dispatch_static_scratch(void** out);
 // have_hist: the segment histogram is already in the scratch (written by
 // launch_topk_hist), so the histogram launch is skipped.
 hipError_t launch_dispatch(const int32_t* ids, const float* w, int T, int k, int E,
