@@ -21,7 +21,13 @@
 // contiguous tile range [x*per, (x+1)*per) and its 4 MB L2 serves all n-blocks
 // of an m-tile and all m-tiles of an expert close together in time.
 //
-// Tile: BM rows x 256 weight rows (EPI_SWIGLU: 128 gate + the matching 128 up
+// Kernels, by rows per group on average: up to 16 the streaming kernel
+// (decode batches, a pure weight stream), 17-95 the BM-row kernel described
+// next, from 96 the 256-row tiles of the 8-wave pipelined kernel (or of the
+// plain 256-row kernel for K loops the pipelined one does not take); each is
+// described at its definition.
+//
+// BM-row kernel.  Tile: BM rows x 256 weight rows (EPI_SWIGLU: 128 gate + the matching 128 up
 // rows; otherwise 256 output columns), BK = 64 (128 bytes per row); K needs
 // only to be a multiple of 8 (16-byte chunks): chunks past K read zeros.  Both
 // operands stream through an NS-stage LDS ring filled by direct global->LDS
@@ -255,12 +261,12 @@ __device__ __forceinline__ void kloop(f32x4_t (&acc)[BM / 16][NJ], u32x4_t* ring
 
 // Tile schedule shared by every workgroup: s_off <- offsets (E+1), s_tb[g] <-
 // first m-tile of group g (exclusive scan of ceil(rows/BM)), s_tb[G] = total.
-template <int BM>
+template <int BM, int NT = kThreads>
 __device__ __forceinline__ void build_schedule(const GemmArgs& p, int* s_off, int* s_tb, int* s_wsum, int tid,
                                                int lane, int wave) {
   const int G = p.G;
   if (p.offsets) {
-    for (int g = tid; g <= G; g += kThreads) s_off[g] = p.offsets[g];
+    for (int g = tid; g <= G; g += NT) s_off[g] = p.offsets[g];
   } else if (tid == 0) {
     s_off[0] = 0;
     s_off[1] = p.M;
@@ -286,7 +292,7 @@ __device__ __forceinline__ void build_schedule(const GemmArgs& p, int* s_off, in
     if (g1 < G) s_tb[g1] = excl + t0;
     if (tid == 0) {
       int tot = 0;
-      for (int w = 0; w < kThreads / 64; ++w) tot += s_wsum[w];
+      for (int w = 0; w < NT / 64; ++w) tot += s_wsum[w];
       s_tb[G] = tot;
     }
   }
@@ -1253,29 +1259,114 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_big_kernel(GemmArg
 //    issued after the stage it needs (an extra index DMA only makes a wait
 //    stricter).  Counts above 63 are clamped: vmcnt cannot exceed 63, so once
 //    more than 63 operations follow a stage, that stage has retired.
-template <int EPI>
-struct PipeEpi {
-  // EPI_F16S: per row sub-tile and 64-column segment, one exponent and 8 values
-  static constexpr int kStores = (EPI == EPI_SWIGLU) ? 32 : (EPI == EPI_F16S) ? 72 : 64;
-};
-
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_clamped() {
   wait_vmcnt<(N > 63 ? 63 : N)>();
 }
 
-// Next-tile DMA plan from the row indices staged in LDS (gathered rows) or
-// the packed row numbers (contiguous rows).
+struct PipeNext {
+  bool has;
+  int g, m0, rows, n0;
+};
+
+// ---------------------------------------------------------------- 8-wave pipelined kernel
+// Used for large groups (at least 96 rows per group on average: the prefill
+// workloads).  256x256 output tiles (EPI_SWIGLU: 128 h columns, i.e. 128 gate
+// rows and the matching 128 up rows of w13), persistent workgroups of eight
+// waves, two per SIMD: with one wave per SIMD every stall of the single
+// instruction stream (a DMA waiting for room in the texture queues, an LDS
+// read, a barrier) leaves the matrix core idle; with two, the SIMD issues the
+// other wave's MFMAs meanwhile.  MI355X sustains the same MFMA rate with one
+// or two waves per SIMD, and its LDS serves about 200 B/clk to eight waves
+// against about 115 B/clk to four.
+//
+// K loop: 32-wide K stages (A 256 rows and B 256 rows x 64 bytes, 32 KB)
+// through a 4-stage LDS ring filled by direct global->LDS DMA three stages
+// ahead, one barrier per stage.  The ring never drains between tiles: the
+// last four steps of a tile fill it with the workgroup's next tile, whose
+// gathered row indices arrive in LDS by a 4-byte DMA four steps earlier.
+// Rows past a group's end fetch through an out-of-range offset (zeros in LDS,
+// no data moved) and are never stored.  A K loop not a multiple of four
+// stages (PAD) is padded with chunks that read zeros.  Chunk c of row r sits
+// at 16-byte position c ^ ((r >> 2) & 3) of the row's 64 bytes, which the
+// 32x32x16 fragment reads take without bank conflicts.
+//
+// Wave w (SIMD w % 4) has wm = w / 4 and wn = w % 4: it owns row sub-tiles
+// wm, wm + 2, wm + 4, wm + 6 of 32 rows (so both waves of a SIMD lose rows
+// alike in a partly filled tile; sub-tiles wholly past the group's end skip
+// their MFMAs) and weight sub-tiles of 32 rows: for EPI_SWIGLU the gate rows
+// 32 wn .. 32 wn + 31 and the same up rows (h columns 32 wn ..), otherwise
+// output columns 64 wn .. 64 wn + 63 (one 64-column segment of the fp16 +
+// exponent layout).  Accumulators: 4 x 2 32x32 blocks, 128 fp32 per lane.
+// Each stage is 32 DMA instructions, four per wave (two A, two B); the
+// epilogue issues a fixed number of stores per wave, so every vmcnt wait is
+// an exact count of the operations issued after the stage it needs.
+constexpr int kThreads8 = 512;
+
+struct P8 {
+  static constexpr int PER_WAVE = 4;  // DMA instructions per wave per stage
+};
+
+struct Plan8 {
+  uint32_t a_off[2];
+  uint32_t b_off[2];
+};
+
 template <int EPI>
-__device__ __forceinline__ void pipe_plan(BigPlan& d, const GemmArgs& p, const int* s_gidx, int rows, int m0,
-                                          int n0, int wave, int lane, uint32_t row_bytes) {
+struct Pipe8Epi {
+  // 16-byte stores per wave per tile: EPI_SWIGLU 2 per row sub-tile, EPI_F16S
+  // 4 and one exponent, EPI_BF16 4, EPI_F32 8
+  static constexpr int kStores = (EPI == EPI_SWIGLU) ? 8 : (EPI == EPI_F16S) ? 20 : (EPI == EPI_BF16) ? 16 : 32;
+};
+
+// Column groups g (even) and g + 1 of a row, each four 16-bit values (two
+// dwords) held by lanes l (columns 8g + 0..3, 8(g+1) + 0..3) and l ^ 32
+// (columns 8g + 4..7, 8(g+1) + 4..7): one swap of the upper half of the first
+// with the lower half of the second (v_permlane32_swap) leaves lane l < 32
+// with the 8 columns of group g and lane l + 32 with those of group g + 1, in
+// column order, as one 16-byte store each.
+__device__ __forceinline__ u32x4_t pair_columns(uint32_t g_lo, uint32_t g_hi, uint32_t h_lo, uint32_t h_hi) {
+  const auto x = __builtin_amdgcn_permlane32_swap(g_lo, h_lo, false, false);
+  const auto y = __builtin_amdgcn_permlane32_swap(g_hi, h_hi, false, false);
+  return u32x4_t{(uint32_t)x[0], (uint32_t)y[0], (uint32_t)x[1], (uint32_t)y[1]};
+}
+
+__device__ __forceinline__ void p8_issue(u32x4_t* buf, const Plan8& d, u32x4_t ra, u32x4_t rb, int wave,
+                                         int kbytes) {
 #pragma unroll
-  for (int qi = 0; qi < 4; ++qi) {
-    const int q = qi * 4 + wave;
+  for (int qi = 0; qi < 2; ++qi) dma16(buf + (qi * 8 + wave) * 64, ra, d.a_off[qi], kbytes);
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) dma16(buf + Big::A_SLOTS + (qi * 8 + wave) * 64, rb, d.b_off[qi], kbytes);
+}
+
+// As stage_plan: chunks at or past the end of a row read zeros (padded K loops).
+__device__ __forceinline__ Plan8 p8_stage_plan(const Plan8& d, uint32_t cb, int kbytes, uint32_t row_bytes) {
+  Plan8 m;
+  const bool dead = cb + (uint32_t)kbytes >= row_bytes;
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    m.a_off[qi] = dead ? 0x80000000u : d.a_off[qi];
+    m.b_off[qi] = dead ? 0x80000000u : d.b_off[qi];
+  }
+  return m;
+}
+
+// DMA plan of a tile: instruction q = 8 qi + wave covers tile rows 16 q ..
+// 16 q + 15; lane l fetches chunk (l & 3) ^ swz of row 16 q + (l >> 2).  A rows
+// past the tile's rows fetch through an out-of-range offset (zeros, no data
+// moved); weight rows past N are clamped to the last one (never stored).
+// Gathered row indices come from `gidx` (LDS, the next tile) or from global
+// memory (`from_global`, the first tile).
+template <int EPI>
+__device__ __forceinline__ void p8_plan(Plan8& d, const GemmArgs& p, const int* gidx, bool from_global, int rows,
+                                        int m0, int n0, int wave, int lane, uint32_t row_bytes) {
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    const int q = qi * 8 + wave;
     const int r = q * 16 + (lane >> 2);
     const int c = (lane & 3) ^ big_swz(r);
     if (r < rows) {
-      const int grow = p.gather ? s_gidx[r] : (m0 + r);
+      const int grow = p.gather ? (from_global ? p.gather[m0 + r] : gidx[r]) : (m0 + r);
       d.a_off[qi] = (uint32_t)grow * row_bytes + (uint32_t)c * 16u;
     } else {
       d.a_off[qi] = 0x80000000u;
@@ -1291,54 +1382,113 @@ __device__ __forceinline__ void pipe_plan(BigPlan& d, const GemmArgs& p, const i
   }
 }
 
-struct PipeNext {
-  bool has;
-  int g, m0, rows, n0;
+struct Frags8 {
+  bf16x8_t a[2][4];
+  bf16x8_t b[2][2];
 };
+
+// Slot offset of weight sub-tile j from the wave's first weight row.
+template <int EPI>
+__device__ __forceinline__ constexpr int p8_b_off(int j) {
+  return (EPI == EPI_SWIGLU) ? 512 * j : 128 * j;
+}
+
+template <int EPI, int LIVE>
+__device__ __forceinline__ void p8_read(Frags8& f, const u32x4_t* __restrict__ buf, const int (&a_slot)[2],
+                                        const int (&b_slot)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) f.b[h][j] = __builtin_bit_cast(bf16x8_t, buf[b_slot[h] + p8_b_off<EPI>(j)]);
+#pragma unroll
+    for (int i = 0; i < LIVE; ++i) f.a[h][i] = __builtin_bit_cast(bf16x8_t, buf[a_slot[h] + 256 * i]);
+  }
+}
+
+// One K step of a wave with LIVE >= 1 live row sub-tiles: 4 LIVE MFMAs in
+// 2 LIVE groups of two (k16 half h, row sub-tile i), the wave's 4 DMA
+// instructions of stage kt+4 spread over the groups.  One register set of
+// fragments: once the last MFMA of half h has issued, half h's fragments of
+// the next stage are read into the same registers (the other wave of the SIMD
+// keeps the matrix core busy while they arrive).
+template <int EPI, int LIVE>
+__device__ __forceinline__ void p8_step(f32x16_t (&acc)[4][2], Frags8& f, u32x4_t* refill,
+                                        const u32x4_t* __restrict__ next_buf, bool dma, int kbytes, const Plan8& d,
+                                        u32x4_t ra, u32x4_t rb, int wave, const int (&a_slot)[2],
+                                        const int (&b_slot)[2]) {
+  static_assert(LIVE >= 1 && LIVE <= 4, "live row sub-tiles");
+  constexpr int NG = 2 * LIVE;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int h = g / LIVE, i = g % LIVE;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[h][j], f.a[h][i], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (dma) {
+#pragma unroll
+      for (int q = (g * 4) / NG; q < ((g + 1) * 4) / NG; ++q) {
+        if (q < 2) dma16(refill + (q * 8 + wave) * 64, ra, d.a_off[q], kbytes);
+        else dma16(refill + Big::A_SLOTS + ((q - 2) * 8 + wave) * 64, rb, d.b_off[q - 2], kbytes);
+      }
+    }
+    if (i == LIVE - 1) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        f.b[h][jj] = __builtin_bit_cast(bf16x8_t, next_buf[b_slot[h] + p8_b_off<EPI>(jj)]);
+#pragma unroll
+      for (int ii = 0; ii < LIVE; ++ii)
+        f.a[h][ii] = __builtin_bit_cast(bf16x8_t, next_buf[a_slot[h] + 256 * ii]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
 
 // One tile's K loop.  On entry stages 0..3 of this tile are in flight (or
 // landed); `after_epi` says whether the previous tile's epilogue stores were
-// issued after them.  With nx.has, the loop stages the next tile's row
-// indices, builds its plan into `dn` and issues its stages 0..3.  PAD: the
-// K loop is padded to whole groups of 4 stages.
+// issued after them.  Step kt waits for this wave's DMA of stage kt+1, meets
+// the other waves at the barrier (which publishes the stage and proves that
+// every wave has read stage kt's buffer), refills that buffer with stage
+// kt+4 and computes stage kt.  With nx.has the last four steps issue the next
+// tile's stages 0..3 instead, from the plan built at step KT-4 out of the row
+// indices that waves 0..3 (64 rows each) staged into s_gidx at step KT-8.
 template <int EPI, int LIVE, bool PAD>
-__device__ __forceinline__ void pipe_kloop(f32x16_t (&acc)[4][4], u32x4_t* s0, u32x4_t* s1, u32x4_t* s2,
-                                           u32x4_t* s3, int* s_gidx, const GemmArgs& p, const BigPlan& d,
-                                           u32x4_t ra, u32x4_t rb, BigPlan& dn, u32x4_t rbn, const PipeNext& nx,
-                                           bool after_epi, int wave, int lane, int KT, uint32_t row_bytes,
-                                           const int (&a_slot)[2], const int (&b_slot)[2]) {
-  constexpr int S = PipeEpi<EPI>::kStores;
+__device__ __forceinline__ void pipe8_kloop(f32x16_t (&acc)[4][2], u32x4_t* s0, u32x4_t* s1, u32x4_t* s2,
+                                            u32x4_t* s3, int* s_gidx, const GemmArgs& p, const Plan8& d,
+                                            u32x4_t ra, u32x4_t rb, Plan8& dn, u32x4_t rbn, const PipeNext& nx,
+                                            bool after_epi, int wave, int lane, int KT, uint32_t row_bytes,
+                                            const int (&a_slot)[2], const int (&b_slot)[2]) {
+  constexpr int S = Pipe8Epi<EPI>::kStores;
+  constexpr int PW = P8::PER_WAVE;
   u32x4_t* bufs[4] = {s0, s1, s2, s3};
-  if (after_epi) wait_vmcnt_clamped<3 * Big::PER_WAVE + S>();
-  else wait_vmcnt<3 * Big::PER_WAVE>();
+  if (after_epi) wait_vmcnt_clamped<3 * PW + S>();
+  else wait_vmcnt<3 * PW>();
   lds_barrier();
-  BigFrags fx, fy;
-  big_read<EPI, LIVE>(fx, s0, a_slot, b_slot);
+  Frags8 f;
+  if constexpr (LIVE > 0) p8_read<EPI, LIVE>(f, s0, a_slot, b_slot);
   for (int kt0 = 0; kt0 < KT; kt0 += 4) {
     const bool last = kt0 + 4 == KT;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int kt = kt0 + u;
-      BigFrags& cur = (u & 1) ? fy : fx;
-      BigFrags& nxt = (u & 1) ? fx : fy;
-      // wait for stage kt+1 (the next tile's stage 0 at the last step)
+#define MOE_P8_STEP(PL) \
+  p8_step<EPI, LIVE>(acc, f, bufs[u], bufs[(u + 1) & 3], dma, kbytes, PL, ra, rbs, wave, a_slot, b_slot)
       if (last && !nx.has) {
-        if (u == 0) wait_vmcnt<2 * Big::PER_WAVE>();
-        else if (u == 1) wait_vmcnt<Big::PER_WAVE>();
+        if (u == 0) wait_vmcnt<2 * PW>();
+        else if (u == 1) wait_vmcnt<PW>();
         else wait_vmcnt<0>();
       } else if (kt0 == 0 && u < 3 && after_epi) {
-        wait_vmcnt_clamped<2 * Big::PER_WAVE + S>();
+        wait_vmcnt_clamped<2 * PW + S>();
       } else {
-        wait_vmcnt<2 * Big::PER_WAVE>();
+        wait_vmcnt<2 * PW>();
       }
       lds_barrier();
-      if (u == 0 && kt0 + 8 == KT && nx.has && p.gather) {
-        // next tile's row indices -> s_gidx (row 64*wave + lane)
+      if (u == 0 && kt0 + 8 == KT && nx.has && p.gather && wave < 4) {
         const int r = 64 * wave + lane;
         const uint32_t voff = (r < nx.rows) ? (uint32_t)(nx.m0 + r) * 4u : 0x80000000u;
         dma4(s_gidx + 64 * wave, make_rsrc(p.gather, (uint32_t)p.M * 4u), voff, 0);
       }
-      if (u == 0 && last && nx.has) pipe_plan<EPI>(dn, p, s_gidx, nx.rows, nx.m0, nx.n0, wave, lane, row_bytes);
+      if (u == 0 && last && nx.has) p8_plan<EPI>(dn, p, s_gidx, false, nx.rows, nx.m0, nx.n0, wave, lane, row_bytes);
       bool dma;
       int kbytes;
       if (!last) {
@@ -1348,30 +1498,142 @@ __device__ __forceinline__ void pipe_kloop(f32x16_t (&acc)[4][4], u32x4_t* s0, u
         dma = nx.has;
         kbytes = u * Big::KB * 2;
       }
-      const BigPlan& dd = last ? dn : d;
+      Plan8 dd;
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi) {
+        dd.a_off[qi] = last ? dn.a_off[qi] : d.a_off[qi];
+        dd.b_off[qi] = last ? dn.b_off[qi] : d.b_off[qi];
+      }
       const u32x4_t rbs = last ? rbn : rb;
       if constexpr (PAD) {
-        const BigPlan dk = stage_plan(dd, big_chunk_bytes(lane), kbytes, row_bytes);
+        const Plan8 dk = p8_stage_plan(dd, big_chunk_bytes(lane), kbytes, row_bytes);
         if constexpr (LIVE >= 1) {
-          big_step<EPI, LIVE>(acc, cur, nxt, bufs[u], bufs[(u + 1) & 3], dma, kbytes, dk, ra, rbs, wave, a_slot,
-                              b_slot);
+          MOE_P8_STEP(dk);
         } else {
-          if (dma) big_issue(bufs[u], dk, ra, rbs, wave, kbytes);
+          if (dma) p8_issue(bufs[u], dk, ra, rbs, wave, kbytes);
         }
       } else {
         if constexpr (LIVE >= 1) {
-          big_step<EPI, LIVE>(acc, cur, nxt, bufs[u], bufs[(u + 1) & 3], dma, kbytes, dd, ra, rbs, wave, a_slot,
-                              b_slot);
+          MOE_P8_STEP(dd);
         } else {
-          if (dma) big_issue(bufs[u], dd, ra, rbs, wave, kbytes);
+          if (dma) p8_issue(bufs[u], dd, ra, rbs, wave, kbytes);
         }
       }
     }
   }
 }
 
+// Epilogue of the 8-wave kernels: exactly Pipe8Epi<EPI>::kStores buffer
+// stores per wave (rows past the tile and columns past N go to an offset past
+// the buffer, which stores nothing), so that the K loops' vmcnt waits stay
+// exact counts.
+// Epilogue of the 8-wave kernel: exactly Pipe8Epi<EPI>::kStores buffer
+// stores per wave, 16 bytes per lane (rows past the tile and columns past N go
+// to an offset past the buffer, which stores nothing), so that the K loop's
+// vmcnt waits stay exact counts.  Lane l (row 32 (2i + wm) + (l & 31)) holds
+// columns 8g + 4 (l >> 5) + 0..3 of each 32-column block; pair_columns gives
+// each lane 8 consecutive columns of its row.
+template <int EPI>
+__device__ __forceinline__ void p8_epilogue(const f32x16_t (&acc)[4][2], const GemmArgs& p,
+                                            __amdgpu_buffer_rsrc_t ro, int rows, int m0, int n0, int wm, int wn,
+                                            int lane) {
+  const int rin = lane & 31;
+  const int hi = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 32 * (2 * i + wm) + rin;
+    const bool row_ok = row < rows;
+    if (EPI == EPI_SWIGLU) {
+      uint32_t hb[4][2];
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          hb[gq][c] = (uint32_t)f32_to_bf16_rne(silu_mul(acc[i][0][4 * gq + 2 * c], acc[i][1][4 * gq + 2 * c])) |
+                      ((uint32_t)f32_to_bf16_rne(silu_mul(acc[i][0][4 * gq + 2 * c + 1],
+                                                          acc[i][1][4 * gq + 2 * c + 1])) << 16);
+#pragma unroll
+      for (int gp = 0; gp < 4; gp += 2) {
+        const u32x4_t v = pair_columns(hb[gp][0], hb[gp][1], hb[gp + 1][0], hb[gp + 1][1]);
+        const int col = n0 + 32 * wn + 8 * (gp + hi);
+        const uint32_t off =
+            (row_ok && col < p.N) ? (uint32_t)(((int64_t)(m0 + row) * p.ldo + col) * 2) : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, (int)off, 0, 0);
+      }
+    } else if (EPI == EPI_F16S) {
+      // this wave's 64 columns are one segment: this lane's 32 values and
+      // the 32 of lane ^ 32, which holds the same row
+      const int nseg = (int)(p.ldo / kF16SegCols);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          p.scale_out, (short)0, (int)((size_t)p.M * nseg * 4), kBufferWord3);
+      float m = 0.f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(acc[i][j][e]));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      const int kx = f16s_exponent(m);
+      const int seg_col = n0 + 64 * wn;
+      const uint32_t soff = (row_ok && seg_col < p.N && lane < 32)
+                                ? (uint32_t)(((int64_t)(m0 + row) * nseg + seg_col / kF16SegCols) * 4)
+                                : 0x80000000u;
+      __builtin_amdgcn_raw_buffer_store_b32((uint32_t)kx, rs, (int)soff, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        uint32_t hv[4][2];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            hv[gq][c] = pack_f16x2(ldexpf(acc[i][j][4 * gq + 2 * c], kx), ldexpf(acc[i][j][4 * gq + 2 * c + 1], kx));
+#pragma unroll
+        for (int gp = 0; gp < 4; gp += 2) {
+          const u32x4_t v = pair_columns(hv[gp][0], hv[gp][1], hv[gp + 1][0], hv[gp + 1][1]);
+          const int col = seg_col + 32 * j + 8 * (gp + hi);
+          const uint32_t off =
+              (row_ok && col < p.N) ? (uint32_t)(((int64_t)(m0 + row) * p.ldo + col) * 2) : 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b128(v, ro, (int)off, 0, 0);
+        }
+      }
+    } else if (EPI == EPI_BF16) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        uint32_t hv[4][2];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) hv[gq][c] = pack_bf16x2(acc[i][j][4 * gq + 2 * c], acc[i][j][4 * gq + 2 * c + 1]);
+#pragma unroll
+        for (int gp = 0; gp < 4; gp += 2) {
+          const u32x4_t v = pair_columns(hv[gp][0], hv[gp][1], hv[gp + 1][0], hv[gp + 1][1]);
+          const int col = n0 + 64 * wn + 32 * j + 8 * (gp + hi);
+          const uint32_t off =
+              (row_ok && col < p.N) ? (uint32_t)(((int64_t)(m0 + row) * p.ldo + col) * 2) : 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b128(v, ro, (int)off, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int col = n0 + 64 * wn + 32 * j + 8 * gq + 4 * hi;
+          typedef float f32x4b_t __attribute__((ext_vector_type(4)));
+          const f32x4b_t v = {acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
+                              acc[i][j][4 * gq + 3]};
+          const uint32_t off =
+              (row_ok && col < p.N) ? (uint32_t)(((int64_t)(m0 + row) * p.ldo + col) * 4) : 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), ro, (int)off, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+#undef MOE_P8_STEP
+
 template <int EPI, bool PAD>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kThreads8) void grouped_gemm_bf16_pipe8_kernel(GemmArgs p) {
   constexpr int BM = Big::BM;
   constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
 
@@ -1381,15 +1643,15 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
   __shared__ u32x4_t st3[Big::SLOTS];
   __shared__ int s_off[kMaxGroups + 1];
   __shared__ int s_tb[kMaxGroups + 1];
-  __shared__ int s_wsum[kThreads / 64];
+  __shared__ int s_wsum[kThreads8 / 64];
   __shared__ int s_gidx[BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int G = p.G;
-  build_schedule<BM>(p, s_off, s_tb, s_wsum, tid, lane, wave);
+  build_schedule<BM, kThreads8>(p, s_off, s_tb, s_wsum, tid, lane, wave);
 
   const int total_m = s_tb[G];
   const int nblk = (p.N + BN_OUT - 1) / BN_OUT;
@@ -1400,8 +1662,6 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
   const int per = (total + kXcds - 1) / kXcds;
   const int t_begin = xcd * per;
   const int t_end = min(total, t_begin + per);
-  // whole groups of 4 stages (PAD: chunks past K read zeros; otherwise K is a
-  // multiple of 4 stages already)
   const int KT = PAD ? ((p.K + Big::KB - 1) / Big::KB + 3) & ~3 : p.K / Big::KB;
   const uint32_t row_bytes = (uint32_t)p.K * 2u;
   int t = t_begin + slot;
@@ -1413,7 +1673,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
   for (int h = 0; h < 2; ++h) {
     const int pos = (2 * h + (lane >> 5)) ^ big_swz(rin);
     a_slot[h] = (32 * wm + rin) * 4 + pos;
-    b_slot[h] = Big::A_SLOTS + (((EPI == EPI_SWIGLU) ? 64 : 128) * wn + rin) * 4 + pos;
+    b_slot[h] = Big::A_SLOTS + (((EPI == EPI_SWIGLU) ? 32 : 64) * wn + rin) * 4 + pos;
   }
   const u32x4_t ra = make_rsrc(p.A, (uint32_t)p.a_rows * row_bytes);
   const int b_rows_total = (EPI == EPI_SWIGLU) ? 2 * p.up_row0 : p.N;
@@ -1422,49 +1682,26 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
   const __amdgpu_buffer_rsrc_t ro =
       __builtin_amdgcn_make_buffer_rsrc(p.out, (short)0, (int)((size_t)p.M * p.ldo * out_elt), kBufferWord3);
 
-  // first tile: plan from global row indices (nothing is in flight yet)
   TileCoord tc = tile_coord<BM>(t, nblk, G, s_tb, s_off);
-  BigPlan d;
-  {
-    const int n0 = tc.nb * BN_OUT;
-#pragma unroll
-    for (int qi = 0; qi < 4; ++qi) {
-      const int q = qi * 4 + wave;
-      const int r = q * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ big_swz(r);
-      if (r < tc.rows) {
-        const int grow = p.gather ? p.gather[tc.m0 + r] : (tc.m0 + r);
-        d.a_off[qi] = (uint32_t)grow * row_bytes + (uint32_t)c * 16u;
-      } else {
-        d.a_off[qi] = 0x80000000u;
-      }
-      int wr;
-      if (EPI == EPI_SWIGLU) {
-        const int col = min(n0 + (r & 127), p.N - 1);
-        wr = (r < 128) ? col : p.up_row0 + col;
-      } else {
-        wr = min(n0 + r, p.N - 1);
-      }
-      d.b_off[qi] = (uint32_t)wr * row_bytes + (uint32_t)c * 16u;
-    }
-  }
+  Plan8 d;
+  p8_plan<EPI>(d, p, nullptr, true, tc.rows, tc.m0, tc.nb * BN_OUT, wave, lane, row_bytes);
   u32x4_t rb = make_rsrc(p.B + (int64_t)tc.g * p.b_group_stride, b_bytes);
   if constexpr (PAD) {
     const uint32_t cb = big_chunk_bytes(lane);
-    big_issue(st0, stage_plan(d, cb, 0, row_bytes), ra, rb, wave, 0);
-    big_issue(st1, stage_plan(d, cb, 1 * Big::KB * 2, row_bytes), ra, rb, wave, 1 * Big::KB * 2);
-    big_issue(st2, stage_plan(d, cb, 2 * Big::KB * 2, row_bytes), ra, rb, wave, 2 * Big::KB * 2);
-    big_issue(st3, stage_plan(d, cb, 3 * Big::KB * 2, row_bytes), ra, rb, wave, 3 * Big::KB * 2);
+    p8_issue(st0, p8_stage_plan(d, cb, 0, row_bytes), ra, rb, wave, 0);
+    p8_issue(st1, p8_stage_plan(d, cb, 1 * Big::KB * 2, row_bytes), ra, rb, wave, 1 * Big::KB * 2);
+    p8_issue(st2, p8_stage_plan(d, cb, 2 * Big::KB * 2, row_bytes), ra, rb, wave, 2 * Big::KB * 2);
+    p8_issue(st3, p8_stage_plan(d, cb, 3 * Big::KB * 2, row_bytes), ra, rb, wave, 3 * Big::KB * 2);
   } else {
-    big_issue(st0, d, ra, rb, wave, 0);
-    big_issue(st1, d, ra, rb, wave, 1 * Big::KB * 2);
-    big_issue(st2, d, ra, rb, wave, 2 * Big::KB * 2);
-    big_issue(st3, d, ra, rb, wave, 3 * Big::KB * 2);
+    p8_issue(st0, d, ra, rb, wave, 0);
+    p8_issue(st1, d, ra, rb, wave, 1 * Big::KB * 2);
+    p8_issue(st2, d, ra, rb, wave, 2 * Big::KB * 2);
+    p8_issue(st3, d, ra, rb, wave, 3 * Big::KB * 2);
   }
 
   bool after_epi = false;
   while (true) {
-    const int g = tc.g, m0 = tc.m0, rows = tc.rows, n0 = tc.nb * BN_OUT;
+    const int m0 = tc.m0, rows = tc.rows, n0 = tc.nb * BN_OUT;
     PipeNext nx;
     const int tn = t + nslots;
     nx.has = tn < t_end;
@@ -1475,120 +1712,29 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_pipe_kernel(GemmAr
     nx.rows = tcn.rows;
     nx.n0 = tcn.nb * BN_OUT;
     const u32x4_t rbn = make_rsrc(p.B + (int64_t)tcn.g * p.b_group_stride, b_bytes);
-    BigPlan dn = d;
+    Plan8 dn = d;
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
     const int units = (rows + 31) >> 5;
     const int live = __builtin_amdgcn_readfirstlane(min(4, (units - wm + 1) >> 1));
     switch (live) {
-#define MOE_PIPE_CASE(n)                                                                                        \
-  case n:                                                                                                       \
-    pipe_kloop<EPI, n, PAD>(acc, st0, st1, st2, st3, s_gidx, p, d, ra, rb, dn, rbn, nx, after_epi, wave, lane, \
-                            KT, row_bytes, a_slot, b_slot);                                                     \
+#define MOE_PIPE8_CASE(n)                                                                                        \
+  case n:                                                                                                        \
+    pipe8_kloop<EPI, n, PAD>(acc, st0, st1, st2, st3, s_gidx, p, d, ra, rb, dn, rbn, nx, after_epi, wave, lane, \
+                             KT, row_bytes, a_slot, b_slot);                                                     \
     break;
-      MOE_PIPE_CASE(0) MOE_PIPE_CASE(1) MOE_PIPE_CASE(2) MOE_PIPE_CASE(3) MOE_PIPE_CASE(4)
-#undef MOE_PIPE_CASE
+      MOE_PIPE8_CASE(0) MOE_PIPE8_CASE(1) MOE_PIPE8_CASE(2) MOE_PIPE8_CASE(3) MOE_PIPE8_CASE(4)
+#undef MOE_PIPE8_CASE
       default: break;
     }
 
-    // ---- epilogue: exactly PipeEpi<EPI>::kStores buffer stores per wave
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 32 * (2 * i + wm) + rin;
-      const bool row_ok = row < rows;
-      if (EPI == EPI_SWIGLU) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int col = n0 + 64 * wn + 32 * j + 8 * gq + 4 * (lane >> 5);
-            uint32_t hb[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const float gv = acc[i][j][4 * gq + c];
-              const float uv = acc[i][j + 2][4 * gq + c];
-              hb[c] = f32_to_bf16_rne(silu_mul(gv, uv));
-            }
-            typedef int i32x2_t __attribute__((ext_vector_type(2)));
-            const i32x2_t v = {(int)(hb[0] | (hb[1] << 16)), (int)(hb[2] | (hb[3] << 16))};
-            const uint32_t off = (row_ok && col < p.N) ? (uint32_t)(((int64_t)(m0 + row) * p.ldo + col) * 2)
-                                                       : 0x80000000u;
-            __builtin_amdgcn_raw_buffer_store_b64(v, ro, (int)off, 0, 0);
-          }
-        }
-      } else if (EPI == EPI_F16S) {
-        // two 64-column segments per wave row: j = 2s, 2s + 1 (this lane's 32
-        // values and the 32 of lane ^ 32, which holds the same row)
-        const int nseg = (int)(p.ldo / kF16SegCols);
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            p.scale_out, (short)0, (int)((size_t)p.M * nseg * 4), kBufferWord3);
-#pragma unroll
-        for (int sg = 0; sg < 2; ++sg) {
-          float m = 0.f;
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(acc[i][2 * sg + jj][e]));
-          m = fmaxf(m, __shfl_xor(m, 32, 64));
-          const int kx = f16s_exponent(m);
-          const int seg_col = n0 + 128 * wn + 64 * sg;
-          const uint32_t soff = (row_ok && seg_col < p.N && lane < 32)
-                                    ? (uint32_t)(((int64_t)(m0 + row) * nseg + seg_col / kF16SegCols) * 4)
-                                    : 0x80000000u;
-          __builtin_amdgcn_raw_buffer_store_b32((uint32_t)kx, rs, (int)soff, 0, 0);
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int j = 2 * sg + jj;
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-              const int col = n0 + 128 * wn + 32 * j + 8 * gq + 4 * (lane >> 5);
-              typedef int i32x2_t __attribute__((ext_vector_type(2)));
-              const i32x2_t v = {(int)pack_f16x2(ldexpf(acc[i][j][4 * gq], kx), ldexpf(acc[i][j][4 * gq + 1], kx)),
-                                 (int)pack_f16x2(ldexpf(acc[i][j][4 * gq + 2], kx),
-                                                 ldexpf(acc[i][j][4 * gq + 3], kx))};
-              const uint32_t off = (row_ok && col < p.N) ? (uint32_t)(((int64_t)(m0 + row) * p.ldo + col) * 2)
-                                                         : 0x80000000u;
-              __builtin_amdgcn_raw_buffer_store_b64(v, ro, (int)off, 0, 0);
-            }
-          }
-        }
-      } else if (EPI == EPI_BF16) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int col = n0 + 128 * wn + 32 * j + 8 * gq + 4 * (lane >> 5);
-            typedef int i32x2_t __attribute__((ext_vector_type(2)));
-            const i32x2_t v = {(int)pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]),
-                               (int)pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3])};
-            const uint32_t off = (row_ok && col < p.N) ? (uint32_t)(((int64_t)(m0 + row) * p.ldo + col) * 2)
-                                                       : 0x80000000u;
-            __builtin_amdgcn_raw_buffer_store_b64(v, ro, (int)off, 0, 0);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int col = n0 + 128 * wn + 32 * j + 8 * gq + 4 * (lane >> 5);
-            typedef float f32x4b_t __attribute__((ext_vector_type(4)));
-            const f32x4b_t v = {acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
-                                acc[i][j][4 * gq + 3]};
-            const uint32_t off = (row_ok && col < p.N) ? (uint32_t)(((int64_t)(m0 + row) * p.ldo + col) * 4)
-                                                       : 0x80000000u;
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), ro, (int)off, 0, 0);
-          }
-        }
-      }
-    }
+    p8_epilogue<EPI>(acc, p, ro, rows, m0, n0, wm, wn, lane);
     if (!nx.has) break;
-    (void)g;
     t = tn;
     tc = tcn;
     d = dn;
@@ -1829,9 +1975,9 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t s, const char* name) {
   if (grid < kXcds) grid = kXcds;
   profile_begin(name, s);
   if (a.K % (4 * Big::KB) != 0)
-    hipLaunchKernelGGL((grouped_gemm_bf16_pipe_kernel<EPI, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16_pipe8_kernel<EPI, true>), dim3((unsigned)grid), dim3(kThreads8), 0, s, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_bf16_pipe_kernel<EPI, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16_pipe8_kernel<EPI, false>), dim3((unsigned)grid), dim3(kThreads8), 0, s, a);
   profile_end(s);
   return hipGetLastError();
 }
