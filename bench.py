@@ -103,6 +103,9 @@ KERNEL_SOURCES = {
     "ffn_gate_up_bf16": "route_dispatch_grouped_amd/csrc/grouped_gemm_bf16.hip",
     "ffn_down_bf16": "route_dispatch_grouped_amd/csrc/grouped_gemm_bf16.hip",
     "combine": "route_dispatch_grouped_amd/csrc/combine.hip",
+    "router_topk_hist": "route_dispatch_grouped_amd/csrc/dispatch.hip",
+    "dispatch_scan": "route_dispatch_grouped_amd/csrc/dispatch.hip",
+    "dispatch_scatter": "route_dispatch_grouped_amd/csrc/dispatch.hip",
 }
 
 
@@ -537,6 +540,12 @@ def main():
         per_kernel[n] = {"avg_us": round(avg_s * 1e6, 2), "launches_per_step": c // max(args.steps, 1),
                          "bound": ent["bound"], "achieved": ent["achieved"], "unit": ent["unit"],
                          "frac": ent["frac"]}
+        tr = measured_traffic(n, cfg.name)
+        if tr is not None:
+            # HBM bytes from the committed FETCH_SIZE/WRITE_SIZE summary over this run's duration
+            per_kernel[n]["hbm_traffic_bytes"] = round(tr)
+            per_kernel[n]["hbm_gbs_counters"] = round(tr / avg_s / 1e9, 1)
+            per_kernel[n]["hbm_frac_counters"] = round(tr / avg_s / 1e9 / PEAK_HBM_GBS, 4)
         if dominant is None or ms > kernels[dominant][0]:
             dominant = n
     if dominant is not None:
