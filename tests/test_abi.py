@@ -27,6 +27,11 @@ def header_functions():
 
 @pytest.fixture(scope="module")
 def lib():
+    # MOE_ABI_LIB: run these checks against another build of the library (the
+    # host-sanitized one, see test_abi_sanitized.py)
+    path = os.environ.get("MOE_ABI_LIB")
+    if path:
+        return rdg.load_library(path)
     from conftest import ensure_library
     return ensure_library()
 
