@@ -10,22 +10,36 @@
 namespace moe {
 namespace {
 
-// One thread per (token, column); column E is the shared expert's gate vector.
+// fp32 router logits (+ the shared-expert gate logit as row E): one wave per
+// (token, router row).  Each lane multiplies 4 consecutive hidden elements per
+// pass (16-byte loads, H % 4 == 0) and the wave sums its 64 partial dot
+// products.
 __global__ __launch_bounds__(256) void router_logits_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
     const float* __restrict__ gate, int T, int H, int E, float* __restrict__ logits,
     float* __restrict__ gate_logit) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
   const int C = E + (gate != nullptr ? 1 : 0);
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)T * C) return;
-  const int t = (int)(idx / C);
-  const int c = (int)(idx - (int64_t)t * C);
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= (int64_t)T * C) return;
+  const int t = (int)(item / C);
+  const int c = (int)(item - (int64_t)t * C);
   const float* xr = x + (int64_t)t * H;
   const float* w = (c < E) ? wr + (int64_t)c * H : gate;
   float acc = 0.f;
-  for (int h = 0; h < H; ++h) acc = fmaf(xr[h], w[h], acc);
-  if (c < E) logits[(int64_t)t * E + c] = acc + (bias ? bias[c] : 0.f);
-  else gate_logit[t] = acc;
+  for (int h = 4 * lane; h < H; h += 256) {
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(xr + h);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(w + h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = fmaf(a[i], b[i], acc);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, 64);
+  if (lane == 0) {
+    if (c < E) logits[(int64_t)t * E + c] = acc + (bias ? bias[c] : 0.f);
+    else gate_logit[t] = acc;
+  }
 }
 
 // One wavefront per token (topk_row).
@@ -123,7 +137,7 @@ hipError_t launch_router_logits_f32(const float* x, const float* wr, const float
                                     int T, int H, int E, float* logits, float* gate_logit, hipStream_t s) {
   const int64_t n = (int64_t)T * (E + (gate ? 1 : 0));
   if (n == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((n + 255) / 256);
+  const unsigned blocks = (unsigned)((n + 3) / 4);  // four waves per workgroup, one per (token, row)
   profile_begin("router_logits_f32", s);
   hipLaunchKernelGGL(router_logits_f32_kernel, dim3(blocks), dim3(256), 0, s, x, wr, bias, gate, T, H, E,
                      logits, gate_logit);
