@@ -36,10 +36,9 @@
  *  - Device-side preconditions that the host cannot see (expert ids in
  *    [0, E), offsets consistent with P) are the caller's contract; the plan
  *    produced by moe_dispatch_plan always satisfies them.
- *  - Limits: 1 <= E <= 512, 1 <= k <= E, T*k < 2^31.  bf16: H a multiple of
- *    64, I (and the shared expert's I) a multiple of 16, which admits the
- *    expert widths of 8-way tensor-parallel slices (768 / 8 = 96,
- *    1408 / 8 = 176).  f32: H multiple of 8, I multiple of 16.
+ *  - Limits: 1 <= E <= 512, 1 <= k <= E, T*k < 2^31, H a multiple of 8.
+ *    I (and the shared expert's I) a multiple of 16, which admits the expert
+ *    widths of 8-way tensor-parallel slices (768 / 8 = 96, 1408 / 8 = 176).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

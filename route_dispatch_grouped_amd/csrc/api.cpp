@@ -55,8 +55,7 @@ moe_status check_sizes(int64_t T, int64_t H, int64_t E, int64_t k, int dtype, bo
   if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16) return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
   if (need_h) {
     if (H < 1) return fail(MOE_ERR_INVALID_ARG, "hidden_size must be >= 1");
-    if (dtype == MOE_DTYPE_BF16 && H % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16 needs hidden_size % 64 == 0");
-    if (dtype == MOE_DTYPE_F32 && H % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "f32 needs hidden_size % 8 == 0");
+    if (H % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "hidden_size must be a multiple of 8 (16-byte rows)");
   }
   return MOE_OK;
 }

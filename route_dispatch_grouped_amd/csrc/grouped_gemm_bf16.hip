@@ -1986,15 +1986,16 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t s, const char* name) {
 // stages, padding with chunks that read zeros; it takes a K loop when the
 // padding adds at most a third to it, and with gathered rows only from 8
 // stages on (the next tile's row indices are staged at step KT - 8, four
-// steps before its first DMA).  K not a multiple of 32 (possible for the down projection only, whose
-// rows are not gathered) always runs here: the plain 256-row kernel needs
-// whole stages.
+// steps before its first DMA).  K not a multiple of 32 (H or I a multiple of
+// 8 or 16 only) runs here whenever it can, whatever the padding: the plain
+// 256-row kernel needs whole stages.
 bool pipe_fits(const GemmArgs& a) {
   const int64_t KT = (a.K + Big::KB - 1) / Big::KB;
   const int64_t KTp = (KT + 3) & ~(int64_t)3;
-  if (a.K % Big::KB != 0) return a.gather == nullptr;
+  const int64_t min_stages = a.gather ? 8 : 4;
+  if (a.K % Big::KB != 0) return KTp >= min_stages;
   if (3 * KTp > 4 * KT) return false;
-  return a.gather ? KTp >= 8 : KTp >= 4;
+  return KTp >= min_stages;
 }
 
 template <int EPI>
@@ -2010,6 +2011,9 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s, const char* name) {
     default: break;
   }
   if (pipe_fits(a)) return launch_pipe<EPI>(a, s, name);
+  // a short K loop that is not whole 32-wide stages, with gathered rows
+  // (hidden size a multiple of 8 only): 128-row tiles, which mask any K tail
+  if (a.K % Big::KB != 0) return launch_bm<128, EPI>(a, s, name);
   return launch_big<EPI>(a, s, name);
 }
 

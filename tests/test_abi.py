@@ -70,8 +70,9 @@ def test_router_validation(lib):
     assert router(lib, ids=NULL) == INVALID and last(lib) == "topk_ids is NULL"
     assert router(lib, w=NULL) == INVALID and last(lib) == "topk_weights is NULL"
     assert router(lib, x=NULL) == INVALID and last(lib) == "hidden_states is NULL"
-    assert router(lib, H=100) == UNSUP
+    assert router(lib, H=100) == UNSUP and "multiple of 8" in last(lib)
     assert router(lib, H=100, dtype=F32) == UNSUP
+    assert router(lib, H=0) == INVALID
     assert router(lib, dtype=7) == INVALID
     assert router(lib, x=BAD) == UNSUP and "aligned" in last(lib)
     assert router(lib, gate=P16) == INVALID and "shared_gate" in last(lib)

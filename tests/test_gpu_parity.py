@@ -96,6 +96,21 @@ SMALL = {
     "bf16_i176_decode": workloads.config("qwen15_moe_decode").scaled(
         name="bf16_i176_decode", num_tokens=16, hidden_size=256, num_experts=60, top_k=4, intermediate_size=176,
         shared_intermediate_size=704),
+    # hidden sizes that are multiples of 8 but not of 64 (16-byte rows): the
+    # router's and gate/up's K and the down projection's columns end inside a
+    # stage or a column block on every path (the streaming kernel and the
+    # small-batch router; 32-row tiles; the pipelined 256-row kernel with
+    # gathered rows and a padded K loop; the 128-row tiles that take a short
+    # gathered K loop), with fp32 packed outputs (no 64-column segments)
+    "bf16_h136_decode": workloads.config("qwen15_moe_decode").scaled(
+        name="bf16_h136_decode", num_tokens=16, hidden_size=136, num_experts=60, top_k=4, intermediate_size=96,
+        shared_intermediate_size=160),
+    "bf16_h200_mid_rows": workloads.config("qwen3_30b_a3b_prefill").scaled(
+        name="bf16_h200_mid_rows", num_tokens=333, hidden_size=200, num_experts=16, top_k=3, intermediate_size=128),
+    "bf16_h1000_pipe": workloads.config("qwen3_30b_a3b_prefill").scaled(
+        name="bf16_h1000_pipe", num_tokens=1200, hidden_size=1000, num_experts=4, top_k=2, intermediate_size=192),
+    "bf16_h104_short_k": workloads.config("qwen3_30b_a3b_prefill").scaled(
+        name="bf16_h104_short_k", num_tokens=600, hidden_size=104, num_experts=2, top_k=1, intermediate_size=64),
 }
 
 
