@@ -686,6 +686,19 @@ size_t moe_forward_workspace_size(int64_t num_tokens, int64_t hidden_size, int64
       .bytes;
 }
 
+// True when the forward's down projection stores the packed expert outputs as
+// fp16 + one exponent per 64 columns (bf16 layers on the 256-row kernels,
+// H a multiple of 64); otherwise they are fp32.  Depends on the shapes only.
+static bool forward_y_f16s(int64_t P, int64_t E, int64_t H, int dtype) {
+  if (dtype != MOE_DTYPE_BF16 || H % moe::kF16SegCols != 0 || P <= 0) return false;
+  static const int32_t grouped = 0;  // any non-NULL offsets: a grouped GEMM
+  moe::GemmArgs probe = gemm_args();
+  probe.M = (int)P;
+  probe.G = (int)E;
+  probe.offsets = &grouped;
+  return moe::grouped_gemm_has_f16s(probe);
+}
+
 moe_status moe_forward(const void* hidden_states, const void* router_weight, const float* router_bias, const void* w13,
                        const void* w2, const void* shared_w13, const void* shared_w2, const void* shared_gate,
                        int64_t num_tokens, int64_t hidden_size, int64_t num_experts, int64_t top_k,
@@ -699,7 +712,9 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
     return fail(MOE_ERR_INVALID_ARG, "shared_w13, shared_w2 and shared_gate must be given together");
   const int64_t Is = nshared ? shared_intermediate_size : 0;
   if (nshared) RETURN_IF_ERR(check_inter(Is, dtype, "shared_intermediate_size"));
-  RETURN_IF_ERR(check_buffer_bytes(num_tokens, hidden_size, top_k, intermediate_size, dtype, 4));
+  // the packed expert outputs take 2 bytes per value when stored as fp16 + exponents
+  const int64_t y_elt = forward_y_f16s(num_tokens * top_k, num_experts, hidden_size, dtype) ? 2 : 4;
+  RETURN_IF_ERR(check_buffer_bytes(num_tokens, hidden_size, top_k, intermediate_size, dtype, y_elt));
   if (nshared) RETURN_IF_ERR(check_buffer_bytes(num_tokens, hidden_size, 1, Is, dtype, 4));
   if (out_dtype != MOE_DTYPE_F32 && out_dtype != MOE_DTYPE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "out_dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
@@ -796,16 +811,9 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
   // y's fp32-sized slot.
   int y_format = moe::Y_F32;
   int32_t* y_scale = nullptr;
-  if (dtype == MOE_DTYPE_BF16) {
-    moe::GemmArgs probe = gemm_args();
-    probe.M = P;
-    probe.G = E;
-    probe.offsets = L.offsets;
-    probe.K = I;
-    if (moe::grouped_gemm_has_f16s(probe) && H % moe::kF16SegCols == 0) {
-      y_format = moe::Y_F16S;
-      y_scale = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(L.y) + align_up((size_t)P * H * 2));
-    }
+  if (forward_y_f16s(P, E, H, dtype)) {
+    y_format = moe::Y_F16S;
+    y_scale = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(L.y) + align_up((size_t)P * H * 2));
   }
   e = run_ffn(hidden_states, L.packed_ids, L.offsets, w13, w2, T, P, H, E, I, dtype, L.h, L.y, y_format, y_scale, s,
               false, L.counters, L.partial);

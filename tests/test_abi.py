@@ -196,10 +196,14 @@ def test_forward_validation(lib):
     big = lib.moe_forward_workspace_size(8192, 2048, 128, 8, 768, 0, BF16)
     # y [P,H] f32 dominates: 65536 * 2048 * 4 bytes
     assert big > 65536 * 2048 * 4
-    # the largest batch of the Qwen3-30B-A3B layer: y [P, H] f32 must stay
-    # under 2 GiB (32-bit buffer offsets), so T = 32767 is the last valid one
-    assert lib.moe_forward_workspace_size(32767, 2048, 128, 8, 768, 0, BF16) > 32767 * 8 * 2048 * 4
-    assert forward(lib, T=32768, H=2048, E=128, k=8, I=768, wsb=1 << 40) == UNSUP and "2 GiB" in last(lib)
+    # the largest batch of the Qwen3-30B-A3B layer: its packed expert outputs
+    # are fp16 + exponents, and y [P, H] fp16 must stay under 2 GiB (32-bit
+    # buffer offsets), so T = 65535 is the last valid one; the workspace keeps
+    # an fp32-sized slot for them
+    assert lib.moe_forward_workspace_size(65535, 2048, 128, 8, 768, 0, BF16) > 65535 * 8 * 2048 * 4
+    assert forward(lib, T=65536, H=2048, E=128, k=8, I=768, wsb=1 << 40) == UNSUP and "2 GiB" in last(lib)
+    # with H not a multiple of 64 the outputs stay fp32: the limit is half as many tokens
+    assert forward(lib, T=32768, H=2048 + 8, E=128, k=8, I=768, wsb=1 << 40) == UNSUP and "2 GiB" in last(lib)
 
 
 def test_profile_collect_empty(lib):

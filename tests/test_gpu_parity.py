@@ -279,12 +279,13 @@ def test_full_size_forward_every_token(name):
 
 def test_forward_largest_batch_every_token():
     """The largest batch the bf16 layer takes at the Qwen3-30B-A3B shape:
-    T = 32767 tokens, so that y [T*8, 2048] in fp32 is just under 2 GiB, the
-    limit of the kernels' 32-bit buffer offsets (T = 32768 is rejected on the
-    host).  Routing and the plan bit-exact, every token's output against the
+    T = 65535 tokens, so that the packed expert outputs y [T*8, 2048], stored
+    as fp16 + exponents on this path, are just under 2 GiB, the limit of the
+    kernels' 32-bit buffer offsets (T = 65536 is rejected on the host).
+    Routing and the plan bit-exact, every token's output against the
     oracle."""
-    cfg = workloads.config("qwen3_30b_a3b_prefill").scaled(name="qwen3_largest_batch", num_tokens=32767)
-    assert cfg.num_tokens * cfg.top_k * cfg.hidden_size * 4 < 2 ** 31
+    cfg = workloads.config("qwen3_30b_a3b_prefill").scaled(name="qwen3_largest_batch", num_tokens=65535)
+    assert cfg.num_tokens * cfg.top_k * cfg.hidden_size * 2 < 2 ** 31
     inp = workloads.generate(cfg, seed=4)
     log("[parity-full] largest batch: generated")
     dev = device_inputs(inp)
