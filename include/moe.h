@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 #define MOE_MAX_EXPERTS 512
 
 typedef enum moe_status {
@@ -63,7 +63,12 @@ typedef enum moe_status {
 
 typedef enum moe_dtype {
   MOE_DTYPE_F32 = 0,
-  MOE_DTYPE_BF16 = 1
+  MOE_DTYPE_BF16 = 1,
+  /* a bf16 layer whose expert weights (w13, w2 and the shared expert's
+   * shared_w13, shared_w2) are in the K-blocked layout that moe_pack_weights
+   * writes; activations, the router weight and the shared gate stay
+   * row-major.  Accepted wherever a bf16 layer is. */
+  MOE_DTYPE_BF16_KB32 = 2
 } moe_dtype;
 
 /* Projection of one expert, as a per-expert checkpoint names it. */
@@ -386,6 +391,29 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight,
 moe_status moe_tp_load_expert(const void* src, int proj, int64_t hidden_size, int64_t intermediate_size,
                               int tp_size, int tp_rank, int64_t expert, int64_t local_experts, int dtype,
                               void* dst, void* stream);
+
+/*
+ * K-blocked expert weights for MOE_DTYPE_BF16_KB32 layers, written once when
+ * a layer is loaded.
+ * [DWDP README "Executor Module": the executor runs each expert's FFN from
+ *  its weights; modelexpress refit test: the fused w13 [E, 2I, H] and w2
+ *  [E, H, I] it reads]
+ *
+ *   dst[g][b][r][i] = src[g][r][32*b + i]   for b < ceil(k/32), i < 32
+ *                     (0 where 32*b + i >= k)
+ *
+ * src [groups, rows, k] bf16, row-major: w13 (groups = E, rows = 2I, k = H),
+ * w2 (E, H, I), or the shared expert's shared_w13 (1, 2Is, H) and shared_w2
+ * (1, H, Is).  dst: moe_packed_weights_size(groups, rows, k) bytes.  A K step
+ * of 32 of a block of rows is then one contiguous run of memory: the grouped
+ * GEMMs fetch whole 128-byte lines from it where a row-major K step of 32
+ * covers half a line of each row.
+ * k a multiple of 8; src and dst 16-byte aligned and not overlapping; one
+ * group's packed bytes under 2 GiB (UNSUPPORTED otherwise); NULL pointers or
+ * sizes < 1: INVALID_ARG.  Enqueued on `stream`, nothing allocated.
+ */
+size_t moe_packed_weights_size(int64_t groups, int64_t rows, int64_t k);
+moe_status moe_pack_weights(const void* src, void* dst, int64_t groups, int64_t rows, int64_t k, void* stream);
 
 /*
  * Kernel timing for measurement tools.  While enabled, every kernel the

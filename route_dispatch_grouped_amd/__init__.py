@@ -31,7 +31,10 @@ __all__ = [
     "MOE_OK",
     "MOE_DTYPE_F32",
     "MOE_DTYPE_BF16",
+    "MOE_DTYPE_BF16_KB32",
     "MoeError",
+    "PackedWeights",
+    "pack_weights",
     "load_library",
     "library_loaded",
     "moe_router_topk",
@@ -57,6 +60,7 @@ __all__ = [
 MOE_OK = 0
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
+MOE_DTYPE_BF16_KB32 = 2
 MOE_PROJ_GATE = 0
 MOE_PROJ_UP = 1
 MOE_PROJ_DOWN = 2
@@ -96,6 +100,8 @@ _SIGNATURES = {
     "moe_ep_rank_counts": (_int, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
     "moe_tp_load_expert": (_int, [_c_void_p, _int, _i64, _i64, _int, _int, _i64, _i64, _int, _c_void_p,
                                   _c_void_p]),
+    "moe_packed_weights_size": (_size, [_i64, _i64, _i64]),
+    "moe_pack_weights": (_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p]),
     "moe_profile_enable": (None, [_int]),
     "moe_profile_collect": (_int, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(_i64), _int]),
@@ -380,6 +386,56 @@ def moe_ep_rank_counts(expert_offsets: torch.Tensor, num_ranks: int, stream=None
     return {"send_counts": counts, "send_offsets": starts}
 
 
+class PackedWeights:
+    """Expert weights in the K-blocked layout of ``moe_pack_weights``: ``data``,
+    a flat bf16 device tensor, and ``shape``, the (groups, rows, k) shape of the
+    row-major weights it was packed from (``(rows, k)`` for the shared
+    expert's)."""
+
+    def __init__(self, data: torch.Tensor, shape):
+        self.data = data
+        self.shape = tuple(int(v) for v in shape)
+        self.dtype = torch.bfloat16
+        self.device = data.device
+
+
+def pack_weights(w: torch.Tensor, stream=None) -> PackedWeights:
+    """K-blocked copy of bf16 expert weights ``[groups, rows, k]`` or ``[rows, k]``
+    (include/moe.h: moe_pack_weights), for layers called with packed weights."""
+    lib = load_library()
+    if w.dtype != torch.bfloat16:
+        raise TypeError("only bf16 weights are packed")
+    shape = tuple(w.shape)
+    G, R, K = (1,) + shape if w.dim() == 2 else shape
+    _need(w, "weights", shape, torch.bfloat16)
+    with _on(stream):
+        n = int(lib.moe_packed_weights_size(G, R, K))
+        data = torch.empty((n // 2,), dtype=torch.bfloat16, device=w.device)
+    _check("moe_pack_weights", lib.moe_pack_weights(_ptr(w), _ptr(data), G, R, K, _stream(stream)))
+    return PackedWeights(data, shape)
+
+
+def _weights(ws, names, shapes, dt):
+    """Checks expert weights given all row-major (tensors of `shapes`) or all
+    packed (PackedWeights of those shapes); returns (pointers, packed)."""
+    given = [w for w in ws if w is not None]
+    packed = [isinstance(w, PackedWeights) for w in given]
+    if any(packed) and not all(packed):
+        raise ValueError("expert weights must be all packed or all row-major")
+    ptrs = []
+    for w, name, shape in zip(ws, names, shapes):
+        if w is None:
+            ptrs.append(None)
+        elif isinstance(w, PackedWeights):
+            if w.shape != tuple(shape) or dt != torch.bfloat16:
+                raise ValueError(f"{name}: packed weights of shape {w.shape}, expected {tuple(shape)} (bf16 layers)")
+            ptrs.append(_ptr(w.data))
+        else:
+            _need(w, name, shape, dt)
+            ptrs.append(_ptr(w))
+    return ptrs, bool(given) and all(packed)
+
+
 def moe_grouped_ffn(hidden_states: torch.Tensor, packed_token_indices: Optional[torch.Tensor],
                     expert_offsets: Optional[torch.Tensor], w13: torch.Tensor, w2: torch.Tensor, top_k: int,
                     out_dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
@@ -395,8 +451,8 @@ def moe_grouped_ffn(hidden_states: torch.Tensor, packed_token_indices: Optional[
     dt = hidden_states.dtype
     P = T * top_k
     _need(hidden_states, "hidden_states", (T, H), dt)
-    _need(w13, "w13", (E, 2 * I, H), dt)
-    _need(w2, "w2", (E, H, I), dt)
+    (p13, p2), packed = _weights([w13, w2], ["w13", "w2"], [(E, 2 * I, H), (E, H, I)], dt)
+    code = MOE_DTYPE_BF16_KB32 if packed else _dtype_code(dt)
     if packed_token_indices is not None:
         _need(packed_token_indices, "packed_token_indices", (P,), torch.int32)
     if expert_offsets is not None:
@@ -406,9 +462,9 @@ def moe_grouped_ffn(hidden_states: torch.Tensor, packed_token_indices: Optional[
         y = torch.empty((P, H), dtype=out_dtype, device=dev)
         ws_bytes = lib.moe_grouped_ffn_workspace_size(T, H, top_k, E, I, _dtype_code(dt))
         ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
-    st = lib.moe_grouped_ffn(_ptr(hidden_states), _ptr(packed_token_indices), _ptr(expert_offsets), _ptr(w13),
-                             _ptr(w2), T, H, E, int(top_k), I, _dtype_code(dt), _dtype_code(out_dtype), _ptr(y),
-                             _ptr(ws), ws.numel(), _stream(stream))
+    st = lib.moe_grouped_ffn(_ptr(hidden_states), _ptr(packed_token_indices), _ptr(expert_offsets), p13, p2,
+                             T, H, E, int(top_k), I, code, _dtype_code(out_dtype), _ptr(y), _ptr(ws), ws.numel(),
+                             _stream(stream))
     _check("moe_grouped_ffn", st)
     return y
 
@@ -522,16 +578,16 @@ def moe_forward(hidden_states: torch.Tensor, router_weight: torch.Tensor, w13: t
     dt = hidden_states.dtype
     _need(hidden_states, "hidden_states", (T, H), dt)
     _need(router_weight, "router_weight", (E, H), dt)
-    _need(w13, "w13", (E, 2 * I, H), dt)
-    _need(w2, "w2", (E, H, I), dt)
     if router_bias is not None:
         _need(router_bias, "router_bias", (E,), torch.float32)
     Is = 0
     if shared_w13 is not None:
         Is = shared_w13.shape[0] // 2
-        _need(shared_w13, "shared_w13", (2 * Is, H), dt)
-        _need(shared_w2, "shared_w2", (H, Is), dt)
         _need(shared_gate, "shared_gate", (H,), dt)
+    (p13, p2, ps13, ps2), packed = _weights(
+        [w13, w2, shared_w13, shared_w2], ["w13", "w2", "shared_w13", "shared_w2"],
+        [(E, 2 * I, H), (E, H, I), (2 * Is, H), (H, Is)], dt)
+    code = MOE_DTYPE_BF16_KB32 if packed else _dtype_code(dt)
     dev = hidden_states.device
     with _on(stream):
         if out is None:
@@ -546,9 +602,9 @@ def moe_forward(hidden_states: torch.Tensor, router_weight: torch.Tensor, w13: t
             ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
             wts = torch.empty((T, top_k), dtype=torch.float32, device=dev)
             logits = torch.empty((T, E), dtype=torch.float32, device=dev)
-    st = lib.moe_forward(_ptr(hidden_states), _ptr(router_weight), _ptr(router_bias), _ptr(w13), _ptr(w2),
-                         _ptr(shared_w13), _ptr(shared_w2), _ptr(shared_gate), T, H, E, int(top_k), I, Is,
-                         int(bool(renormalize)), _dtype_code(dt), _dtype_code(out_dtype), _ptr(out), _ptr(ids),
+    st = lib.moe_forward(_ptr(hidden_states), _ptr(router_weight), _ptr(router_bias), p13, p2,
+                         ps13, ps2, _ptr(shared_gate), T, H, E, int(top_k), I, Is,
+                         int(bool(renormalize)), code, _dtype_code(out_dtype), _ptr(out), _ptr(ids),
                          _ptr(wts), _ptr(logits), _ptr(workspace), workspace.numel(), _stream(stream))
     _check("moe_forward", st)
     if return_routing:
@@ -562,12 +618,20 @@ class MoeLayer:
     Mirrors the explicit-layer binding of the DWDP README ("How To Use",
     ``build_reference(hidden_size, num_experts, top_k, experts)``): the expert
     weights are given as the fused ``w13 [E, 2I, H]`` and ``w2 [E, H, I]``.
-    ``forward`` allocates nothing once the layer has seen the largest token
-    count it will be called with.
+    A bf16 layer keeps K-blocked copies of its expert weights
+    (``pack_weights``, made here once; ``pack=False`` keeps the tensors as
+    given).  ``forward`` allocates nothing once the layer has seen the largest
+    token count it will be called with.
     """
 
     def __init__(self, router_weight, w13, w2, top_k, router_bias=None, shared_w13=None, shared_w2=None,
-                 shared_gate=None, renormalize=True, out_dtype=torch.float32):
+                 shared_gate=None, renormalize=True, out_dtype=torch.float32, pack=None):
+        if pack is None:
+            pack = isinstance(w13, torch.Tensor) and w13.dtype == torch.bfloat16
+        if pack:
+            w13, w2 = pack_weights(w13), pack_weights(w2)
+            if shared_w13 is not None:
+                shared_w13, shared_w2 = pack_weights(shared_w13), pack_weights(shared_w2)
         self.router_weight, self.w13, self.w2 = router_weight, w13, w2
         self.router_bias = router_bias
         self.shared_w13, self.shared_w2, self.shared_gate = shared_w13, shared_w2, shared_gate

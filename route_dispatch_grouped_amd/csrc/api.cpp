@@ -78,6 +78,15 @@ moe_status check_inter(int64_t I, int dtype, const char* name) {
   return MOE_OK;
 }
 
+// One expert's K-blocked w13 [2I, H] and w2 [H, I] must each stay under 2 GiB
+// (32-bit buffer offsets).
+moe_status check_packed_bytes(int64_t H, int64_t I) {
+  const size_t lim = ((size_t)1 << 31) - 1;
+  if (moe::kb32_bytes(2 * I, H) > lim || moe::kb32_bytes(H, I) > lim)
+    return fail(MOE_ERR_UNSUPPORTED, "one expert's packed weights exceed 2 GiB (32-bit buffer offsets)");
+  return MOE_OK;
+}
+
 #define REQUIRE_PTR(p)                                                       \
   do {                                                                       \
     if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, #p " is NULL");     \
@@ -203,8 +212,9 @@ hipError_t run_router(const void* x, const void* wr, const float* bias, const vo
 // bf16 when y_dtype is MOE_DTYPE_BF16 (bf16 layers only), else fp32.
 // y_format (moe::YFormat, bf16 layers only for Y_BF16 and Y_F16S): fp32 y,
 // bf16 y, or fp16 y with the exponents y_scale [P, H/64].
+// packed: w13 / w2 K-blocked (moe_pack_weights), bf16 layers only.
 hipError_t run_ffn(const void* x, const int32_t* gather, const int32_t* offsets, const void* w13, const void* w2,
-                   int T_rows, int P, int H, int E, int I, int dtype, void* h, void* y, int y_format,
+                   int T_rows, int P, int H, int E, int I, int dtype, bool packed, void* h, void* y, int y_format,
                    int32_t* y_scale, hipStream_t s, bool shared, int* counters, float* partial) {
   hipError_t e;
   if (dtype == MOE_DTYPE_BF16) {
@@ -224,8 +234,12 @@ hipError_t run_ffn(const void* x, const int32_t* gather, const int32_t* offsets,
     a.ldo = I;
     a.tile_counter = counters;
     a.partial = partial;
-    e = moe::launch_grouped_gemm_bf16(a, moe::EPI_SWIGLU, s, shared ? "shared_gate_up_bf16" : "ffn_gate_up_bf16");
-    if (e != hipSuccess) return e;
+    if (packed) {
+      a.b_group_bytes = (uint32_t)moe::kb32_bytes(2 * I, H);
+      a.b_group_stride = (int64_t)a.b_group_bytes / 2;
+      a.b_row_pitch = 64;
+      a.b_blk_pitch = 64u * (uint32_t)(2 * I);
+    }
     moe::GemmArgs b = gemm_args();
     b.A = static_cast<const uint16_t*>(h);
     b.gather = nullptr;
@@ -245,6 +259,22 @@ hipError_t run_ffn(const void* x, const int32_t* gather, const int32_t* offsets,
     const moe::GemmEpilogue epi = (y_format == moe::Y_BF16)   ? moe::EPI_BF16
                                   : (y_format == moe::Y_F16S) ? moe::EPI_F16S
                                                               : moe::EPI_F32;
+    if (packed) {
+      b.b_group_bytes = (uint32_t)moe::kb32_bytes(H, I);
+      b.b_group_stride = (int64_t)b.b_group_bytes / 2;
+      b.b_row_pitch = 64;
+      b.b_blk_pitch = 64u * (uint32_t)H;
+    }
+    // h K-blocked ([I/32][P][32]) when both GEMMs run the pipelined kernel:
+    // the down projection then fetches whole 128-byte lines of it
+    if (I % moe::kKBlock == 0 && moe::grouped_gemm_runs_pipe8(a, moe::EPI_SWIGLU) &&
+        moe::grouped_gemm_runs_pipe8(b, epi)) {
+      a.out_kblocked = 1;
+      b.a_row_pitch = 64;
+      b.a_blk_pitch = 64u * (uint32_t)P;
+    }
+    e = moe::launch_grouped_gemm_bf16(a, moe::EPI_SWIGLU, s, shared ? "shared_gate_up_bf16" : "ffn_gate_up_bf16");
+    if (e != hipSuccess) return e;
     return moe::launch_grouped_gemm_bf16(b, epi, s, shared ? "shared_down_bf16" : "ffn_down_bf16");
   }
   e = moe::launch_ffn_gate_up_f32(static_cast<const float*>(x), gather, offsets, static_cast<const float*>(w13), P,
@@ -383,6 +413,7 @@ moe_status moe_router_topk(const void* hidden_states, const void* router_weight,
                            const void* shared_gate, int64_t num_tokens, int64_t hidden_size, int64_t num_experts,
                            int64_t top_k, int renormalize, int dtype, float* router_logits, float* routing_probs,
                            int32_t* topk_ids, float* topk_weights, float* shared_gate_logit, void* stream) {
+  if (dtype == MOE_DTYPE_BF16_KB32) dtype = MOE_DTYPE_BF16;  // the router weight is row-major either way
   RETURN_IF_ERR(check_sizes(num_tokens, hidden_size, num_experts, top_k, dtype, true));
   RETURN_IF_ERR(check_buffer_bytes(num_tokens, hidden_size, 1, 1, dtype));
   if (num_tokens == 0) return succeed();
@@ -413,6 +444,7 @@ moe_status moe_router_topk_grouped(const void* hidden_states, const void* router
                                    int64_t n_group, int64_t topk_group, int renormalize, int dtype,
                                    float* router_logits, float* routing_probs, int32_t* topk_ids, float* topk_weights,
                                    void* stream) {
+  if (dtype == MOE_DTYPE_BF16_KB32) dtype = MOE_DTYPE_BF16;  // the router weight is row-major either way
   RETURN_IF_ERR(check_sizes(num_tokens, hidden_size, num_experts, top_k, dtype, true));
   RETURN_IF_ERR(check_buffer_bytes(num_tokens, hidden_size, 1, 1, dtype));
   if (n_group < 1 || n_group > 64) return fail(MOE_ERR_INVALID_ARG, "n_group must be in [1, 64]");
@@ -538,6 +570,8 @@ moe_status moe_tp_load_expert(const void* src, int proj, int64_t hidden_size, in
                               void* dst, void* stream) {
   REQUIRE_PTR(src);
   REQUIRE_PTR(dst);
+  if (dtype == MOE_DTYPE_BF16_KB32)
+    return fail(MOE_ERR_INVALID_ARG, "the loader writes row-major weights: load with MOE_DTYPE_BF16, then moe_pack_weights");
   if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
   if (proj != MOE_PROJ_GATE && proj != MOE_PROJ_UP && proj != MOE_PROJ_DOWN)
     return fail(MOE_ERR_INVALID_ARG, "unknown proj");
@@ -564,6 +598,28 @@ moe_status moe_tp_load_expert(const void* src, int proj, int64_t hidden_size, in
                     "moe_tp_load_expert");
 }
 
+size_t moe_packed_weights_size(int64_t groups, int64_t rows, int64_t k) {
+  if (groups < 1 || rows < 1 || k < 1) return 0;
+  return (size_t)groups * moe::kb32_bytes(rows, k);
+}
+
+moe_status moe_pack_weights(const void* src, void* dst, int64_t groups, int64_t rows, int64_t k, void* stream) {
+  REQUIRE_PTR(src);
+  REQUIRE_PTR(dst);
+  if (groups < 1 || rows < 1 || k < 1) return fail(MOE_ERR_INVALID_ARG, "groups, rows and k must be >= 1");
+  if (k % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "k must be a multiple of 8 (16-byte rows)");
+  if (moe::kb32_bytes(rows, k) > ((size_t)1 << 31) - 1)
+    return fail(MOE_ERR_UNSUPPORTED, "one group's packed weights exceed 2 GiB (32-bit buffer offsets)");
+  REQUIRE_ALIGNED(src);
+  REQUIRE_ALIGNED(dst);
+  const char* s0 = static_cast<const char*>(src);
+  const char* d0 = static_cast<const char*>(dst);
+  const size_t src_bytes = (size_t)groups * rows * k * 2, dst_bytes = moe_packed_weights_size(groups, rows, k);
+  if (s0 < d0 + dst_bytes && d0 < s0 + src_bytes) return fail(MOE_ERR_INVALID_ARG, "src and dst overlap");
+  return hip_status(moe::launch_pack_kb32(src, dst, groups, rows, k, static_cast<hipStream_t>(stream)),
+                    "moe_pack_weights");
+}
+
 moe_status moe_ep_rank_counts(const int32_t* expert_offsets, int64_t num_experts, int64_t num_ranks,
                               int32_t* send_counts, int32_t* send_offsets, void* stream) {
   REQUIRE_PTR(expert_offsets);
@@ -586,6 +642,7 @@ size_t grouped_ffn_partial_bytes(int64_t P, int64_t H, int64_t E, int64_t I, int
 
 size_t moe_grouped_ffn_workspace_size(int64_t num_tokens, int64_t hidden_size, int64_t top_k, int64_t num_experts,
                                       int64_t intermediate_size, int dtype) {
+  if (dtype == MOE_DTYPE_BF16_KB32) dtype = MOE_DTYPE_BF16;
   if (num_tokens < 0 || hidden_size < 1 || top_k < 1 || num_experts < 1 || intermediate_size < 1) return 0;
   const int64_t P = num_tokens * top_k;
   // tile counters of the two GEMMs, h, then the split-K partial sums
@@ -598,8 +655,11 @@ moe_status moe_grouped_ffn(const void* hidden_states, const int32_t* packed_toke
                            int64_t hidden_size, int64_t num_experts, int64_t top_k, int64_t intermediate_size,
                            int dtype, int expert_out_dtype, void* packed_expert_outputs, void* workspace,
                            size_t workspace_bytes, void* stream) {
+  const bool packed = dtype == MOE_DTYPE_BF16_KB32;
+  if (packed) dtype = MOE_DTYPE_BF16;
   RETURN_IF_ERR(check_sizes(num_tokens, hidden_size, num_experts, top_k, dtype, true));
   RETURN_IF_ERR(check_inter(intermediate_size, dtype, "intermediate_size"));
+  if (packed) RETURN_IF_ERR(check_packed_bytes(hidden_size, intermediate_size));
   if (expert_out_dtype != MOE_DTYPE_F32 && expert_out_dtype != MOE_DTYPE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "expert_out_dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
   if (expert_out_dtype == MOE_DTYPE_BF16 && dtype != MOE_DTYPE_BF16)
@@ -636,7 +696,7 @@ moe_status moe_grouped_ffn(const void* hidden_states, const int32_t* packed_toke
     if (ez != hipSuccess) return hip_status(ez, "moe_grouped_ffn");
   }
   return hip_status(run_ffn(hidden_states, packed_token_indices, expert_offsets, w13, w2, (int)num_tokens, P,
-                            (int)hidden_size, (int)num_experts, (int)intermediate_size, dtype, h,
+                            (int)hidden_size, (int)num_experts, (int)intermediate_size, dtype, packed, h,
                             packed_expert_outputs, expert_out_dtype == MOE_DTYPE_BF16 ? moe::Y_BF16 : moe::Y_F32,
                             nullptr, s, false,
                             dtype == MOE_DTYPE_BF16 ? counters : nullptr,
@@ -678,6 +738,7 @@ moe_status moe_combine(const void* packed_expert_outputs, const int32_t* inverse
 
 size_t moe_forward_workspace_size(int64_t num_tokens, int64_t hidden_size, int64_t num_experts, int64_t top_k,
                                   int64_t intermediate_size, int64_t shared_intermediate_size, int dtype) {
+  if (dtype == MOE_DTYPE_BF16_KB32) dtype = MOE_DTYPE_BF16;
   if (num_tokens < 0 || hidden_size < 1 || num_experts < 1 || top_k < 1 || intermediate_size < 1 ||
       shared_intermediate_size < 0)
     return 0;
@@ -705,13 +766,17 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
                        int64_t intermediate_size, int64_t shared_intermediate_size, int renormalize, int dtype,
                        int out_dtype, void* output, int32_t* topk_ids_out, float* topk_weights_out,
                        float* router_logits_out, void* workspace, size_t workspace_bytes, void* stream) {
+  const bool packed = dtype == MOE_DTYPE_BF16_KB32;
+  if (packed) dtype = MOE_DTYPE_BF16;
   RETURN_IF_ERR(check_sizes(num_tokens, hidden_size, num_experts, top_k, dtype, true));
   RETURN_IF_ERR(check_inter(intermediate_size, dtype, "intermediate_size"));
+  if (packed) RETURN_IF_ERR(check_packed_bytes(hidden_size, intermediate_size));
   const int nshared = (shared_w13 != nullptr) + (shared_w2 != nullptr) + (shared_gate != nullptr);
   if (nshared != 0 && nshared != 3)
     return fail(MOE_ERR_INVALID_ARG, "shared_w13, shared_w2 and shared_gate must be given together");
   const int64_t Is = nshared ? shared_intermediate_size : 0;
   if (nshared) RETURN_IF_ERR(check_inter(Is, dtype, "shared_intermediate_size"));
+  if (nshared && packed) RETURN_IF_ERR(check_packed_bytes(hidden_size, Is));
   // the packed expert outputs take 2 bytes per value when stored as fp16 + exponents
   const int64_t y_elt = forward_y_f16s(num_tokens * top_k, num_experts, hidden_size, dtype) ? 2 : 4;
   RETURN_IF_ERR(check_buffer_bytes(num_tokens, hidden_size, top_k, intermediate_size, dtype, y_elt));
@@ -795,7 +860,7 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
         if (e != hipSuccess) return hip_status(e, "moe_forward(shared expert)");
       }
     }
-    e = run_ffn(hidden_states, nullptr, nullptr, shared_w13, shared_w2, T, T, H, 1, (int)Is, dtype, L.hs, L.ys,
+    e = run_ffn(hidden_states, nullptr, nullptr, shared_w13, shared_w2, T, T, H, 1, (int)Is, dtype, packed, L.hs, L.ys,
                 moe::Y_F32, nullptr, ss, true, shared_counters, L.partial_shared);
     if (e != hipSuccess) return hip_status(e, "moe_forward(shared expert)");
     if (aux != nullptr) {
@@ -815,7 +880,8 @@ moe_status moe_forward(const void* hidden_states, const void* router_weight, con
     y_format = moe::Y_F16S;
     y_scale = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(L.y) + align_up((size_t)P * H * 2));
   }
-  e = run_ffn(hidden_states, L.packed_ids, L.offsets, w13, w2, T, P, H, E, I, dtype, L.h, L.y, y_format, y_scale, s,
+  e = run_ffn(hidden_states, L.packed_ids, L.offsets, w13, w2, T, P, H, E, I, dtype, packed, L.h, L.y, y_format,
+              y_scale, s,
               false, L.counters, L.partial);
   if (e != hipSuccess) return hip_status(e, "moe_forward(experts)");
   if (aux != nullptr) {

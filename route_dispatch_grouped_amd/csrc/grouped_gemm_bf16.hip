@@ -156,6 +156,17 @@ struct DmaPlan {
   bool ktail;
 };
 
+// Byte offset of the 16-byte chunk at byte cb of a stage row of row r, for an
+// operand whose element (r, k) sits at row_pitch * r + blk_pitch * (k / 32) +
+// 2 * (k % 32) (row-major: row_pitch = 2K, blk_pitch = 64).  The stage's own
+// K offset goes separately into the DMA's scalar offset (stage_off).
+__device__ __forceinline__ uint32_t chunk_off(int r, uint32_t cb, uint32_t row_pitch, uint32_t blk_pitch) {
+  return (uint32_t)r * row_pitch + (cb >> 6) * blk_pitch + (cb & 63u);
+}
+// Scalar offset of the stage starting at logical byte kbytes of a row (a
+// multiple of 64).
+__device__ __forceinline__ int stage_off(int kbytes, uint32_t blk_pitch) { return (kbytes >> 6) * (int)blk_pitch; }
+
 // Raw buffer resource (gfx9 V#): 48-bit base, stride 0, size in bytes; loads
 // past `bytes` return zero instead of faulting.
 __device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t bytes) {
@@ -193,7 +204,7 @@ __device__ __forceinline__ void dma4(const int* lds_dst, u32x4_t rsrc, uint32_t 
 
 template <int BM, int BR>
 __device__ __forceinline__ void issue_stage(u32x4_t* buf, const DmaPlan<BM, BR>& d, u32x4_t ra, u32x4_t rb,
-                                            int wave, int kbytes) {
+                                            int wave, int kbytes, uint32_t b_blk) {
   using C = Tile<BM, BR>;
 #pragma unroll
   for (int qi = 0; qi < C::A_MAX; ++qi) {
@@ -207,7 +218,7 @@ __device__ __forceinline__ void issue_stage(u32x4_t* buf, const DmaPlan<BM, BR>&
     const int q = qi * 4 + wave;
     uint32_t v = d.b_off[qi];
     if (d.ktail && d.b_cb[qi] + (uint32_t)kbytes >= d.row_bytes) v = 0x80000000u;
-    dma16(buf + BM * 8 + q * 64, rb, v, kbytes);
+    dma16(buf + BM * 8 + q * 64, rb, v, stage_off(kbytes, b_blk));
   }
 }
 
@@ -235,14 +246,14 @@ __device__ __forceinline__ void mma_stage(f32x4_t (&acc)[BM / 16][NJ], const u32
 template <int BM, int BR, int NJ, int LIVE>
 __device__ __forceinline__ void kloop(f32x4_t (&acc)[BM / 16][NJ], u32x4_t* ring, const DmaPlan<BM, BR>& d,
                                       u32x4_t ra, u32x4_t rb, int wave, int lane, int KT, int kbase, bool wave_live,
-                                      const int (&brow)[NJ]) {
+                                      const int (&brow)[NJ], uint32_t b_blk) {
   using C = Tile<BM, BR>;
   static_assert(NJ == C::NJ, "weight sub-tiles per wave");
   constexpr int NS = C::NS;
   // prologue: stages 0 .. NS-2 in flight (kbase: byte offset of this tile's K range)
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
-    if (st < KT) issue_stage<BM, BR>(ring + st * C::SLOTS, d, ra, rb, wave, kbase + st * BK * 2);
+    if (st < KT) issue_stage<BM, BR>(ring + st * C::SLOTS, d, ra, rb, wave, kbase + st * BK * 2, b_blk);
   for (int kt0 = 0; kt0 < KT; kt0 += NS) {
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
@@ -253,7 +264,8 @@ __device__ __forceinline__ void kloop(f32x4_t (&acc)[BM / 16][NJ], u32x4_t* ring
       else wait_vmcnt<0>();
       lds_barrier();
       if (kt + NS - 1 < KT)
-        issue_stage<BM, BR>(ring + ((u + NS - 1) % NS) * C::SLOTS, d, ra, rb, wave, kbase + (kt + NS - 1) * BK * 2);
+        issue_stage<BM, BR>(ring + ((u + NS - 1) % NS) * C::SLOTS, d, ra, rb, wave, kbase + (kt + NS - 1) * BK * 2,
+                            b_blk);
       if (wave_live) mma_stage<BM, NJ, LIVE>(acc, ring + u * C::SLOTS, brow, lane);
     }
   }
@@ -412,14 +424,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
       // the router) fetch through an offset past the buffer: zeros, no traffic
       const int col = (EPI == EPI_SWIGLU) ? n0 + (r & 127) : n0 + r;
       const int wr = (EPI == EPI_SWIGLU && r >= 128) ? p.up_row0 + col : col;
-      d.b_off[qi] = (col < p.N) ? (uint32_t)wr * row_bytes + (uint32_t)c * 16u : 0x80000000u;
+      d.b_off[qi] = (col < p.N) ? chunk_off(wr, (uint32_t)c * 16u, p.b_row_pitch, p.b_blk_pitch) : 0x80000000u;
       d.b_cb[qi] = (uint32_t)c * 16u;
     }
     d.row_bytes = row_bytes;
     d.ktail = (p.K % BK) != 0;
     const u32x4_t ra = make_rsrc(p.A, (uint32_t)p.a_rows * row_bytes);
-    const int b_rows_total = (EPI == EPI_SWIGLU) ? 2 * p.up_row0 : p.N;
-    const u32x4_t rb = make_rsrc(Bg, (uint32_t)b_rows_total * row_bytes);
+    const u32x4_t rb = make_rsrc(Bg, p.b_group_bytes);
 
     const int wave_col0 = (EPI == EPI_SWIGLU) ? n0 + 32 * wave : n0 + (BR / 4) * wave;
     const bool wave_live = wave_col0 < p.N;
@@ -434,7 +445,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs p)
 #define MOE_LIVE_CASE(n)                                                                                      \
   case n:                                                                                                     \
     if (n <= MSUB)                                                                                            \
-      kloop<BM, BR, NJ, (n <= MSUB ? n : MSUB)>(acc, ring, d, ra, rb, wave, lane, KT, kbase, wave_live, brow); \
+      kloop<BM, BR, NJ, (n <= MSUB ? n : MSUB)>(acc, ring, d, ra, rb, wave, lane, KT, kbase, wave_live, brow,   \
+                                                p.b_blk_pitch);                                                  \
     break;
       MOE_LIVE_CASE(1) MOE_LIVE_CASE(2) MOE_LIVE_CASE(3) MOE_LIVE_CASE(4)
       MOE_LIVE_CASE(5) MOE_LIVE_CASE(6) MOE_LIVE_CASE(7) MOE_LIVE_CASE(8)
@@ -632,15 +644,14 @@ __device__ __forceinline__ void stream_plan(StreamPlan<BM>& d, const GemmArgs& p
       col = u.n0 + rb;
       wr = col;
     }
-    d.b_off[qi] = (col < p.N) ? (uint32_t)wr * row_bytes + (uint32_t)c * 16u : 0x80000000u;
+    d.b_off[qi] = (col < p.N) ? chunk_off(wr, (uint32_t)c * 16u, p.b_row_pitch, p.b_blk_pitch) : 0x80000000u;
   }
-  const int b_rows_total = (EPI == EPI_SWIGLU) ? 2 * p.up_row0 : p.N;
-  d.rb = make_rsrc(p.B + (int64_t)u.g * p.b_group_stride, (uint32_t)b_rows_total * row_bytes);
+  d.rb = make_rsrc(p.B + (int64_t)u.g * p.b_group_stride, p.b_group_bytes);
 }
 
 template <int BM>
 __device__ __forceinline__ void stream_issue(u32x4_t* buf, const StreamPlan<BM>& d, u32x4_t ra, int wave, int kbytes,
-                                             uint32_t row_bytes, bool ktail) {
+                                             uint32_t row_bytes, bool ktail, uint32_t b_blk) {
   using C = StreamTile<BM>;
 #pragma unroll
   for (int qi = 0; qi < C::A_PER; ++qi) {
@@ -652,7 +663,7 @@ __device__ __forceinline__ void stream_issue(u32x4_t* buf, const StreamPlan<BM>&
   for (int qi = 0; qi < C::B_PER; ++qi) {
     uint32_t v = d.b_off[qi];
     if (ktail && d.b_cb[qi] + (uint32_t)kbytes >= row_bytes) v = 0x80000000u;
-    dma16(buf + BM * kStreamCH + (qi * 4 + wave) * 64, d.rb, v, kbytes);
+    dma16(buf + BM * kStreamCH + (qi * 4 + wave) * 64, d.rb, v, stage_off(kbytes, b_blk));
   }
 }
 
@@ -731,7 +742,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_stream_kernel(Gemm
 
   auto issue_next = [&]() {
     stream_issue<BM>(ring + dma_slot * C::SLOTS, dp, ra, wave, (ud.kc * KTc + kt_dma) * kStageBytes, row_bytes,
-                     ktail);
+                     ktail, p.b_blk_pitch);
     ++issued;
     dma_slot = (dma_slot + 1 == kStreamNS) ? 0 : dma_slot + 1;
     if (++kt_dma == ud.KT) {
@@ -874,11 +885,12 @@ struct BigPlan {
 };
 
 __device__ __forceinline__ void big_issue(u32x4_t* buf, const BigPlan& d, u32x4_t ra, u32x4_t rb, int wave,
-                                          int kbytes) {
+                                          int kbytes, uint32_t b_blk) {
 #pragma unroll
   for (int qi = 0; qi < 4; ++qi) dma16(buf + (qi * 4 + wave) * 64, ra, d.a_off[qi], kbytes);
 #pragma unroll
-  for (int qi = 0; qi < 4; ++qi) dma16(buf + Big::A_SLOTS + (qi * 4 + wave) * 64, rb, d.b_off[qi], kbytes);
+  for (int qi = 0; qi < 4; ++qi)
+    dma16(buf + Big::A_SLOTS + (qi * 4 + wave) * 64, rb, d.b_off[qi], stage_off(kbytes, b_blk));
 }
 
 // Byte position of this lane's 16-byte chunk inside a 64-byte stage row.  A
@@ -952,7 +964,7 @@ template <int EPI, int LIVE>
 __device__ __forceinline__ void big_step(f32x16_t (&acc)[4][4], const BigFrags& cur, BigFrags& nxt,
                                          u32x4_t* refill, const u32x4_t* __restrict__ next_buf, bool dma, int kbytes,
                                          const BigPlan& d, u32x4_t ra, u32x4_t rb, int wave,
-                                         const int (&a_slot)[2], const int (&b_slot)[2]) {
+                                         const int (&a_slot)[2], const int (&b_slot)[2], uint32_t b_blk) {
   static_assert(LIVE >= 1 && LIVE <= 4, "live row sub-tiles");
   constexpr int NG = 2 * LIVE;
 #pragma unroll
@@ -966,7 +978,7 @@ __device__ __forceinline__ void big_step(f32x16_t (&acc)[4][4], const BigFrags& 
 #pragma unroll
       for (int q = (g * 8) / NG; q < ((g + 1) * 8) / NG; ++q) {
         if (q < 4) dma16(refill + (q * 4 + wave) * 64, ra, d.a_off[q], kbytes);
-        else dma16(refill + Big::A_SLOTS + ((q - 4) * 4 + wave) * 64, rb, d.b_off[q - 4], kbytes);
+        else dma16(refill + Big::A_SLOTS + ((q - 4) * 4 + wave) * 64, rb, d.b_off[q - 4], stage_off(kbytes, b_blk));
       }
     }
     // read chunk c (0, 1: weight fragments of h = c; 2, 3: row fragments of
@@ -998,19 +1010,19 @@ __device__ __forceinline__ void big_step(f32x16_t (&acc)[4][4], const BigFrags& 
 template <int EPI, int LIVE>
 __device__ __forceinline__ void big_kloop(f32x16_t (&acc)[4][4], u32x4_t* s0, u32x4_t* s1, u32x4_t* s2,
                                           u32x4_t* s3, const BigPlan& d, u32x4_t ra, u32x4_t rb, int wave, int KT,
-                                          const int (&a_slot)[2], const int (&b_slot)[2]) {
+                                          const int (&a_slot)[2], const int (&b_slot)[2], uint32_t b_blk) {
   u32x4_t* bufs[4] = {s0, s1, s2, s3};
   int issued = 0;
 #pragma unroll
   for (int st = 0; st < 3; ++st)
     if (st < KT) {
-      big_issue(bufs[st], d, ra, rb, wave, st * Big::KB * 2);
+      big_issue(bufs[st], d, ra, rb, wave, st * Big::KB * 2, b_blk);
       ++issued;
     }
   big_wait(0, issued);
   lds_barrier();
   if (3 < KT) {
-    big_issue(s3, d, ra, rb, wave, 3 * Big::KB * 2);
+    big_issue(s3, d, ra, rb, wave, 3 * Big::KB * 2, b_blk);
     ++issued;
   }
   BigFrags fx, fy;
@@ -1027,9 +1039,9 @@ __device__ __forceinline__ void big_kloop(f32x16_t (&acc)[4][4], u32x4_t* s0, u3
       const bool dma = kt + 4 < KT;
       if constexpr (LIVE >= 1) {
         big_step<EPI, LIVE>(acc, cur, nxt, bufs[u], bufs[(u + 1) & 3], dma, (kt + 4) * Big::KB * 2, d, ra, rb,
-                            wave, a_slot, b_slot);
+                            wave, a_slot, b_slot, b_blk);
       } else {
-        if (dma) big_issue(bufs[u], d, ra, rb, wave, (kt + 4) * Big::KB * 2);
+        if (dma) big_issue(bufs[u], d, ra, rb, wave, (kt + 4) * Big::KB * 2, b_blk);
       }
       if (dma) ++issued;
     }
@@ -1121,11 +1133,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_big_kernel(GemmArg
       } else {
         wr = min(n0 + r, p.N - 1);
       }
-      d.b_off[qi] = (uint32_t)wr * row_bytes + (uint32_t)c * 16u;
+      d.b_off[qi] = chunk_off(wr, (uint32_t)c * 16u, p.b_row_pitch, p.b_blk_pitch);
     }
     const u32x4_t ra = make_rsrc(p.A, (uint32_t)p.a_rows * row_bytes);
-    const int b_rows_total = (EPI == EPI_SWIGLU) ? 2 * p.up_row0 : p.N;
-    const u32x4_t rb = make_rsrc(Bg, (uint32_t)b_rows_total * row_bytes);
+    const u32x4_t rb = make_rsrc(Bg, p.b_group_bytes);
 
     f32x16_t acc[4][4];
 #pragma unroll
@@ -1139,7 +1150,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_big_kernel(GemmArg
     const int live = __builtin_amdgcn_readfirstlane(min(4, (units - wm + 1) >> 1));
     switch (live) {
 #define MOE_BIG_CASE(n) \
-  case n: big_kloop<EPI, n>(acc, st0, st1, st2, st3, d, ra, rb, wave, KT, a_slot, b_slot); break;
+  case n: big_kloop<EPI, n>(acc, st0, st1, st2, st3, d, ra, rb, wave, KT, a_slot, b_slot, p.b_blk_pitch); break;
       MOE_BIG_CASE(0) MOE_BIG_CASE(1) MOE_BIG_CASE(2) MOE_BIG_CASE(3) MOE_BIG_CASE(4)
 #undef MOE_BIG_CASE
       default: break;
@@ -1331,12 +1342,14 @@ __device__ __forceinline__ u32x4_t pair_columns(uint32_t g_lo, uint32_t g_hi, ui
   return u32x4_t{(uint32_t)x[0], (uint32_t)y[0], (uint32_t)x[1], (uint32_t)y[1]};
 }
 
+// a_blk / b_blk: block pitches of A and B (64 for row-major operands).
 __device__ __forceinline__ void p8_issue(u32x4_t* buf, const Plan8& d, u32x4_t ra, u32x4_t rb, int wave,
-                                         int kbytes) {
+                                         int kbytes, uint32_t a_blk, uint32_t b_blk) {
 #pragma unroll
-  for (int qi = 0; qi < 2; ++qi) dma16(buf + (qi * 8 + wave) * 64, ra, d.a_off[qi], kbytes);
+  for (int qi = 0; qi < 2; ++qi) dma16(buf + (qi * 8 + wave) * 64, ra, d.a_off[qi], stage_off(kbytes, a_blk));
 #pragma unroll
-  for (int qi = 0; qi < 2; ++qi) dma16(buf + Big::A_SLOTS + (qi * 8 + wave) * 64, rb, d.b_off[qi], kbytes);
+  for (int qi = 0; qi < 2; ++qi)
+    dma16(buf + Big::A_SLOTS + (qi * 8 + wave) * 64, rb, d.b_off[qi], stage_off(kbytes, b_blk));
 }
 
 // As stage_plan: chunks at or past the end of a row read zeros (padded K loops).
@@ -1367,7 +1380,7 @@ __device__ __forceinline__ void p8_plan(Plan8& d, const GemmArgs& p, const int* 
     const int c = (lane & 3) ^ big_swz(r);
     if (r < rows) {
       const int grow = p.gather ? (from_global ? p.gather[m0 + r] : gidx[r]) : (m0 + r);
-      d.a_off[qi] = (uint32_t)grow * row_bytes + (uint32_t)c * 16u;
+      d.a_off[qi] = chunk_off(grow, (uint32_t)c * 16u, p.a_row_pitch, p.a_blk_pitch);
     } else {
       d.a_off[qi] = 0x80000000u;
     }
@@ -1378,7 +1391,7 @@ __device__ __forceinline__ void p8_plan(Plan8& d, const GemmArgs& p, const int* 
     } else {
       wr = min(n0 + r, p.N - 1);
     }
-    d.b_off[qi] = (uint32_t)wr * row_bytes + (uint32_t)c * 16u;
+    d.b_off[qi] = chunk_off(wr, (uint32_t)c * 16u, p.b_row_pitch, p.b_blk_pitch);
   }
 }
 
@@ -1415,7 +1428,7 @@ template <int EPI, int LIVE>
 __device__ __forceinline__ void p8_step(f32x16_t (&acc)[4][2], Frags8& f, u32x4_t* refill,
                                         const u32x4_t* __restrict__ next_buf, bool dma, int kbytes, const Plan8& d,
                                         u32x4_t ra, u32x4_t rb, int wave, const int (&a_slot)[2],
-                                        const int (&b_slot)[2]) {
+                                        const int (&b_slot)[2], uint32_t a_blk, uint32_t b_blk) {
   static_assert(LIVE >= 1 && LIVE <= 4, "live row sub-tiles");
   constexpr int NG = 2 * LIVE;
 #pragma unroll
@@ -1428,8 +1441,8 @@ __device__ __forceinline__ void p8_step(f32x16_t (&acc)[4][2], Frags8& f, u32x4_
     if (dma) {
 #pragma unroll
       for (int q = (g * 4) / NG; q < ((g + 1) * 4) / NG; ++q) {
-        if (q < 2) dma16(refill + (q * 8 + wave) * 64, ra, d.a_off[q], kbytes);
-        else dma16(refill + Big::A_SLOTS + ((q - 2) * 8 + wave) * 64, rb, d.b_off[q - 2], kbytes);
+        if (q < 2) dma16(refill + (q * 8 + wave) * 64, ra, d.a_off[q], stage_off(kbytes, a_blk));
+        else dma16(refill + Big::A_SLOTS + ((q - 2) * 8 + wave) * 64, rb, d.b_off[q - 2], stage_off(kbytes, b_blk));
       }
     }
     if (i == LIVE - 1) {
@@ -1472,7 +1485,8 @@ __device__ __forceinline__ void pipe8_kloop(f32x16_t (&acc)[4][2], u32x4_t* s0, 
     for (int u = 0; u < 4; ++u) {
       const int kt = kt0 + u;
 #define MOE_P8_STEP(PL) \
-  p8_step<EPI, LIVE>(acc, f, bufs[u], bufs[(u + 1) & 3], dma, kbytes, PL, ra, rbs, wave, a_slot, b_slot)
+  p8_step<EPI, LIVE>(acc, f, bufs[u], bufs[(u + 1) & 3], dma, kbytes, PL, ra, rbs, wave, a_slot, b_slot, \
+                     p.a_blk_pitch, p.b_blk_pitch)
       if (last && !nx.has) {
         if (u == 0) wait_vmcnt<2 * PW>();
         else if (u == 1) wait_vmcnt<PW>();
@@ -1510,13 +1524,13 @@ __device__ __forceinline__ void pipe8_kloop(f32x16_t (&acc)[4][2], u32x4_t* s0, 
         if constexpr (LIVE >= 1) {
           MOE_P8_STEP(dk);
         } else {
-          if (dma) p8_issue(bufs[u], dk, ra, rbs, wave, kbytes);
+          if (dma) p8_issue(bufs[u], dk, ra, rbs, wave, kbytes, p.a_blk_pitch, p.b_blk_pitch);
         }
       } else {
         if constexpr (LIVE >= 1) {
           MOE_P8_STEP(dd);
         } else {
-          if (dma) p8_issue(bufs[u], dd, ra, rbs, wave, kbytes);
+          if (dma) p8_issue(bufs[u], dd, ra, rbs, wave, kbytes, p.a_blk_pitch, p.b_blk_pitch);
         }
       }
     }
@@ -1556,8 +1570,10 @@ __device__ __forceinline__ void p8_epilogue(const f32x16_t (&acc)[4][2], const G
       for (int gp = 0; gp < 4; gp += 2) {
         const u32x4_t v = pair_columns(hb[gp][0], hb[gp][1], hb[gp + 1][0], hb[gp + 1][1]);
         const int col = n0 + 32 * wn + 8 * (gp + hi);
-        const uint32_t off =
-            (row_ok && col < p.N) ? (uint32_t)(((int64_t)(m0 + row) * p.ldo + col) * 2) : 0x80000000u;
+        // row-major h, or K-blocked [N/32][M][32] for a down projection that reads it so
+        const int64_t e = p.out_kblocked ? ((int64_t)(col >> 5) * p.M + (m0 + row)) * 32 + (col & 31)
+                                         : (int64_t)(m0 + row) * p.ldo + col;
+        const uint32_t off = (row_ok && col < p.N) ? (uint32_t)(e * 2) : 0x80000000u;
         __builtin_amdgcn_raw_buffer_store_b128(v, ro, (int)off, 0, 0);
       }
     } else if (EPI == EPI_F16S) {
@@ -1676,8 +1692,7 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_bf16_pipe8_kernel(Gemm
     b_slot[h] = Big::A_SLOTS + (((EPI == EPI_SWIGLU) ? 32 : 64) * wn + rin) * 4 + pos;
   }
   const u32x4_t ra = make_rsrc(p.A, (uint32_t)p.a_rows * row_bytes);
-  const int b_rows_total = (EPI == EPI_SWIGLU) ? 2 * p.up_row0 : p.N;
-  const uint32_t b_bytes = (uint32_t)b_rows_total * row_bytes;
+  const uint32_t b_bytes = p.b_group_bytes;
   const size_t out_elt = (EPI == EPI_F32) ? 4 : 2;
   const __amdgpu_buffer_rsrc_t ro =
       __builtin_amdgcn_make_buffer_rsrc(p.out, (short)0, (int)((size_t)p.M * p.ldo * out_elt), kBufferWord3);
@@ -1688,15 +1703,15 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_bf16_pipe8_kernel(Gemm
   u32x4_t rb = make_rsrc(p.B + (int64_t)tc.g * p.b_group_stride, b_bytes);
   if constexpr (PAD) {
     const uint32_t cb = big_chunk_bytes(lane);
-    p8_issue(st0, p8_stage_plan(d, cb, 0, row_bytes), ra, rb, wave, 0);
-    p8_issue(st1, p8_stage_plan(d, cb, 1 * Big::KB * 2, row_bytes), ra, rb, wave, 1 * Big::KB * 2);
-    p8_issue(st2, p8_stage_plan(d, cb, 2 * Big::KB * 2, row_bytes), ra, rb, wave, 2 * Big::KB * 2);
-    p8_issue(st3, p8_stage_plan(d, cb, 3 * Big::KB * 2, row_bytes), ra, rb, wave, 3 * Big::KB * 2);
+    p8_issue(st0, p8_stage_plan(d, cb, 0, row_bytes), ra, rb, wave, 0, p.a_blk_pitch, p.b_blk_pitch);
+    p8_issue(st1, p8_stage_plan(d, cb, 1 * Big::KB * 2, row_bytes), ra, rb, wave, 1 * Big::KB * 2, p.a_blk_pitch, p.b_blk_pitch);
+    p8_issue(st2, p8_stage_plan(d, cb, 2 * Big::KB * 2, row_bytes), ra, rb, wave, 2 * Big::KB * 2, p.a_blk_pitch, p.b_blk_pitch);
+    p8_issue(st3, p8_stage_plan(d, cb, 3 * Big::KB * 2, row_bytes), ra, rb, wave, 3 * Big::KB * 2, p.a_blk_pitch, p.b_blk_pitch);
   } else {
-    p8_issue(st0, d, ra, rb, wave, 0);
-    p8_issue(st1, d, ra, rb, wave, 1 * Big::KB * 2);
-    p8_issue(st2, d, ra, rb, wave, 2 * Big::KB * 2);
-    p8_issue(st3, d, ra, rb, wave, 3 * Big::KB * 2);
+    p8_issue(st0, d, ra, rb, wave, 0, p.a_blk_pitch, p.b_blk_pitch);
+    p8_issue(st1, d, ra, rb, wave, 1 * Big::KB * 2, p.a_blk_pitch, p.b_blk_pitch);
+    p8_issue(st2, d, ra, rb, wave, 2 * Big::KB * 2, p.a_blk_pitch, p.b_blk_pitch);
+    p8_issue(st3, d, ra, rb, wave, 3 * Big::KB * 2, p.a_blk_pitch, p.b_blk_pitch);
   }
 
   bool after_epi = false;
@@ -2045,8 +2060,32 @@ bool grouped_gemm_has_f16s(const GemmArgs& a) {
   return a.M > 0 && pick_bm(a.M, groups) == 0;
 }
 
-hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, GemmEpilogue epi, hipStream_t s, const char* name) {
-  if (a.M <= 0) return hipSuccess;
+bool grouped_gemm_runs_pipe8(const GemmArgs& a, GemmEpilogue epi) {
+  if (epi == EPI_ROUTER || a.M <= 0) return false;
+  const int64_t groups = a.offsets ? (a.G < a.M ? a.G : a.M) : 1;
+  if (pick_bm(a.M, groups) != 0) return false;
+  return pipe_fits(a);
+}
+
+hipError_t launch_grouped_gemm_bf16(const GemmArgs& a_in, GemmEpilogue epi, hipStream_t s, const char* name) {
+  if (a_in.M <= 0) return hipSuccess;
+  // operand layouts: row-major unless given
+  GemmArgs a = a_in;
+  const int b_rows_total = (epi == EPI_SWIGLU) ? 2 * a.up_row0 : a.N;
+  if (a.b_row_pitch == 0) {
+    a.b_row_pitch = (uint32_t)a.K * 2u;
+    a.b_blk_pitch = 64u;
+  }
+  if (a.b_group_bytes == 0) a.b_group_bytes = (uint32_t)b_rows_total * (uint32_t)a.K * 2u;
+  if (a.a_row_pitch == 0) {
+    a.a_row_pitch = (uint32_t)a.K * 2u;
+    a.a_blk_pitch = 64u;
+  }
+  // a K-blocked A (not gathered) or a K-blocked h output: the pipelined kernel only
+  const bool a_blocked = a.a_row_pitch != (uint32_t)a.K * 2u || a.a_blk_pitch != 64u;
+  if ((a_blocked || a.out_kblocked) && !grouped_gemm_runs_pipe8(a, epi)) return hipErrorInvalidValue;
+  if (a_blocked && a.gather != nullptr) return hipErrorInvalidValue;
+  if (a.out_kblocked && (epi != EPI_SWIGLU || a.N % kKBlock != 0 || a.ldo != a.N)) return hipErrorInvalidValue;
   if (epi == EPI_F16S) {
     if (!grouped_gemm_has_f16s(a) || a.scale_out == nullptr || a.N % kF16SegCols != 0 || a.ldo % kF16SegCols != 0)
       return hipErrorInvalidValue;

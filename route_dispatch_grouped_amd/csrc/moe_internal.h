@@ -54,7 +54,24 @@ struct GemmArgs {
   int* tile_counter;        // large-group kernel: 8 zeroed ints (per-XCD tile grabs) or NULL
   float* partial;           // split-K scratch of grouped_gemm_partial_bytes() bytes, or NULL (no split)
   int ksplit;               // set by launch_grouped_gemm_bf16 (callers leave it 0)
+  // Byte layout of a group of B: element (r, k) at b_row_pitch * r +
+  // b_blk_pitch * (k / 32) + 2 * (k % 32).  Row-major [rows][K]: (2K, 64);
+  // K-blocked [ceil(K/32)][rows][32] (kb32_bytes): (64, 64 * rows).  0: row-major.
+  uint32_t b_row_pitch, b_blk_pitch;
+  uint32_t b_group_bytes;   // bytes one group's B occupies (0: rows * 2K)
+  // The same for A (rows not gathered): only the pipelined kernel reads a
+  // K-blocked A, the h that its own gate/up epilogue wrote K-blocked.  0: row-major.
+  uint32_t a_row_pitch, a_blk_pitch;
+  int out_kblocked;         // EPI_SWIGLU on the pipelined kernel: h written K-blocked [I/32][M][32]
 };
+
+// Bytes of a K-blocked matrix of `rows` rows of length K: ceil(K/32) blocks of
+// rows x 32 elements, the tail block zero-padded.
+constexpr int kKBlock = 32;
+inline size_t kb32_bytes(int64_t rows, int64_t K) { return (size_t)((K + kKBlock - 1) / kKBlock) * rows * kKBlock * 2; }
+// True when the grouped GEMM for `a` (epilogue epi) runs the 8-wave pipelined
+// kernel: the only kernel that reads a K-blocked A or writes a K-blocked h.
+bool grouped_gemm_runs_pipe8(const GemmArgs& a, GemmEpilogue epi);
 
 constexpr int kTileCounterInts = 8;
 // True when the grouped GEMM for `a` runs the large-group kernel (which uses
@@ -142,6 +159,11 @@ constexpr int kTopkDispatchSmallT = 64;
 hipError_t launch_topk_dispatch_small(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
                                       float* weights, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                                       int32_t* packed_ids, hipStream_t s, int* zero_ints, int n_zero);
+
+// ---------------------------------------------------------------- weights
+// K-blocked copy of G row-major [R, K] bf16 matrices (K a multiple of 8):
+// dst[g][b][r][i] = src[g][r][32 b + i], zero past K; kb32_bytes(R, K) per group.
+hipError_t launch_pack_kb32(const void* src, void* dst, int64_t G, int64_t R, int64_t K, hipStream_t s);
 
 // ---------------------------------------------------------------- combine
 // y [P,H]: fp32 (y_format 0), bf16 (1), or fp16 with the EPI_F16S

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
 
 OK, INVALID, UNSUP, WS, HIP = 0, 1, 2, 3, 4
-F32, BF16 = 0, 1
+F32, BF16, KB32 = 0, 1, 2
 P16 = ctypes.c_void_p(4096)  # fake, 16-byte aligned device address: never dereferenced here
 BAD = ctypes.c_void_p(4098)  # misaligned
 NULL = None
@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
     for code, text in [(0, b"MOE_OK"), (1, b"MOE_ERR_INVALID_ARG"), (2, b"MOE_ERR_UNSUPPORTED"),
                        (3, b"MOE_ERR_WORKSPACE"), (4, b"MOE_ERR_HIP")]:
         assert lib.moe_status_string(code) == text
@@ -235,6 +235,7 @@ def test_tp_load_expert_validation(lib):
     assert load(dst=NULL) == INVALID and "dst" in last(lib)
     assert load(proj=3) == INVALID and "proj" in last(lib)
     assert load(dtype=7) == INVALID and "dtype" in last(lib)
+    assert load(dtype=KB32) == INVALID and "moe_pack_weights" in last(lib)
     assert load(G=0) == INVALID and "tp_rank" in last(lib)
     assert load(r=2) == INVALID and "tp_rank" in last(lib)
     assert load(r=-1) == INVALID
@@ -252,3 +253,32 @@ def test_ep_rank_counts_validation(lib):
     assert rc(G=0) == INVALID and "num_ranks" in last(lib)
     assert rc(G=9) == INVALID and "num_ranks" in last(lib)
     assert rc(E=0) == INVALID and rc(E=513, G=2) == INVALID
+
+
+def test_pack_weights_validation(lib):
+    def pack(src=P16, dst=ctypes.c_void_p(1 << 30), G=2, R=64, K=64):
+        return lib.moe_pack_weights(src, dst, G, R, K, NULL)
+    # ceil(K / 32) blocks of R x 32 bf16 per group, the tail block padded
+    assert lib.moe_packed_weights_size(2, 64, 64) == 2 * 2 * 64 * 32 * 2
+    assert lib.moe_packed_weights_size(1, 3, 40) == 1 * 2 * 3 * 32 * 2
+    assert lib.moe_packed_weights_size(0, 3, 40) == 0
+    assert pack(src=NULL) == INVALID and last(lib) == "src is NULL"
+    assert pack(dst=NULL) == INVALID
+    assert pack(G=0) == INVALID and pack(R=0) == INVALID and pack(K=0) == INVALID
+    assert pack(K=100) == UNSUP and "multiple of 8" in last(lib)
+    assert pack(src=BAD) == UNSUP and "aligned" in last(lib)
+    assert pack(dst=ctypes.c_void_p(4096 + 64)) == INVALID and "overlap" in last(lib)
+    assert pack(G=1, R=65536, K=32768) == UNSUP and "2 GiB" in last(lib)
+
+
+def test_packed_dtype_is_a_bf16_layer(lib):
+    # the K-blocked dtype takes the bf16 layer's limits and workspace sizes
+    assert ffn(lib, dtype=KB32, I=72) == UNSUP and "% 16" in last(lib)
+    assert ffn(lib, dtype=KB32, T=0) == OK
+    assert forward(lib, dtype=KB32, T=0) == OK
+    assert router(lib, dtype=KB32, T=0) == OK
+    assert (lib.moe_grouped_ffn_workspace_size(64, 256, 2, 8, 128, KB32) ==
+            lib.moe_grouped_ffn_workspace_size(64, 256, 2, 8, 128, BF16))
+    assert (lib.moe_forward_workspace_size(64, 256, 8, 2, 128, 64, KB32) ==
+            lib.moe_forward_workspace_size(64, 256, 8, 2, 128, 64, BF16))
+    assert ffn(lib, dtype=KB32, H=65536, I=32768, T=1, k=1) == UNSUP and "2 GiB" in last(lib)
