@@ -50,6 +50,7 @@
 // clamped (valid) row and are never stored; 16-row sub-tiles wholly past the
 // end skip their MFMAs (a straight-line K loop per live sub-tile count).
 #include <atomic>
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -1648,8 +1649,219 @@ __device__ __forceinline__ void p8_epilogue(const f32x16_t (&acc)[4][2], const G
 
 #undef MOE_P8_STEP
 
-template <int EPI, bool PAD>
+// ---------------------------------------------------------------- 8-wave kernel, A in whole lines
+// For a row-major A and K a multiple of 128 (the gathered token rows of
+// gate/up; h or dense rows elsewhere) A is fetched in 128-byte row pieces
+// that cover two consecutive stages: one whole-line request per row and two
+// stages instead of two half-line requests.  The A halves of slots 2j and
+// 2j + 1 form pair slot j (tile rows 0..127 in slot 2j, rows 128..255 in slot
+// 2j + 1, 128 bytes per row), shared by stages 4m + 2j and 4m + 2j + 1.  A pair
+// slot is free once both of its stages have been read, at the barrier of the
+// second: odd steps kt fetch A for stages kt + 3 and kt + 4 (two and three
+// steps ahead), and every step fetches B for stage kt + 4 into its own slot,
+// as in the 8-wave kernel above.  Chunk c (16 bytes: k 8c .. 8c + 7 of the
+// pair) of row r sits at position c ^ ((r >> 1) & 7) of the row's 128 bytes,
+// so the 32x32x16 fragment reads of 16 lanes (16 rows, one chunk) cover 16
+// distinct 16-byte bank groups.
+//
+// Per wave, even steps issue 2 DMA instructions (B) and odd steps 6 (4 A,
+// then 2 B).  The wait before step kt needs this wave's last instruction of
+// stage kt + 1: for even kt the B of step kt - 3 (8 instructions issued since),
+// for odd kt the last A of step kt - 2 (4 since).
+struct Plan8A {
+  uint32_t a_off[4];
+  uint32_t b_off[2];
+};
+
+__device__ __forceinline__ int ap_swz(int r) { return (r >> 1) & 7; }
+
+// DMA plan of a tile.  A: instruction q = 8 qi + wave covers tile rows 8q ..
+// 8q + 7; lane l fetches chunk (l & 7) ^ ap_swz(r) of row r = 8q + (l >> 3)
+// (rows past the tile read zeros through an out-of-range offset).  B: as in
+// p8_plan.
+template <int EPI>
+__device__ __forceinline__ void p8a_plan(Plan8A& d, const GemmArgs& p, const int* gidx, bool from_global, int rows,
+                                         int m0, int n0, int wave, int lane) {
+#pragma unroll
+  for (int qi = 0; qi < 4; ++qi) {
+    const int r = (qi * 8 + wave) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ap_swz(r);
+    if (r < rows) {
+      const int grow = p.gather ? (from_global ? p.gather[m0 + r] : gidx[r]) : (m0 + r);
+      d.a_off[qi] = (uint32_t)grow * p.a_row_pitch + (uint32_t)c * 16u;
+    } else {
+      d.a_off[qi] = 0x80000000u;
+    }
+  }
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    const int q = qi * 8 + wave;
+    const int r = q * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ big_swz(r);
+    int wr;
+    if (EPI == EPI_SWIGLU) {
+      const int col = min(n0 + (r & 127), p.N - 1);
+      wr = (r < 128) ? col : p.up_row0 + col;
+    } else {
+      wr = min(n0 + r, p.N - 1);
+    }
+    d.b_off[qi] = chunk_off(wr, (uint32_t)c * 16u, p.b_row_pitch, p.b_blk_pitch);
+  }
+}
+
+// DMA instruction q of step U (kt % 4): for odd U, q < 4 are the A pair
+// (stages kt + 3, kt + 4 into pair slot U / 2), the rest B of stage kt + 4
+// into slot U.  a_kbytes: byte offset of the pair in a row; b_kbytes: of the
+// B stage.
+template <int U>
+__device__ __forceinline__ void p8a_dma(int q, u32x4_t* const (&bufs)[4], const Plan8A& d, u32x4_t ra, u32x4_t rb,
+                                        int wave, int a_kbytes, int b_kbytes, uint32_t b_blk) {
+  constexpr int NA = (U & 1) ? 4 : 0;
+  if (q < NA) {
+    dma16(bufs[(U >> 1) * 2 + (q >> 1)] + ((q & 1) * 8 + wave) * 64, ra, d.a_off[q], a_kbytes);
+  } else {
+    const int qb = q - NA;
+    dma16(bufs[U] + Big::A_SLOTS + (qb * 8 + wave) * 64, rb, d.b_off[qb], stage_off(b_kbytes, b_blk));
+  }
+}
+
+template <int U>
+__device__ __forceinline__ void p8a_issue(u32x4_t* const (&bufs)[4], const Plan8A& d, u32x4_t ra, u32x4_t rb,
+                                          int wave, int a_kbytes, int b_kbytes, uint32_t b_blk) {
+  constexpr int NQ = (U & 1) ? 6 : 2;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) p8a_dma<U>(q, bufs, d, ra, rb, wave, a_kbytes, b_kbytes, b_blk);
+}
+
+// Fragments of the stage held in slot U: B from slot U, A from pair slot
+// U / 2 at half U % 2.  a_idx[h]: this lane's A chunk of k16 half h in the
+// first stage of a pair (row sub-tiles i and i + 2 share it, in slots 2j and
+// 2j + 1); the second stage's chunk is 4 positions further, i.e. position
+// bit 2 flipped.
+template <int EPI, int LIVE, int U>
+__device__ __forceinline__ void p8a_read_half(Frags8& f, int h, u32x4_t* const (&bufs)[4], const int (&a_idx)[2],
+                                              const int (&b_slot)[2]) {
+  constexpr int S = U & 1, J = U >> 1;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) f.b[h][j] = __builtin_bit_cast(bf16x8_t, bufs[U][b_slot[h] + p8_b_off<EPI>(j)]);
+  const int ai = a_idx[h] ^ (4 * S);
+#pragma unroll
+  for (int i = 0; i < LIVE; ++i) f.a[h][i] = __builtin_bit_cast(bf16x8_t, bufs[2 * J + (i >> 1)][ai + 512 * (i & 1)]);
+}
+
+// One K step (slot U = kt % 4) of a wave with LIVE >= 1 live row sub-tiles:
+// as p8_step, with this step's DMA instructions spread over the MFMA groups
+// and the next stage's fragments read from slot (U + 1) % 4.
+template <int EPI, int LIVE, int U>
+__device__ __forceinline__ void p8a_step(f32x16_t (&acc)[4][2], Frags8& f, u32x4_t* const (&bufs)[4], bool dma,
+                                         int a_kbytes, int b_kbytes, const Plan8A& d, u32x4_t ra, u32x4_t rb,
+                                         int wave, const int (&a_idx)[2], const int (&b_slot)[2],
+                                         uint32_t b_blk) {
+  static_assert(LIVE >= 1 && LIVE <= 4, "live row sub-tiles");
+  constexpr int NG = 2 * LIVE;
+  constexpr int NQ = (U & 1) ? 6 : 2;
+  constexpr int UN = (U + 1) & 3;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int h = g / LIVE, i = g % LIVE;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[h][j], f.a[h][i], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (dma) {
+#pragma unroll
+      for (int q = (g * NQ) / NG; q < ((g + 1) * NQ) / NG; ++q)
+        p8a_dma<U>(q, bufs, d, ra, rb, wave, a_kbytes, b_kbytes, b_blk);
+    }
+    if (i == LIVE - 1) p8a_read_half<EPI, LIVE, UN>(f, h, bufs, a_idx, b_slot);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Step kt = kt0 + U of a tile's K loop: the wait, the barrier, the next
+// tile's row indices (step KT - 8) and plan (step KT - 4), and the step.
+// LAST: one of the last four steps, whose DMAs fetch the next tile's stages
+// 0..3 (plan dn, weights rbn) if there is one.  The last four steps are
+// separate code so that the plan of each step's DMAs is known without a
+// select between two plans.
+template <int EPI, int LIVE, int U, bool LAST>
+__device__ __forceinline__ void p8a_kstep(f32x16_t (&acc)[4][2], Frags8& f, u32x4_t* const (&bufs)[4], int* s_gidx,
+                                          const GemmArgs& p, const Plan8A& d, u32x4_t ra, u32x4_t rb, Plan8A& dn,
+                                          u32x4_t rbn, const PipeNext& nx, bool after_epi, int wave, int lane,
+                                          int KT, int kt0, const int (&a_idx)[2], const int (&b_slot)[2]) {
+  constexpr int S = Pipe8Epi<EPI>::kStores;
+  constexpr int W = (U & 1) ? 4 : 8;
+  const int kt = kt0 + U;
+  if (LAST && !nx.has) {
+    // nothing is issued in the last four steps: stage KT - 3 has 8
+    // instructions after it, stage KT - 2 (its A at step KT - 5) 2, stage
+    // KT - 1 none
+    if (U == 0) wait_vmcnt<8>();
+    else if (U == 1) wait_vmcnt<2>();
+    else wait_vmcnt<0>();
+  } else if (kt0 == 0 && U < 3 && after_epi) {
+    wait_vmcnt_clamped<W + S>();
+  } else {
+    wait_vmcnt<W>();
+  }
+  lds_barrier();
+  if (!LAST && U == 0 && kt0 + 8 == KT && nx.has && p.gather && wave < 4) {
+    const int r = 64 * wave + lane;
+    const uint32_t voff = (r < nx.rows) ? (uint32_t)(nx.m0 + r) * 4u : 0x80000000u;
+    dma4(s_gidx + 64 * wave, make_rsrc(p.gather, (uint32_t)p.M * 4u), voff, 0);
+  }
+  if (LAST && U == 0 && nx.has) p8a_plan<EPI>(dn, p, s_gidx, false, nx.rows, nx.m0, nx.n0, wave, lane);
+  const bool dma = LAST ? nx.has : true;
+  const int a_kbytes = LAST ? (U - 1) * Big::KB * 2 : (kt + 3) * Big::KB * 2;
+  const int b_kbytes = LAST ? U * Big::KB * 2 : (kt + 4) * Big::KB * 2;
+  const Plan8A& dd = LAST ? dn : d;
+  const u32x4_t rbs = LAST ? rbn : rb;
+  if constexpr (LIVE >= 1) {
+    p8a_step<EPI, LIVE, U>(acc, f, bufs, dma, a_kbytes, b_kbytes, dd, ra, rbs, wave, a_idx, b_slot, p.b_blk_pitch);
+  } else {
+    if (dma) p8a_issue<U>(bufs, dd, ra, rbs, wave, a_kbytes, b_kbytes, p.b_blk_pitch);
+  }
+}
+
+// One tile's K loop.  On entry stages 0..3 of this tile are in flight (or
+// landed), issued in step order: B0 | A(0,1) B1 | B2 | A(2,3) B3, so 10
+// instructions follow stage 0's last (plus the previous tile's epilogue
+// stores when `after_epi`).
+template <int EPI, int LIVE>
+__device__ __forceinline__ void pipe8a_kloop(f32x16_t (&acc)[4][2], u32x4_t* const (&bufs)[4], int* s_gidx,
+                                             const GemmArgs& p, const Plan8A& d, u32x4_t ra, u32x4_t rb,
+                                             Plan8A& dn, u32x4_t rbn, const PipeNext& nx, bool after_epi, int wave,
+                                             int lane, int KT, const int (&a_idx)[2], const int (&b_slot)[2]) {
+  constexpr int S = Pipe8Epi<EPI>::kStores;
+  if (after_epi) wait_vmcnt_clamped<10 + S>();
+  else wait_vmcnt<10>();
+  lds_barrier();
+  Frags8 f;
+  if constexpr (LIVE > 0) {
+    p8a_read_half<EPI, LIVE, 0>(f, 0, bufs, a_idx, b_slot);
+    p8a_read_half<EPI, LIVE, 0>(f, 1, bufs, a_idx, b_slot);
+  }
+#define MOE_P8A_STEP(U, LAST)                                                                                     \
+  p8a_kstep<EPI, LIVE, U, LAST>(acc, f, bufs, s_gidx, p, d, ra, rb, dn, rbn, nx, after_epi, wave, lane, KT, kt0, \
+                                a_idx, b_slot)
+  int kt0 = 0;
+  for (; kt0 + 4 < KT; kt0 += 4) {
+    MOE_P8A_STEP(0, false);
+    MOE_P8A_STEP(1, false);
+    MOE_P8A_STEP(2, false);
+    MOE_P8A_STEP(3, false);
+  }
+  MOE_P8A_STEP(0, true);
+  MOE_P8A_STEP(1, true);
+  MOE_P8A_STEP(2, true);
+  MOE_P8A_STEP(3, true);
+#undef MOE_P8A_STEP
+}
+
+template <int EPI, bool PAD, bool AP>
 __global__ __launch_bounds__(kThreads8) void grouped_gemm_bf16_pipe8_kernel(GemmArgs p) {
+  static_assert(!(PAD && AP), "whole-line A needs K a multiple of 128");
+  using PlanT = std::conditional_t<AP, Plan8A, Plan8>;
   constexpr int BM = Big::BM;
   constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
 
@@ -1685,12 +1897,15 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_bf16_pipe8_kernel(Gemm
 
   const int rin = lane & 31;
   int a_slot[2], b_slot[2];
+  int a_idx[2];  // whole-line A: k16 half h of a pair's first stage
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int pos = (2 * h + (lane >> 5)) ^ big_swz(rin);
     a_slot[h] = (32 * wm + rin) * 4 + pos;
     b_slot[h] = Big::A_SLOTS + (((EPI == EPI_SWIGLU) ? 32 : 64) * wn + rin) * 4 + pos;
+    a_idx[h] = (32 * wm + rin) * 8 + ((2 * h + (lane >> 5)) ^ ap_swz(32 * wm + rin));
   }
+  u32x4_t* const bufs[4] = {st0, st1, st2, st3};
   const u32x4_t ra = make_rsrc(p.A, (uint32_t)p.a_rows * row_bytes);
   const uint32_t b_bytes = p.b_group_bytes;
   const size_t out_elt = (EPI == EPI_F32) ? 4 : 2;
@@ -1698,10 +1913,17 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_bf16_pipe8_kernel(Gemm
       __builtin_amdgcn_make_buffer_rsrc(p.out, (short)0, (int)((size_t)p.M * p.ldo * out_elt), kBufferWord3);
 
   TileCoord tc = tile_coord<BM>(t, nblk, G, s_tb, s_off);
-  Plan8 d;
-  p8_plan<EPI>(d, p, nullptr, true, tc.rows, tc.m0, tc.nb * BN_OUT, wave, lane, row_bytes);
+  PlanT d;
+  if constexpr (AP) p8a_plan<EPI>(d, p, nullptr, true, tc.rows, tc.m0, tc.nb * BN_OUT, wave, lane);
+  else p8_plan<EPI>(d, p, nullptr, true, tc.rows, tc.m0, tc.nb * BN_OUT, wave, lane, row_bytes);
   u32x4_t rb = make_rsrc(p.B + (int64_t)tc.g * p.b_group_stride, b_bytes);
-  if constexpr (PAD) {
+  if constexpr (AP) {
+    // step order: B0 | A(0,1) B1 | B2 | A(2,3) B3
+    p8a_issue<0>(bufs, d, ra, rb, wave, 0, 0, p.b_blk_pitch);
+    p8a_issue<1>(bufs, d, ra, rb, wave, 0, 1 * Big::KB * 2, p.b_blk_pitch);
+    p8a_issue<2>(bufs, d, ra, rb, wave, 0, 2 * Big::KB * 2, p.b_blk_pitch);
+    p8a_issue<3>(bufs, d, ra, rb, wave, 2 * Big::KB * 2, 3 * Big::KB * 2, p.b_blk_pitch);
+  } else if constexpr (PAD) {
     const uint32_t cb = big_chunk_bytes(lane);
     p8_issue(st0, p8_stage_plan(d, cb, 0, row_bytes), ra, rb, wave, 0, p.a_blk_pitch, p.b_blk_pitch);
     p8_issue(st1, p8_stage_plan(d, cb, 1 * Big::KB * 2, row_bytes), ra, rb, wave, 1 * Big::KB * 2, p.a_blk_pitch, p.b_blk_pitch);
@@ -1727,7 +1949,7 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_bf16_pipe8_kernel(Gemm
     nx.rows = tcn.rows;
     nx.n0 = tcn.nb * BN_OUT;
     const u32x4_t rbn = make_rsrc(p.B + (int64_t)tcn.g * p.b_group_stride, b_bytes);
-    Plan8 dn = d;
+    PlanT dn = d;
 
     f32x16_t acc[4][2];
 #pragma unroll
@@ -1740,8 +1962,12 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_bf16_pipe8_kernel(Gemm
     switch (live) {
 #define MOE_PIPE8_CASE(n)                                                                                        \
   case n:                                                                                                        \
-    pipe8_kloop<EPI, n, PAD>(acc, st0, st1, st2, st3, s_gidx, p, d, ra, rb, dn, rbn, nx, after_epi, wave, lane, \
-                             KT, row_bytes, a_slot, b_slot);                                                     \
+    if constexpr (AP)                                                                                            \
+      pipe8a_kloop<EPI, n>(acc, bufs, s_gidx, p, d, ra, rb, dn, rbn, nx, after_epi, wave, lane, KT, a_idx,      \
+                           b_slot);                                                                              \
+    else                                                                                                         \
+      pipe8_kloop<EPI, n, PAD>(acc, st0, st1, st2, st3, s_gidx, p, d, ra, rb, dn, rbn, nx, after_epi, wave,     \
+                               lane, KT, row_bytes, a_slot, b_slot);                                             \
     break;
       MOE_PIPE8_CASE(0) MOE_PIPE8_CASE(1) MOE_PIPE8_CASE(2) MOE_PIPE8_CASE(3) MOE_PIPE8_CASE(4)
 #undef MOE_PIPE8_CASE
@@ -1988,11 +2214,19 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t s, const char* name) {
   if (ub < grid) grid = ub;
   grid = ((grid + kXcds - 1) / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
+  // A row-major (gathered or plain rows, not K-blocked) with whole groups of
+  // four stages: A in whole 128-byte lines
+  const bool a_rows = a.a_row_pitch == (uint32_t)a.K * 2u && a.a_blk_pitch == 64u;
   profile_begin(name, s);
   if (a.K % (4 * Big::KB) != 0)
-    hipLaunchKernelGGL((grouped_gemm_bf16_pipe8_kernel<EPI, true>), dim3((unsigned)grid), dim3(kThreads8), 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16_pipe8_kernel<EPI, true, false>), dim3((unsigned)grid), dim3(kThreads8), 0,
+                       s, a);
+  else if (a_rows)
+    hipLaunchKernelGGL((grouped_gemm_bf16_pipe8_kernel<EPI, false, true>), dim3((unsigned)grid), dim3(kThreads8), 0,
+                       s, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_bf16_pipe8_kernel<EPI, false>), dim3((unsigned)grid), dim3(kThreads8), 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16_pipe8_kernel<EPI, false, false>), dim3((unsigned)grid), dim3(kThreads8), 0,
+                       s, a);
   profile_end(s);
   return hipGetLastError();
 }

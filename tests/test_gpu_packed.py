@@ -35,6 +35,9 @@ BF16_SMALL = {
                         intermediate_size=96, shared_intermediate_size=176),
     "tp8_pipe": dict(base="qwen3_30b_a3b_prefill", num_tokens=4096, hidden_size=512, num_experts=16, top_k=8,
                      intermediate_size=96),
+    # packed w2 under a down projection that reads row-major h in whole lines
+    "rowmajor_h_down": dict(base="qwen3_30b_a3b_prefill", num_tokens=2048, hidden_size=160, num_experts=8, top_k=2,
+                            intermediate_size=256),
 }
 
 

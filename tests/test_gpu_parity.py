@@ -111,6 +111,17 @@ SMALL = {
         name="bf16_h1000_pipe", num_tokens=1200, hidden_size=1000, num_experts=4, top_k=2, intermediate_size=192),
     "bf16_h104_short_k": workloads.config("qwen3_30b_a3b_prefill").scaled(
         name="bf16_h104_short_k", num_tokens=600, hidden_size=104, num_experts=2, top_k=1, intermediate_size=64),
+    # the pipelined kernel fetching A in whole 128-byte lines (two stages per
+    # fetch): gathered token rows with the shortest such K loop (8 stages, so
+    # the next tile's row indices are staged at its first step), and a down
+    # projection reading row-major h (gate/up on the plain 256-row kernel,
+    # since its 5-stage K loop would pad by more than a third), fp16 +
+    # exponent outputs
+    "bf16_pipe_k256": workloads.config("qwen3_30b_a3b_prefill").scaled(
+        name="bf16_pipe_k256", num_tokens=2048, hidden_size=256, num_experts=8, top_k=2, intermediate_size=128),
+    "bf16_rowmajor_h_down": workloads.config("qwen3_30b_a3b_prefill").scaled(
+        name="bf16_rowmajor_h_down", num_tokens=2048, hidden_size=160, num_experts=8, top_k=2,
+        intermediate_size=256),
 }
 
 
@@ -300,12 +311,14 @@ def test_forward_largest_batch_every_token():
 
 
 @pytest.mark.parametrize("T,H,I,dtype", [(16, 256, 192, "bf16"), (80, 128, 96, "bf16"), (1000, 256, 160, "bf16"),
-                                          (4096, 512, 256, "bf16"), (37, 64, 48, "f32")])
+                                          (4096, 512, 256, "bf16"), (4096, 128, 128, "bf16"), (37, 64, 48, "f32")])
 def test_grouped_ffn_dense_single_expert(T, H, I, dtype):
     """moe_grouped_ffn with no packed token indices and no offsets (one
     expert owning every row, row p reading token p): a dense SwiGLU MLP,
     against the oracle's expert MLP on all rows.  Covers the streaming,
-    middle and 256-row GEMMs without a gather."""
+    middle and 256-row GEMMs without a gather (H = 128: the pipelined kernel
+    with one group of four stages per tile, so every tile's K loop is also
+    its last four steps)."""
     base = "qwen3_30b_a3b_prefill" if dtype == "bf16" else "tiny_fp32"
     cfg = workloads.config(base).scaled(name="dense_ffn", num_tokens=T, hidden_size=H, num_experts=1, top_k=1,
                                         intermediate_size=I)
