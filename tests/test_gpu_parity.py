@@ -245,12 +245,16 @@ def check_every_token(cfg, inp, f, label):
     """Every token of a full-size forward against the oracle: all logits within
     the rigorous fp32 bound, the GPU's top-k bit-exact on its own logits, ids
     equal to the oracle's outside the near-tie window (its size logged), and
-    every output row within tol * rms of the oracle fed the GPU routing."""
+    every output row within tol * rms of the oracle fed the GPU routing (whose
+    weights are checked against the oracle's weights of the GPU's logits)."""
     T = cfg.num_tokens
     ids_f = f["topk_ids"].cpu().numpy()
     w_f = f["topk_weights"].cpu().numpy().astype(np.float64)
     Lg = f["logits"].cpu().numpy().astype(np.float64)
     assert (ids_f == oracle.select_topk(Lg, cfg.top_k)).all()
+    # the routing weights the forward used, from its own logits
+    w_ref = oracle.routing_weights(Lg, ids_f, cfg.renormalize)
+    assert np.max(np.abs(w_f - w_ref) / np.maximum(w_ref, 1e-30)) <= 1e-5
     L = oracle.router_logits(inp["x"], inp["router_weight"], inp.get("router_bias"))
     err_l = np.abs(Lg - L)
     assert (err_l <= logit_error_bound(inp)).all(), float(err_l.max())
