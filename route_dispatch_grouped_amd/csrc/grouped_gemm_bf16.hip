@@ -89,16 +89,16 @@ struct Tile {
   static_assert(NS >= 3 && VM_WAIT < 64, "ring depth");
 };
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+// two values rounded to bf16 (nearest even), the first in the low half (the
+// lower address): one v_cvt_pk_bf16_f32, which gives the bits of the integer
+// rounding u + 0x7FFF + ((u >> 16) & 1) for every finite input
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
-// two values rounded to bf16, the first in the low half (the lower address)
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
-}
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return static_cast<uint16_t>(pack_bf16x2(f, 0.f)); }
 
 // Exponent k that brings a segment whose largest magnitude is m into
 // [2^14, 2^15) (0 for an all-zero segment; below the normal range the
@@ -113,7 +113,6 @@ __device__ __forceinline__ int f16s_exponent(float m) {
 // two values rounded to fp16 (nearest even; one v_cvt_pk_f16_f32), the first
 // in the low half
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
   typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
   const f32x2_t v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
@@ -1564,9 +1563,8 @@ __device__ __forceinline__ void p8_epilogue(const f32x16_t (&acc)[4][2], const G
       for (int gq = 0; gq < 4; ++gq)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          hb[gq][c] = (uint32_t)f32_to_bf16_rne(silu_mul(acc[i][0][4 * gq + 2 * c], acc[i][1][4 * gq + 2 * c])) |
-                      ((uint32_t)f32_to_bf16_rne(silu_mul(acc[i][0][4 * gq + 2 * c + 1],
-                                                          acc[i][1][4 * gq + 2 * c + 1])) << 16);
+          hb[gq][c] = pack_bf16x2(silu_mul(acc[i][0][4 * gq + 2 * c], acc[i][1][4 * gq + 2 * c]),
+                                  silu_mul(acc[i][0][4 * gq + 2 * c + 1], acc[i][1][4 * gq + 2 * c + 1]));
 #pragma unroll
       for (int gp = 0; gp < 4; gp += 2) {
         const u32x4_t v = pair_columns(hb[gp][0], hb[gp][1], hb[gp + 1][0], hb[gp + 1][1]);
