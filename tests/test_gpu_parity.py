@@ -115,8 +115,9 @@ SMALL = {
     # fetch): gathered token rows with the shortest such K loop (8 stages, so
     # the next tile's row indices are staged at its first step), and a down
     # projection reading row-major h (gate/up on the plain 256-row kernel,
-    # since its 5-stage K loop would pad by more than a third), fp16 +
-    # exponent outputs
+    # since its 5-stage K loop would pad by more than a third): whole-line A
+    # under the grouped FFN's fp32 and bf16 outputs, the plain K loop under
+    # the forward's fp16 + exponent outputs
     "bf16_pipe_k256": workloads.config("qwen3_30b_a3b_prefill").scaled(
         name="bf16_pipe_k256", num_tokens=2048, hidden_size=256, num_experts=8, top_k=2, intermediate_size=128),
     "bf16_rowmajor_h_down": workloads.config("qwen3_30b_a3b_prefill").scaled(
