@@ -103,6 +103,18 @@ def test_packed_layer_bit_equal_to_row_major(name):
         assert torch.equal(y.view(torch.int16), yp.view(torch.int16)), out_dtype
 
 
+@pytest.mark.parametrize("shape", [(1500, 384, 6, 2, 256), (2400, 640, 10, 4, 320), (1000, 200, 5, 3, 144),
+                                   (2048, 192, 24, 6, 208), (1200, 136, 8, 2, 400), (2500, 512, 20, 8, 160)],
+                         ids=lambda t: "T%d_H%d_E%d_k%d_I%d" % t)
+def test_packed_layer_bit_equal_mixed_shapes(shape):
+    """Layers of the mixed parity shapes (whole-line A, padded K loops, K
+    tails, down on the plain 256-row kernel) on packed weights."""
+    T, H, E, k, I = shape
+    cfg = workloads.config("qwen3_30b_a3b_prefill").scaled(name="packed_mixed", num_tokens=T, hidden_size=H,
+                                                            num_experts=E, top_k=k, intermediate_size=I)
+    check_bit_equal(cfg, device_inputs(workloads.generate(cfg, seed=3)))
+
+
 @pytest.mark.parametrize("name", ["qwen15_moe_decode", "qwen3_30b_a3b_prefill", "qwen3_30b_a3b_prefill_zipf",
                                   "dwdp_h4096_e64"])
 def test_packed_layer_bit_equal_at_full_size(name):
