@@ -257,9 +257,13 @@ def decode_measure(rdg, torch, seed, steps=400, warmup=50, flushed_steps=100, fl
     step, reported as tokens/s and as weight bytes streamed per second against
     the HBM peak.  Bytes per step: the touched experts' w13 and w2, the shared
     expert's weights, the router and gate rows (activations are negligible).
-    Two regimes: back-to-back forwards (weights may stay in the 256 MB MALL
-    between steps) and forwards each preceded by a copy of `flush_mib` MiB
-    (the weights come from HBM), each with event-timed p10/p50/p90."""
+    Three regimes, each with event-timed p10/p50/p90: back-to-back forwards
+    (weights may stay in the 256 MB MALL between steps); forwards each
+    preceded by a read-only pass over `flush_mib` MiB (a sum), which leaves
+    the L2s and the MALL holding clean lines of that buffer and none of the
+    weights; and forwards each preceded by a copy of `flush_mib` MiB, whose
+    writes leave the caches full of dirty lines that are written back to HBM
+    while the forward runs."""
     cfg = workloads.config(SECONDARY_WORKLOAD)
     inp = workloads.generate(cfg, seed=seed)
 
@@ -286,7 +290,8 @@ def decode_measure(rdg, torch, seed, steps=400, warmup=50, flushed_steps=100, fl
     n = flush_mib * (1 << 20) // 4
     fa = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
     fb = torch.empty_like(fa)
-    cold = timed_forwards(torch, lambda: layer(x), flushed_steps, flush=lambda: fb.copy_(fa))
+    cold = timed_forwards(torch, lambda: layer(x), flushed_steps, flush=lambda: torch.sum(fa))
+    dirty = timed_forwards(torch, lambda: layer(x), flushed_steps, flush=lambda: fb.copy_(fa))
     del fa, fb
     r = rdg.moe_router_topk(x, d["router_weight"], cfg.top_k, renormalize=cfg.renormalize)
     counts = rdg.moe_dispatch_plan(r["topk_ids"], None, cfg.num_experts)["counts"].cpu().numpy()
@@ -306,7 +311,10 @@ def decode_measure(rdg, torch, seed, steps=400, warmup=50, flushed_steps=100, fl
            "weight_bytes_per_step": nbytes, "achieved": round(gbs, 1), "achieved_unit": "GB/s",
            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
            "unflushed": regime(warm, "back-to-back forwards (weights may stay in the MALL)"),
-           "flushed": regime(cold, f"a {flush_mib} MiB device copy before every forward (cold L2 and MALL)")}
+           "flushed": regime(cold, f"a read-only pass over {flush_mib} MiB before every forward (cold L2 and "
+                                   "MALL)"),
+           "flushed_dirty": regime(dirty, f"a {flush_mib} MiB device copy before every forward (cold L2 and MALL, "
+                                          "their dirty lines written back during the forward)")}
     # one rank of an 8-way tensor-parallel split (I / 8 and Is / 8, router and
     # gate replicated): the same tokens stream an eighth of the expert weights
     G = 8
