@@ -375,6 +375,85 @@ def test_grouped_ffn_dense_single_expert(T, H, I, dtype):
     assert err <= tol_for(cfg) * rms
 
 
+# Rows per expert on both sides of the 256-row m-tile's edges: an empty
+# expert, one row, a 33-row tail (one live 32-row sub-tile plus one row),
+# 255 / 256 / 257, a 288-row expert (a 32-row tail tile), 511 / 512 / 513, and
+# two others; 3422 rows in 12 experts, so both GEMMs take the 256-row kernels.
+TILE_EDGE_COUNTS = [0, 1, 33, 255, 256, 257, 288, 511, 512, 513, 700, 96]
+
+
+def crafted_top1_ids(counts, seed):
+    """Top-1 ids [T, 1] giving expert e exactly counts[e] tokens, in a seeded
+    random token order."""
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    np.random.default_rng(seed).shuffle(ids)
+    return ids.reshape(-1, 1)
+
+
+@pytest.mark.parametrize("H,I", [(512, 256), (320, 160)])
+def test_grouped_ffn_tile_edge_counts(H, I):
+    """moe_grouped_ffn on a plan with the crafted per-expert row counts, every
+    row against the oracle's expert MLP, on row-major and on K-blocked weights
+    (bit-equal to each other).  H = 512: gate/up fetches the gathered token
+    rows in whole lines; H = 320: gate/up pads its K loop to 12 stages, and
+    the down projection (K = 160) runs on the plain 256-row kernel."""
+    counts = TILE_EDGE_COUNTS
+    E, T = len(counts), sum(counts)
+    cfg = workloads.config("qwen3_30b_a3b_prefill").scaled(name="tile_edges", num_tokens=T, hidden_size=H,
+                                                            num_experts=E, top_k=1, intermediate_size=I)
+    inp = workloads.generate(cfg, seed=11)
+    dev = device_inputs(inp)
+    ids = crafted_top1_ids(counts, 11)
+    w = np.ones((T, 1), dtype=np.float32)
+    plan = oracle.dispatch_plan(ids, w, E)
+    assert (plan["counts"] == np.asarray(counts)).all()
+    g = rdg.moe_dispatch_plan(to_device(ids), to_device(w), E)
+    check_plan_equal(g, plan)
+    ref = oracle.expert_ffn(inp["x"], plan["packed_ids"], plan["offsets"], inp["w13"], inp["w2"])
+    ys = []
+    for pack in (False, True):
+        w13 = rdg.pack_weights(dev["w13"]) if pack else dev["w13"]
+        w2 = rdg.pack_weights(dev["w2"]) if pack else dev["w2"]
+        y = rdg.moe_grouped_ffn(dev["x"], g["packed_ids"], g["offsets"], w13, w2, 1)
+        err, rms = rel_max_err(y.cpu().numpy().astype(np.float64), ref)
+        log(f"[parity] tile edges H={H} I={I} packed={pack}: max|err|/rms = {err / rms:.3e}")
+        assert err <= tol_for(cfg) * rms
+        ys.append(y)
+    assert torch.equal(ys[0].view(torch.int32), ys[1].view(torch.int32))
+
+
+def test_forward_tile_edge_counts():
+    """The whole forward with the crafted per-expert row counts, so that the
+    down projection's fp16 + exponent outputs and the combine meet every
+    m-tile edge: router weight row e is the unit vector e and token t's first
+    E inputs are 0 except 8 at its expert, so the router's logits are exact
+    and the top-1 is the crafted one."""
+    counts = TILE_EDGE_COUNTS
+    E, T, H, I = len(counts), sum(counts), 512, 256
+    cfg = workloads.config("qwen3_30b_a3b_prefill").scaled(name="tile_edges_forward", num_tokens=T, hidden_size=H,
+                                                            num_experts=E, top_k=1, intermediate_size=I)
+    inp = dict(workloads.generate(cfg, seed=12))
+    inp.pop("router_bias", None)
+    ids = crafted_top1_ids(counts, 12)[:, 0]
+    rw = np.zeros((E, H), dtype=np.uint16)
+    rw[np.arange(E), np.arange(E)] = 0x3F80  # bf16 1.0
+    x = inp["x"].copy()
+    x[:, :E] = 0
+    x[np.arange(T), ids] = 0x4100  # bf16 8.0
+    inp["x"], inp["router_weight"] = x, rw
+    dev = device_inputs(inp)
+    f = gpu_forward(cfg, dev)
+    assert (f["topk_ids"].cpu().numpy()[:, 0] == ids).all()
+    assert (f["topk_weights"].cpu().numpy() == 1.0).all()
+    res = oracle.forward(inp, 1, cfg.renormalize)
+    err, rms = rel_max_err(f["out"].cpu().numpy().astype(np.float64), res["out"])
+    log(f"[parity] tile edges forward: max|err|/rms = {err / rms:.3e}")
+    assert err <= tol_for(cfg) * rms
+    layer = rdg.MoeLayer(dev["router_weight"], dev["w13"], dev["w2"], 1, pack=True)
+    out_p = layer(dev["x"])
+    assert torch.equal(out_p.view(torch.int32), f["out"].view(torch.int32))
+
+
 def test_dispatch_edge_cases():
     cases = []
     rng = np.random.default_rng(5)
